@@ -1,0 +1,139 @@
+// kda_api.cpp -- the extern "C" boundary of libkda.so: argument validation, dispatch, status.
+// Declarations, layouts and error behaviour are documented in include/kda.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/kda.h"
+#include "kda_internal.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool valid_dtype(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+int64_t esize(int dt) { return dt == KDA_F32 ? 4 : 2; }
+bool supported_d(int32_t d) { return d == 64 || d == 128; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range(const void* p, int64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + static_cast<uintptr_t>(bytes > 0 ? bytes : 0)};
+}
+bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(int status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+        default: return "KDA_UNKNOWN_STATUS";
+    }
+}
+
+int kda_version(void) { return kVersion; }
+
+int kda_gate(const float* A, const void* z, int z_dtype, void* g, int g_dtype, int64_t n_tokens,
+             int32_t H, int32_t dk, float g_min, void* stream) {
+    if (!valid_dtype(z_dtype) || !valid_dtype(g_dtype) || n_tokens < 0 || H < 1 || dk < 1)
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(g_min) || !(g_min >= -5.0f && g_min < 0.0f)) return KDA_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return KDA_OK;
+    if (!A || !z || !g) return KDA_ERR_INVALID_ARGUMENT;
+    const int64_t n = n_tokens * H * dk;
+    const Range rg = range(g, n * esize(g_dtype));
+    if (overlap(rg, range(z, n * esize(z_dtype))) || overlap(rg, range(A, int64_t(H) * dk * 4)))
+        return KDA_ERR_INVALID_ARGUMENT;
+    return from_hip(kda::launch_gate(A, z, z_dtype, g, g_dtype, n_tokens, H, dk, g_min,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t kda_chunk_fwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
+                                    int32_t dv, int32_t chunk) {
+    if (n_seqs < 1 || total_tokens < 0 || H < 1 || !supported_d(dk) || !supported_d(dv) ||
+        chunk != 64)
+        return 0;
+    return kda::chunk_workspace_bytes(n_seqs, total_tokens, H, dk, dv);
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, int in_dtype,
+                  const void* g, int g_dtype, const float* initial_state, float* final_state,
+                  const int32_t* cu_seqlens, void* o, int o_dtype, int32_t B, int64_t T,
+                  int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, int32_t chunk, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(in_dtype) || !valid_dtype(g_dtype) || !valid_dtype(o_dtype))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (B < 1 || T < 0 || n_seqs < 1 || H < 1 || dk < 1 || dv < 1 || !std::isfinite(scale))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (cu_seqlens ? (B != 1) : (n_seqs != B)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_d(dk) || !supported_d(dv) || chunk != 64) return KDA_ERR_UNSUPPORTED;
+    const int64_t ntok = int64_t(B) * T;
+    if (ntok > 0 && (!q || !k || !v || !beta || !g || !o)) return KDA_ERR_INVALID_ARGUMENT;
+    const size_t need = kda::chunk_workspace_bytes(n_seqs, ntok, H, dk, dv);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE;
+
+    const int64_t state_bytes = int64_t(n_seqs) * H * dk * dv * 4;
+    const Range r_q = range(q, ntok * H * dk * esize(in_dtype));
+    const Range r_k = range(k, ntok * H * dk * esize(in_dtype));
+    const Range r_v = range(v, ntok * H * dv * esize(in_dtype));
+    const Range r_b = range(beta, ntok * H * esize(in_dtype));
+    const Range r_g = range(g, ntok * H * dk * esize(g_dtype));
+    const Range r_o = range(o, ntok * H * dv * esize(o_dtype));
+    const Range r_h0 = range(initial_state, initial_state ? state_bytes : 0);
+    const Range r_hT = range(final_state, final_state ? state_bytes : 0);
+    const Range r_cu = range(cu_seqlens, cu_seqlens ? int64_t(n_seqs + 1) * 4 : 0);
+    const Range r_ws = range(workspace, int64_t(workspace_bytes));
+    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_h0, r_hT, r_cu, r_ws})
+        if (overlap(r_o, x)) return KDA_ERR_INVALID_ARGUMENT;
+    // the final state may be the initial state itself, but must not partly overlap it
+    if (initial_state && final_state && initial_state != final_state && overlap(r_h0, r_hT))
+        return KDA_ERR_INVALID_ARGUMENT;
+    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_cu, r_ws})
+        if (overlap(r_hT, x)) return KDA_ERR_INVALID_ARGUMENT;
+
+    kda::ChunkArgs a{};
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
+    a.h0 = initial_state; a.hT = final_state; a.cu = cu_seqlens; a.o = o;
+    a.in_dtype = in_dtype; a.g_dtype = g_dtype; a.o_dtype = o_dtype;
+    a.B = B; a.T = T; a.n_seqs = n_seqs; a.H = H; a.dk = dk; a.dv = dv;
+    a.scale = scale; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return from_hip(kda::launch_chunk(a, static_cast<hipStream_t>(stream)));
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const void* beta, int in_dtype,
+                    const void* g, int g_dtype, float* state, void* o, int o_dtype, int32_t N,
+                    int32_t H, int32_t dk, int32_t dv, float scale, void* stream) {
+    if (!valid_dtype(in_dtype) || !valid_dtype(g_dtype) || !valid_dtype(o_dtype))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (N < 0 || H < 1 || dk < 1 || dv < 1 || !std::isfinite(scale)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_d(dk) || !supported_d(dv)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !beta || !g || !state || !o) return KDA_ERR_INVALID_ARGUMENT;
+    const int64_t units = int64_t(N) * H;
+    const Range r_o = range(o, units * dv * esize(o_dtype));
+    const Range r_s = range(state, units * dk * dv * 4);
+    const Range ins[] = {range(q, units * dk * esize(in_dtype)), range(k, units * dk * esize(in_dtype)),
+                         range(v, units * dv * esize(in_dtype)), range(beta, units * esize(in_dtype)),
+                         range(g, units * dk * esize(g_dtype))};
+    for (const Range& x : ins)
+        if (overlap(r_o, x) || overlap(r_s, x)) return KDA_ERR_INVALID_ARGUMENT;
+    if (overlap(r_o, r_s)) return KDA_ERR_INVALID_ARGUMENT;
+    return from_hip(kda::launch_decode(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype, N,
+                                       H, dk, dv, scale, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// kda_decode.hip -- one-token recurrent update of N independent KDA states, in place.
+//
+// Pages: "Архитектура Kimi K3: как открытая модель с миллионным контекстом конкурирует с
+// лидерами рынка" (bagrov.by), § "Как архитектура Kimi K3 удерживает миллион токенов
+// контекста" (fixed-size state, delta-rule overwrite with write strength beta and forget
+// factor alpha); "Как устроена Kimi K3: …" (savepearlharbor.com), § "Как обслуживать два
+// разных кеша" (the cost of a decode step is reading the large recurrent state).
+//
+// Per (sequence, head), with alpha = exp(g):
+//     a = S^T (alpha * k),  b = S^T (alpha * q)          one read of S, reductions over d_k
+//     u = v - a,            o = scale * (b + beta * (k . q) * u)
+//     S <- Diag(alpha) S + beta k u^T                     one write of S
+// (o follows from o = S_new^T q = S^T Diag(alpha) q + beta u (k . q).)
+//
+// Layout: one 256-lane workgroup per (sequence, head).  Lane t owns four consecutive state
+// columns (16-byte loads/stores) of d_k / (256 / (d_v / 4)) consecutive rows, so each row is
+// read by d_v/4 lanes as one contiguous segment.  Partial column sums meet in LDS.  The state
+// stays in registers between the read and the write; HBM sees it exactly once each way.
+#include "kda_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+template <int DK, int DV, int IDT, int GDT, int ODT>
+__global__ void __launch_bounds__(256) decode_kernel(const void* __restrict__ q,
+                                                     const void* __restrict__ k,
+                                                     const void* __restrict__ v,
+                                                     const void* __restrict__ beta,
+                                                     const void* __restrict__ g,
+                                                     float* __restrict__ state,
+                                                     void* __restrict__ o, float scale) {
+    constexpr int CG = DV / 4;    // lanes per state row
+    constexpr int RG = 256 / CG;  // row groups
+    constexpr int RPT = DK / RG;  // rows per lane
+    static_assert(RPT >= 1 && RG * RPT == DK, "shape");
+
+    __shared__ float s_alpha[DK], s_ak[DK], s_aq[DK], s_k[DK];
+    __shared__ float4 s_red_a[RG][CG];
+    __shared__ float4 s_red_b[RG][CG];
+    __shared__ float s_kq[4];
+
+    const int64_t unit = blockIdx.x;  // sequence * H + head
+    const int t = threadIdx.x;
+    const int cg = t % CG, rg = t / CG;
+    float* S = state + unit * (DK * DV);
+
+    // Issue the whole state read first.
+    float4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        s[i] = *reinterpret_cast<const float4*>(S + (rg * RPT + i) * DV + 4 * cg);
+
+    float kq = 0.0f;
+    if (t < DK) {
+        const float a = expf(load_as_f32<GDT>(g, unit * DK + t));
+        const float kk = load_as_f32<IDT>(k, unit * DK + t);
+        const float qq = load_as_f32<IDT>(q, unit * DK + t);
+        s_alpha[t] = a;
+        s_ak[t] = a * kk;
+        s_aq[t] = a * qq;
+        s_k[t] = kk;
+        kq = kk * qq;
+    }
+    // k . q over the first DK lanes (wavefront reduction, then one value per wave)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) kq += __shfl_xor(kq, off, 64);
+    if ((t & 63) == 0) s_kq[t >> 6] = kq;
+    __syncthreads();
+
+    float4 pa = make_float4(0.f, 0.f, 0.f, 0.f), pb = pa;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg * RPT + i;
+        const float ak = s_ak[r], aq = s_aq[r];
+        pa.x += ak * s[i].x; pa.y += ak * s[i].y; pa.z += ak * s[i].z; pa.w += ak * s[i].w;
+        pb.x += aq * s[i].x; pb.y += aq * s[i].y; pb.z += aq * s[i].z; pb.w += aq * s[i].w;
+    }
+    s_red_a[rg][cg] = pa;
+    s_red_b[rg][cg] = pb;
+    __syncthreads();
+
+    float4 A4 = make_float4(0.f, 0.f, 0.f, 0.f), B4 = A4;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+        const float4 x = s_red_a[r][cg], y = s_red_b[r][cg];
+        A4.x += x.x; A4.y += x.y; A4.z += x.z; A4.w += x.w;
+        B4.x += y.x; B4.y += y.y; B4.z += y.z; B4.w += y.w;
+    }
+    const float kqs = s_kq[0] + s_kq[1] + s_kq[2] + s_kq[3];
+    const float bt = load_as_f32<IDT>(beta, unit);
+    const float4 vv = load4_as_f32<IDT>(v, unit * DV + 4 * cg);
+    const float4 u = make_float4(vv.x - A4.x, vv.y - A4.y, vv.z - A4.z, vv.w - A4.w);
+    if (rg == 0) {
+        const float c = bt * kqs;
+        const float4 oo = make_float4(scale * (B4.x + c * u.x), scale * (B4.y + c * u.y),
+                                      scale * (B4.z + c * u.z), scale * (B4.w + c * u.w));
+        store4_from_f32<ODT>(o, unit * DV + 4 * cg, oo);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg * RPT + i;
+        const float al = s_alpha[r], bk = bt * s_k[r];
+        float4 x = s[i];
+        x.x = al * x.x + bk * u.x;
+        x.y = al * x.y + bk * u.y;
+        x.z = al * x.z + bk * u.z;
+        x.w = al * x.w + bk * u.w;
+        *reinterpret_cast<float4*>(S + r * DV + 4 * cg) = x;
+    }
+}
+
+template <int DK, int DV, int IDT, int GDT, int ODT>
+static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* beta,
+                                  const void* g, float* state, void* o, int32_t N, int32_t H,
+                                  float scale, hipStream_t stream) {
+    const int64_t units = static_cast<int64_t>(N) * H;
+    hipLaunchKernelGGL((decode_kernel<DK, DV, IDT, GDT, ODT>), dim3(static_cast<unsigned>(units)),
+                       dim3(256), 0, stream, q, k, v, beta, g, state, o, scale);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t dispatch_dtypes(const void* q, const void* k, const void* v, const void* beta,
+                                  int idt, const void* g, int gdt, float* state, void* o, int odt,
+                                  int32_t N, int32_t H, float scale, hipStream_t s) {
+#define KDA_DEC(I, G, O)                                                                       \
+    if (idt == I && gdt == G && odt == O)                                                      \
+        return launch_decode_t<DK, DV, I, G, O>(q, k, v, beta, g, state, o, N, H, scale, s);
+    KDA_DEC(KDA_BF16, KDA_BF16, KDA_BF16)
+    KDA_DEC(KDA_BF16, KDA_BF16, KDA_F32)
+    KDA_DEC(KDA_BF16, KDA_F32, KDA_BF16)
+    KDA_DEC(KDA_BF16, KDA_F32, KDA_F32)
+    KDA_DEC(KDA_F32, KDA_BF16, KDA_BF16)
+    KDA_DEC(KDA_F32, KDA_BF16, KDA_F32)
+    KDA_DEC(KDA_F32, KDA_F32, KDA_BF16)
+    KDA_DEC(KDA_F32, KDA_F32, KDA_F32)
+#undef KDA_DEC
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, const void* beta,
+                         int in_dtype, const void* g, int g_dtype, float* state, void* o,
+                         int o_dtype, int32_t N, int32_t H, int32_t dk, int32_t dv, float scale,
+                         hipStream_t stream) {
+    if (dk == 128 && dv == 128)
+        return dispatch_dtypes<128, 128>(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype, N, H, scale, stream);
+    if (dk == 128 && dv == 64)
+        return dispatch_dtypes<128, 64>(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype, N, H, scale, stream);
+    if (dk == 64 && dv == 128)
+        return dispatch_dtypes<64, 128>(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype, N, H, scale, stream);
+    return dispatch_dtypes<64, 64>(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype, N, H, scale, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,42 @@
+// kda_internal.hpp -- launchers the C ABI layer calls after it has validated the arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+hipError_t launch_gate(const float* A, const void* z, int z_dtype, void* g, int g_dtype,
+                       int64_t n_tokens, int32_t H, int32_t dk, float g_min, hipStream_t stream);
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, const void* beta,
+                         int in_dtype, const void* g, int g_dtype, float* state, void* o,
+                         int o_dtype, int32_t N, int32_t H, int32_t dk, int32_t dv, float scale,
+                         hipStream_t stream);
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* beta;
+    const void* g;
+    const float* h0;       // initial state or nullptr
+    float* hT;             // final state or nullptr
+    const int32_t* cu;     // device cu_seqlens or nullptr
+    void* o;
+    int in_dtype, g_dtype, o_dtype;
+    int32_t B;
+    int64_t T;
+    int32_t n_seqs, H, dk, dv;
+    float scale;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+size_t chunk_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
+                             int32_t dv);
+
+hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream);
+
+}  // namespace kda

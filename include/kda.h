@@ -1,0 +1,133 @@
+/*
+ * kda.h -- C ABI of libkda.so, the MI355X (gfx950) implementation of the Kimi Delta Attention
+ * (KDA) forward pass: the forget gate, chunked prefill and the single-token decode step.
+ *
+ * Pages the operations come from (titles as published):
+ *   [bagrov] "Архитектура Kimi K3: как открытая модель с миллионным контекстом конкурирует с
+ *            лидерами рынка" (bagrov.by)
+ *   [habr]   "Как устроена Kimi K3: 2,8 трлн параметров, линейное внимание и агенты на миллион
+ *            токенов" (savepearlharbor.com)
+ *
+ * The recurrence, per (sequence, head), with a fixed d_k x d_v state S (key channel = row):
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,   o_t = scale * S_t^T q_t,
+ *     alpha_t = exp(g_t) (one factor per key channel).
+ * The state has a fixed size, each token partly erases what is stored along its key and writes
+ * its value there, with write strength beta and forget factor alpha ([bagrov, § Как архитектура
+ * Kimi K3 удерживает миллион токенов контекста]); the forget is per channel and acts before
+ * the write ([habr, § Последовательность: три KDA на один глобальный MLA]).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE memory owned by the caller; the library keeps no pointer
+ *     after returning and allocates no device memory.
+ *   - Tensors are contiguous, row-major:
+ *       q, k, g, z : [B, T, H, d_k]          v, o : [B, T, H, d_v]          beta : [B, T, H]
+ *       state      : [N, H, d_k, d_v] fp32 (row = key channel, d_v contiguous)
+ *     Packed variable-length batches use B = 1, T = total tokens and device cu_seqlens[N+1].
+ *     The decode step drops T.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL = the
+ *     default stream).  There is no host synchronisation and the host never reads device data.
+ *     Buffers must stay alive until the stream has passed the work.
+ *   - Every call returns a kda_status; nothing is printed and nothing aborts.  Host-checkable
+ *     argument errors are reported before any device work is enqueued.  Device-resident
+ *     preconditions (g in [-5, 0], well-formed cu_seqlens) are the caller's contract and are not
+ *     checked; violating them gives undefined (but memory-safe) results.
+ *   - Calls are stateless and reentrant.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, bad dtype, aliasing     */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented: d_k/d_v not in {64,128}, ... */
+    KDA_ERR_WORKSPACE = 3,        /* workspace smaller than kda_chunk_fwd_workspace_size()   */
+    KDA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed              */
+} kda_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *kda_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int kda_version(void);
+
+/*
+ * kda_gate -- forget-gate log-decay, [habr, § Последовательность]:
+ *     g[t,h,c] = g_min * sigmoid(exp(A[h,c]) * z[t,h,c]),   sigmoid(x) = 1 / (1 + exp(-x)),
+ * so alpha = exp(g) lies in [e^g_min, 1].  The pages fix g_min = -5; this bound is what keeps
+ * every causal 16-token block of the chunked prefill inside the bf16/fp32 exponent range.
+ *   A       : [H, d_k] fp32, device.
+ *   z       : [n_tokens, H, d_k] in z_dtype (KDA_F32 or KDA_BF16), device.
+ *   g       : [n_tokens, H, d_k] in g_dtype (KDA_F32 or KDA_BF16, round-to-nearest-even), device;
+ *             must not overlap z or A.
+ *   n_tokens: >= 0 (0 is a no-op); H, d_k >= 1.
+ *   g_min   : must lie in [-5, 0); other values return KDA_ERR_UNSUPPORTED.
+ */
+int kda_gate(const float *A, const void *z, int z_dtype, void *g, int g_dtype, int64_t n_tokens,
+             int32_t H, int32_t dk, float g_min, void *stream);
+
+/*
+ * Workspace bytes kda_chunk_fwd needs for these sizes (0 when none).  Never fails; returns 0
+ * for invalid sizes (kda_chunk_fwd then reports the error).
+ */
+size_t kda_chunk_fwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
+                                    int32_t dv, int32_t chunk);
+
+/*
+ * kda_chunk_fwd -- chunked prefill of the recurrence above over whole sequences.
+ * Tokens inside a chunk are handled together and the state is carried from chunk to chunk
+ * ([bagrov, § Уровень чипа: специализированное ядро FlashKDA]); with g >= -5 every causal
+ * 16-token block, diagonal ones included, is a dense matrix product
+ * ([habr, § Последовательность]).
+ *   q, k, v, beta : inputs in in_dtype (KDA_F32 or KDA_BF16), layouts above.
+ *   g             : [B, T, H, d_k] log-decay in g_dtype (KDA_F32 recommended; KDA_BF16 allowed),
+ *                   values must lie in [-5, 0] (caller contract).
+ *   initial_state : [N, H, d_k, d_v] fp32 or NULL (= zeros); never written unless it is also
+ *                   final_state.
+ *   final_state   : [N, H, d_k, d_v] fp32 or NULL; may equal initial_state (in-place update)
+ *                   but must not partially overlap it.
+ *   cu_seqlens    : NULL for B fixed-length sequences of T tokens (then n_seqs must equal B), or
+ *                   device int32 [n_seqs + 1] offsets of a packed batch (then B must be 1,
+ *                   cu_seqlens[0] = 0, non-decreasing, cu_seqlens[n_seqs] = T; caller contract).
+ *                   Empty sequences are allowed: their final state is their initial state.
+ *   o             : [B, T, H, d_v] in o_dtype (KDA_F32 or KDA_BF16); must not overlap any input.
+ *   T             : >= 0 (T = 0 only copies initial_state to final_state, or zeroes it).
+ *   dk, dv        : 64 or 128 each.  chunk: must be 64.  scale: any finite value (1 = none).
+ *   workspace     : device buffer of at least kda_chunk_fwd_workspace_size(...) bytes (may be
+ *                   NULL when that size is 0).
+ * Results match the token-by-token definition up to rounding: the kernels evaluate the chunked
+ * form with fp32 accumulation and split-precision matrix products.
+ */
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *beta, int in_dtype,
+                  const void *g, int g_dtype, const float *initial_state, float *final_state,
+                  const int32_t *cu_seqlens, void *o, int o_dtype, int32_t B, int64_t T,
+                  int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, int32_t chunk, float scale,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_decode_step -- one token of the recurrence for N independent sequences, updating each
+ * state in place.  One pass reads S once and writes it once: reading the large recurrent
+ * state is this step's cost ([habr, § Как обслуживать два разных кеша]).
+ *   q, k, g : [N, H, d_k]; v : [N, H, d_v]; beta : [N, H]; q, k, v, beta in in_dtype, g in g_dtype
+ *             (KDA_F32 or KDA_BF16 each); g must lie in [-5, 0] (caller contract).
+ *   state   : [N, H, d_k, d_v] fp32, read and overwritten in place.
+ *   o       : [N, H, d_v] in o_dtype; must not overlap any input or the state.
+ *   N >= 0 (0 is a no-op); H >= 1; dk, dv: 64 or 128 each.
+ */
+int kda_decode_step(const void *q, const void *k, const void *v, const void *beta, int in_dtype,
+                    const void *g, int g_dtype, float *state, void *o, int o_dtype, int32_t N,
+                    int32_t H, int32_t dk, int32_t dv, float scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,111 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/kda.h declares, and
+rejects host-checkable argument errors before enqueuing any device work.  The pointers passed
+here are never dereferenced: each call below fails validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_60_amd import kda as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "kda.h")
+
+FAKE = 1 << 40          # a host-side address-like integer; validation fails before any use
+INV, UNS, WS = 1, 2, 3
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return K.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(K.EXPORTED), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert K.kda_status_string(0) == "KDA_OK"
+    assert K.kda_status_string(1) == "KDA_ERR_INVALID_ARGUMENT"
+    assert K.kda_status_string(2) == "KDA_ERR_UNSUPPORTED"
+    assert K.kda_status_string(3) == "KDA_ERR_WORKSPACE"
+    assert K.kda_status_string(4) == "KDA_ERR_HIP"
+    assert K.kda_status_string(99) == "KDA_UNKNOWN_STATUS"
+    assert K.kda_version() >= 100
+
+
+def P(x):
+    return ctypes.c_void_p(x) if x else None
+
+
+def chunk(lib, q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, beta=FAKE + 0x30000000,
+          in_dt=1, g=FAKE + 0x40000000, g_dt=0, h0=0, hT=0, cu=0, o=FAKE + 0x50000000, o_dt=1,
+          B=1, T=128, N=1, H=2, dk=128, dv=128, chunk=64, scale=1.0, ws=0, ws_bytes=0):
+    return lib.kda_chunk_fwd(P(q), P(k), P(v), P(beta), in_dt, P(g), g_dt, P(h0), P(hT), P(cu),
+                             P(o), o_dt, B, T, N, H, dk, dv, chunk, scale, P(ws), ws_bytes, None)
+
+
+def test_chunk_fwd_rejects(lib):
+    assert chunk(lib, in_dt=7) == INV
+    assert chunk(lib, g_dt=-1) == INV
+    assert chunk(lib, o_dt=2) == INV
+    assert chunk(lib, B=0) == INV
+    assert chunk(lib, T=-1) == INV
+    assert chunk(lib, H=0) == INV
+    assert chunk(lib, N=2) == INV                       # fixed-length: N must equal B
+    assert chunk(lib, B=2, N=2, cu=FAKE + 0x60000000) == INV   # packed batch needs B == 1
+    assert chunk(lib, dk=96) == UNS
+    assert chunk(lib, dv=256) == UNS
+    assert chunk(lib, chunk=32) == UNS
+    assert chunk(lib, q=0) == INV
+    assert chunk(lib, o=0) == INV
+    assert chunk(lib, scale=float("nan")) == INV
+    assert chunk(lib, o=FAKE + 0x100) == INV            # o overlaps q
+    assert chunk(lib, h0=FAKE + 0x70000000, hT=FAKE + 0x70000000 + 4096) == INV  # partial overlap
+    assert chunk(lib, hT=FAKE + 0x10000010) == INV      # final state overlaps k
+
+
+def test_workspace_size(lib):
+    assert K.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128) >= 0
+    assert K.kda_chunk_fwd_workspace_size(1, 4096, 16, 96, 128) == 0
+    assert K.kda_chunk_fwd_workspace_size(0, 4096, 16, 128, 128) == 0
+
+
+def test_gate_rejects(lib):
+    g = lambda **kw: lib.kda_gate(P(kw.get("A", FAKE)), P(kw.get("z", FAKE + 0x1000000)),  # noqa: E731
+                                  kw.get("zdt", 1), P(kw.get("g", FAKE + 0x2000000)),
+                                  kw.get("gdt", 0), kw.get("n", 10), kw.get("H", 2),
+                                  kw.get("dk", 8), kw.get("gmin", -5.0), None)
+    assert g(zdt=3) == INV
+    assert g(n=-1) == INV
+    assert g(H=0) == INV
+    assert g(gmin=-6.0) == UNS
+    assert g(gmin=0.0) == UNS
+    assert g(gmin=float("inf")) == UNS
+    assert g(A=0) == INV
+    assert g(g=FAKE + 0x1000000 + 8) == INV             # g overlaps z
+    assert g(n=0, A=0, z=0, g=0) == 0                   # nothing to do
+
+
+def test_decode_rejects(lib):
+    d = lambda **kw: lib.kda_decode_step(  # noqa: E731
+        P(kw.get("q", FAKE)), P(FAKE + 0x1000000), P(FAKE + 0x2000000), P(FAKE + 0x3000000),
+        kw.get("idt", 1), P(FAKE + 0x4000000), kw.get("gdt", 1), P(kw.get("S", FAKE + 0x10000000)),
+        P(kw.get("o", FAKE + 0x5000000)), kw.get("odt", 1), kw.get("N", 4), kw.get("H", 2),
+        kw.get("dk", 128), kw.get("dv", 128), 1.0, None)
+    assert d(idt=5) == INV
+    assert d(N=-1) == INV
+    assert d(dk=32) == UNS
+    assert d(q=0) == INV
+    assert d(o=FAKE + 0x10000000 + 64) == INV           # o overlaps the state
+    assert d(N=0, q=0) == 0                              # nothing to do

@@ -1,0 +1,108 @@
+"""GPU parity: kda_gate and kda_decode_step against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_60_amd import inputs
+from gated_delta_rule_60_amd import kda as K
+from kda_testutil import DEV, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("zdt,gdt,shape", [
+    (torch.bfloat16, torch.float32, (3, 77, 4, 128)),
+    (torch.float32, torch.float32, (1, 256, 2, 64)),
+    (torch.bfloat16, torch.bfloat16, (2, 33, 3, 128)),
+    (torch.float32, torch.float32, (5, 3, 7)),          # d_k not a multiple of 4: scalar path
+])
+def test_gate_parity(zdt, gdt, shape):
+    say(f"gate parity z={zdt} g={gdt} shape={shape}")
+    gen = torch.Generator("cpu").manual_seed(7)
+    H, dk = shape[-2], shape[-1]
+    A = torch.randn((H, dk), generator=gen) * 0.5
+    z = (torch.randn(shape, generator=gen) * 3).to(zdt)
+    z[..., 0] = 0.0                                     # g = -2.5 exactly
+    ref = oracle.gate(A, z)
+    g = K.kda_gate(A.to(DEV), z.to(DEV), g_dtype=gdt)
+    torch.cuda.synchronize()
+    got = g.double().cpu().numpy()
+    if gdt == torch.float32:
+        assert np.abs(got - ref).max() <= 2e-6, np.abs(got - ref).max()
+        assert np.all(got[..., 0] == -2.5)
+    else:  # bf16: within one bf16 ulp of the exact value
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+    assert got.max() <= 0.0 and got.min() >= -5.0
+
+
+def test_gate_full_size_sampled():
+    """The long-prefill shape (268M gates), sampled rows against the oracle."""
+    cfg = inputs.config("prefill_long")
+    say("gate full size", cfg)
+    gen = torch.Generator("cpu").manual_seed(11)
+    A = torch.randn((cfg.H, cfg.dk), generator=gen) * 0.5
+    z = (torch.randn((1, cfg.T, cfg.H, cfg.dk), generator=gen) * cfg.z_std).to(torch.bfloat16)
+    g = K.kda_gate(A.to(DEV), z.to(DEV))
+    torch.cuda.synchronize()
+    rows = torch.randint(0, cfg.T, (512,), generator=gen)
+    ref = oracle.gate(A, z[0, rows])
+    got = g[0, rows.to(DEV)].double().cpu().numpy()
+    assert np.abs(got - ref).max() <= 2e-6
+
+
+def _decode_run(cfg, steps, o_dtype=torch.float32, n_check=None):
+    d = inputs.make_decode(cfg, steps=steps)
+    N = cfg.B
+    g_all = torch.from_numpy(oracle.gate(d["A"], d["z"])).to(torch.bfloat16 if cfg.dtype == "bf16"
+                                                            else torch.float32)
+    S_gpu = d["S0"].to(DEV).clone()
+    sel = np.arange(N) if n_check is None else np.unique(
+        np.random.default_rng(0).choice(N, n_check, replace=False))
+    S_ref = d["S0"][sel].double().numpy().copy()
+    worst_o = 0.0
+    dev = {k: d[k].to(DEV) for k in ("q", "k", "v", "beta")}
+    g_dev = g_all.to(DEV)
+    for t in range(steps):
+        o = K.kda_decode_step(dev["q"][t], dev["k"][t], dev["v"][t], dev["beta"][t], g_dev[t],
+                              S_gpu, o_dtype=o_dtype)
+        o_ref = oracle.decode_step(d["q"][t][sel], d["k"][t][sel], d["v"][t][sel],
+                                   d["beta"][t][sel], g_all[t][sel], S_ref)
+        worst_o = max(worst_o, rel_err(o[torch.from_numpy(sel).to(DEV)], o_ref))
+    torch.cuda.synchronize()
+    s_err = rel_err(S_gpu[torch.from_numpy(sel).to(DEV)], S_ref)
+    return worst_o, s_err
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (64, 64, "f32"), (128, 64, "bf16"),
+                                         (64, 128, "f32")])
+def test_decode_parity_small(dk, dv, dtype):
+    cfg = inputs.config("decode", B=6, H=3, dk=dk, dv=dv, dtype=dtype)
+    say("decode parity", cfg)
+    eo, es = _decode_run(cfg, steps=8)
+    say(f"  o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= 1e-5 and es <= 1e-5
+
+
+def test_decode_parity_full_size_sampled():
+    """256 sequences x 32 heads x 64 steps, in place; 8 sequences (256 states) checked."""
+    cfg = inputs.config("decode")
+    say("decode parity full size", cfg)
+    eo, es = _decode_run(cfg, steps=cfg.decode_steps, n_check=8)
+    say(f"  o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= 2e-3 and es <= 2e-3
+    assert eo <= 1e-5 and es <= 1e-5     # fp32 arithmetic throughout: far inside the bound
+
+
+def test_decode_bf16_output_is_rounded_fp32():
+    cfg = inputs.config("decode", B=4, H=2)
+    d = inputs.make_decode(cfg, steps=1)
+    g = torch.from_numpy(oracle.gate(d["A"], d["z"])).to(torch.bfloat16).to(DEV)
+    args = [d[k][0].to(DEV) for k in ("q", "k", "v", "beta")]
+    S1 = d["S0"].to(DEV).clone()
+    S2 = S1.clone()
+    o32 = K.kda_decode_step(*args, g[0], S1, o_dtype=torch.float32)
+    o16 = K.kda_decode_step(*args, g[0], S2, o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o32.to(torch.bfloat16), o16)
+    assert torch.equal(S1, S2)
