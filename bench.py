@@ -1,0 +1,201 @@
+"""Benchmark of the KDA forward pass on one MI355X.
+
+One step = one pass of the prefill hot path over the bf16 prefill workload (B=4, H=16, T=4096,
+d_k=d_v=128, chunk 64, random fp32 initial state): kda_gate (z -> fp32 g) then kda_chunk_fwd
+(o in bf16, final state in fp32).  Inputs are synthetic (seeded generators, the workload's shapes
+and distributions) and resident in HBM before the timed region starts.  The decode workload
+(256 sequences x 32 heads, 64 in-place steps) is timed in the same run and reported under
+"decode".
+
+Prints ONE JSON line.  ``value`` is prefill tokens/s (B*T tokens per step / step time).
+``roofline`` describes the dominant kernel (the fused chunk kernel) with its algorithmic bytes
+per launch divided by its mean launch time, measured with HIP events on the launch stream.
+``cpu_baseline`` is the fp64 oracle (test infrastructure) timed on this host's cores on the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+HBM_PEAK = 8.0e12           # B/s, MI355X HBM3E
+BF16_PEAK = 2516.6e12       # FLOP/s dense
+# Algorithmic work per (token, head) at d_k = d_v = 128, chunk 64 (what the method must move and
+# compute, not what the kernels execute):
+#   bytes: q, k, v bf16 (3*256) + g fp32 (512) + beta bf16 (2) + o bf16 (256) = 1538
+#   FLOP : 6 dk dv + C (3 dk + 2 dv) + C^2 / 3 = 140,629
+PREFILL_BYTES_PER_TH = 1538
+PREFILL_FLOP_PER_TH = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128) + 64 * 64 / 3
+STATE_BYTES = 128 * 128 * 4
+# Decode per (sequence, head, step): state read + write (2 * 64 KiB) + q, k, v, g bf16 + beta + o
+DECODE_BYTES_PER_UNIT = 2 * STATE_BYTES + 4 * 128 * 2 + 2 + 128 * 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-passes", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(the path would shard over sequences and heads, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from gated_delta_rule_60_amd import inputs
+    from gated_delta_rule_60_amd import kda as K
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K.load_library()
+
+    # ------------------------------------------------------------------ prefill workload
+    cfg = inputs.config("prefill_bf16")
+    log("generating", cfg)
+    d = inputs.make_prefill(cfg)
+    B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
+    q, k, v, beta, z = (d[x].to(dev) for x in ("q", "k", "v", "beta", "z"))
+    A, S0 = d["A"].to(dev), d["S0"].to(dev)
+    g = torch.empty(z.shape, dtype=torch.float32, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty_like(S0)
+    stream = torch.cuda.current_stream()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    gate_ms, chunk_ms = [], []
+
+    def step(timed):
+        if timed:
+            ev[0].record(stream)
+        K.kda_gate(A, z, g=g, stream=stream)
+        if timed:
+            ev[1].record(stream)
+        K.kda_chunk_fwd(q, k, v, beta, g, initial_state=S0, final_state=hT, o=o, stream=stream)
+        if timed:
+            ev[2].record(stream)
+            ev[2].synchronize()
+            gate_ms.append(ev[0].elapsed_time(ev[1]))
+            chunk_ms.append(ev[1].elapsed_time(ev[2]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    # wall-clock over exactly K steps
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    # per-kernel durations with HIP events on the launch stream (separate pass, same work)
+    for _ in range(args.steps):
+        step(True)
+    chunk_avg = sum(chunk_ms) / len(chunk_ms)
+    gate_avg = sum(gate_ms) / len(gate_ms)
+
+    tokens = B * T
+    th = tokens * H
+    chunk_bytes = th * PREFILL_BYTES_PER_TH + 2 * B * H * STATE_BYTES
+    chunk_flop = th * PREFILL_FLOP_PER_TH
+    achieved = chunk_bytes / (chunk_avg * 1e-3)
+    value = tokens / (ms_per_step * 1e-3)
+
+    # ------------------------------------------------------------------ decode workload
+    dcfg = inputs.config("decode")
+    log("generating", dcfg)
+    dd = inputs.make_decode(dcfg)
+    N, steps = dcfg.B, dcfg.decode_steps
+    dq, dk_, dv_, db, dz = (dd[x].to(dev) for x in ("q", "k", "v", "beta", "z"))
+    dA = dd["A"].to(dev)
+    dg = K.kda_gate(dA, dz, g_dtype=torch.bfloat16)     # inputs prepared before timing
+    Sd = dd["S0"].to(dev)
+    od = torch.empty((N, dcfg.H, dcfg.dv), dtype=torch.bfloat16, device=dev)
+
+    def decode_pass():
+        for t in range(steps):
+            K.kda_decode_step(dq[t], dk_[t], dv_[t], db[t], dg[t], Sd, o=od, stream=stream)
+
+    decode_pass()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.decode_passes):
+        decode_pass()
+    e1.record(stream)
+    e1.synchronize()
+    dec_ms_step = e0.elapsed_time(e1) / (args.decode_passes * steps)
+    dec_units = N * dcfg.H
+    dec_gbs = dec_units * DECODE_BYTES_PER_UNIT / (dec_ms_step * 1e-3)
+
+    # ------------------------------------------------------------------ CPU baseline (oracle)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("oracle baseline on host cores")
+        t1 = time.perf_counter()
+        g64 = oracle.gate(d["A"], d["z"])
+        _, _, used = oracle.forward(d["q"], d["k"], d["v"], d["beta"], g64, S0=d["S0"],
+                                    nthreads=args.cpu_threads, want_o=True)
+        cpu_s = time.perf_counter() - t1
+        cpu = {"value": round(tokens / cpu_s, 1), "unit": "tokens/s", "cores": int(used),
+               "kind": "oracle",
+               "sample": f"the whole prefill workload (gate + token loop, fp64), {cpu_s:.1f} s"}
+
+    out = {
+        "metric": "KDA prefill tokens/s (% bf16 MFMA peak) + decode state GB/s (% HBM peak)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "KDA chunked prefill, bf16 inputs / fp32 state, B=4 H=16 T=4096 "
+                               "d_k=d_v=128 chunk=64, gate included",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": dk,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
+                     "kernel": "chunk_fwd_kernel", "kernel_ms": round(chunk_avg, 4),
+                     "bytes_per_launch": chunk_bytes},
+        "mfma": {"canonical_tflops": round(chunk_flop / (chunk_avg * 1e-3) / 1e12, 2),
+                 "frac_bf16_peak": round(chunk_flop / (chunk_avg * 1e-3) / BF16_PEAK, 4)},
+        "gate_ms": round(gate_avg, 4),
+        "decode": {"seq_steps_per_s": round(N / (dec_ms_step * 1e-3), 1),
+                   "ms_per_step": round(dec_ms_step, 4),
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbs / 1e9, 1),
+                                "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                                "frac": round(dec_gbs / HBM_PEAK, 4), "traffic": None,
+                                "kernel": "decode_kernel",
+                                "bytes_per_launch": dec_units * DECODE_BYTES_PER_UNIT},
+                   "config": "256 sequences x 32 heads, d_k=d_v=128, fp32 state in place, "
+                             "bf16 q/k/v/beta/g, 64 steps"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
