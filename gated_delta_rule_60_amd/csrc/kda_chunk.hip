@@ -3,37 +3,39 @@
 // Pages (titles as published):
 //   [bagrov] "Архитектура Kimi K3: как открытая модель с миллионным контекстом конкурирует с
 //            лидерами рынка" (bagrov.by): § "Как архитектура Kimi K3 удерживает миллион токенов
-//            контекста" (state, delta rule, bounded forget factor), § "Уровень чипа:
-//            специализированное ядро FlashKDA" (tokens of a block in parallel, then the state is
-//            passed on, spread over independent heads).
+//            контекста" (fixed state, delta rule, bounded forget factor), § "Уровень чипа:
+//            специализированное ядро FlashKDA" (the tokens of a block are processed together,
+//            then the state is passed on, spread over independent heads).
 //   [habr]   "Как устроена Kimi K3: …" (savepearlharbor.com), § "Последовательность: три KDA на
-//            один глобальный MLA" (g = g_min*sigmoid(exp(A) z), g_min = -5 keeps the running decay
-//            products inside the bf16 range so every causal 16-token block, diagonal ones included,
+//            один глобальный MLA" (g = g_min*sigmoid(exp(A) z) with g_min = -5 keeps the running
+//            decay inside the bf16 range, so every causal 16-token block, diagonal ones included,
 //            is a dense matrix product).
 //
-// Chunk form (derived from the token recurrence; C = 64 tokens, chunk-entering state S):
-//   G_r = sum_{t<=r} g_t (per channel),  Kt = e^G * K,  Qt = e^G * Q,  Kb = e^{G_n - G} * K
-//   A[r,s] = beta_r sum_c k_rc k_sc e^{G_rc - G_sc}  (s < r),   P[r,s] = sum_c q_rc k_sc e^{G_rc - G_sc} (s <= r)
-//   W = (I + A)^{-1} beta*(V - Kt S)          (row r of W is beta_r times token r's innovation)
-//   O = scale * (Qt S + P W),                 S <- Diag(e^{G_n}) S + Kb^T W
+// Block form (derived from the token recurrence).  For a block of n <= 16 tokens entering with
+// state S, G_r = sum_{t<=r} g_t (per key channel, restarting at the block), G_15 its end value:
+//   Kt = e^G * K,  Qt = e^G * Q,  Kb = e^{G_15 - G} * K,  Kd = e^{-G} * K     (elementwise)
+//   A = beta * strict_lower(Kt Kd^T),  P = lower(Qt Kd^T)                  (16 x 16)
+//   T' = (I + A)^{-1} Diag(beta)                                            (UT transform)
+//   W  = T' (V - Kt S)        row r of W is beta_r times token r's delta-rule innovation
+//   O  = scale * (Qt S + P W),          S <- Diag(e^{G_15}) S + Kb^T W
+// Kt, Qt, Kb lie in [-1, 1] (factors <= 1); Kd's factor is at most e^{16*5} = e^80, inside the
+// bf16 / fp32 range (e^88.7): the bound on g is what makes the diagonal block a plain dense
+// product.  Successive blocks are chained through S, so the 64-token chunk of the interface is
+// four blocks: its 64 x 64 triangular system is solved blockwise, the coupling between blocks
+// going through the state.
 //
-// A and P are built per 16-row block b with the token before the block as reference R_b:
-//   diagonal tile:   (k_r e^{G_r - R_b}) . (k_s e^{R_b - G_s})       column factors in [1, e^80]
-//   tile b x j<b:    (k_r e^{G_r - R_b} e^{R_b - R_{j+1}}) . (k_s e^{R_{j+1} - G_s})   all factors <= 1
-// With g >= -5 a 16-token span decays by at most e^-80, so e^80 < bf16/fp32 max (e^88.7): the
-// diagonal tiles are plain dense MFMA tiles (split bf16 for range), no pairwise special case.
-//
-// Work split: one 256-lane workgroup per (sequence, head, block of 64 state columns).  Each of the
-// four waves owns 16 state columns for the whole sequence, in fp32 MFMA accumulators.  Per chunk:
-//   staging    lanes own (channel, 32 or 16 tokens): chunk cumsum, decay factors, scaled operands
-//              written once to LDS (2 exps per element)
-//   A/P        20 MFMA tiles (10 per matrix) shared by the waves (16x16x32, fp32 accumulate)
-//   T_bb       one wave inverts the four 16x16 unit-lower diagonal blocks of I + A (substitution)
-//   state      per wave: Y = Kt S, O = Qt S (16x16x32), W by blocked forward substitution
-//              (16x16x16), O += P W, S <- e^{G_n} S + Kb^T W; o stored straight from registers.
-// Precision: products whose operands are range-bounded use fp16 (11-bit significand) in one
-// pass; the diagonal A/P tiles (factors up to e^80), the triangular solve and P W use split bf16
-// (hi*hi + hi*lo + lo*hi).  For fp32 inputs every product is split bf16.
+// Work split: one 256-lane workgroup per (sequence, head, 64 state columns).  Each of the four
+// waves owns 16 state columns for the whole sequence, kept in fp32 MFMA accumulators.  Per
+// 64-token chunk:
+//   phase 1 (wave b handles block b): block-local cumsum by lane shuffles, decay factors and
+//           every MFMA operand written once to LDS in its final 16-bit format; A_b and P_b on
+//           MFMA; T'_b by substitution.  No workgroup barrier: a wave only reads what it wrote.
+//   phase 2 (every wave, its 16 columns, blocks 0..3 in order): Y = Kt S, O = Qt S, W, O += P W,
+//           o stored from registers, S <- e^{G_15} S + Kb^T W.
+// The next chunk's raw inputs are loaded into registers during phases 1 and 2.
+// Precision: operands that are range-bounded use fp16 (11-bit significand) in one pass; the
+// diagonal products (factors up to e^80), T' X and P W use split bf16 (hi*hi + hi*lo + lo*hi).
+// For fp32 inputs every product is split bf16.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -41,144 +43,157 @@ namespace kda {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int CH = 64;      // tokens per chunk
+constexpr int CH = 64;      // tokens per chunk (four 16-token blocks)
 constexpr int BV = 64;      // state columns per workgroup (16 per wave)
 constexpr int NTHR = 256;
-constexpr int LA = CH + 4;  // padded row length of the 64x64 A / P tiles (floats)
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// ---- MFMA wrappers --------------------------------------------------------------------------
-// 16x16x32: lane (m, q) = (lane % 16, lane / 16) supplies row m of A (column m of B) and eight
-// K-slots.  Throughout this file K-slot i of lane group q stands for K index
-//     i < 4 :  4q + i          i >= 4 :  16 + 4q + (i - 4)
-// (applied identically to both operands), so the two 16-row output tiles of an earlier MFMA,
-// whose lane (n, q) holds rows 4q..4q+3 each, form a B operand without any shuffle.
-__device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const __bf16 h = static_cast<__bf16>(x[i]);
-        hi[i] = h;
-        lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(h));
-    }
+// ---- LDS layouts ---------------------------------------------------------------------------
+// [64][DK] 16-bit arrays (token-major): 16-byte units of 8 channels, unit index XOR (row & 7)
+// so that the 16 rows of an MFMA fragment read fall in different banks.
+template <int DK>
+__device__ __forceinline__ int tok_major(int r, int c) {
+    return r * DK + ((((c >> 3) ^ (r & 7))) << 3) + (c & 7);
+}
+// [DK][64] 16-bit arrays (channel-major), same swizzle on units of 8 tokens.
+__device__ __forceinline__ int ch_major(int c, int t) {
+    return c * CH + ((((t >> 3) ^ (c & 7))) << 3) + (t & 7);
 }
 
-__device__ __forceinline__ f32x4 mma32_x3(const float (&a)[8], const float (&b)[8], f32x4 acc) {
-    bf16x8 ah, al, bh, bl;
-    split_bf16(a, ah, al);
-    split_bf16(b, bh, bl);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-    return acc;
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
-__device__ __forceinline__ f16x8 to_f16x8(const float (&x)[8]) {
-    f16x8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = static_cast<_Float16>(x[i]);
-    return r;
+// ---- MFMA wrappers (operands already in their 16-bit format) --------------------------------
+__device__ __forceinline__ f32x4 mfma32_bf16_x3(const bf16x8& ah, const bf16x8& al,
+                                                const bf16x8& bh, const bf16x8& bl, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_bf16_x3(const s16x4& ah, const s16x4& al,
+                                                const s16x4& bh, const s16x4& bl, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mma32_f16(const float (&a)[8], const float (&b)[8], f32x4 acc) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(to_f16x8(a), to_f16x8(b), acc, 0, 0, 0);
-}
-
-template <bool X3>
-__device__ __forceinline__ f32x4 mma32(const float (&a)[8], const float (&b)[8], f32x4 acc) {
-    if constexpr (X3) return mma32_x3(a, b, acc);
-    else return mma32_f16(a, b, acc);
-}
-
-// 16x16x16 (bf16, split): lane (m, q) holds K indices 4q..4q+3; the output layout equals the
-// B-operand layout, so a result feeds the next product directly.
-__device__ __forceinline__ void split_bf16_4(const float (&x)[4], s16x4& hi, s16x4& lo) {
+// four fp32 values -> bf16 hi/lo pairs (16x16x16 operand layout)
+__device__ __forceinline__ void split4(const f32x4& x, s16x4& hi, s16x4& lo) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const __bf16 h = static_cast<__bf16>(x[i]);
-        const __bf16 l = static_cast<__bf16>(x[i] - static_cast<float>(h));
-        hi[i] = __builtin_bit_cast(short, h);
-        lo[i] = __builtin_bit_cast(short, l);
+        const uint16_t h = bf16_bits(x[i]);
+        hi[i] = static_cast<short>(h);
+        lo[i] = static_cast<short>(bf16_bits(x[i] - bf16_val(h)));
+    }
+}
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const __bf16 hb = static_cast<__bf16>(x[i]);
+        hi[i] = hb;
+        lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(hb));
     }
 }
 
-__device__ __forceinline__ f32x4 mma16_x3(const float (&a)[4], const float (&b)[4], f32x4 acc) {
-    s16x4 ah, al, bh, bl;
-    split_bf16_4(a, ah, al);
-    split_bf16_4(b, bh, bl);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
-    return acc;
-}
-
-// Prefetched raw inputs of one staging lane: fp32 as is, bf16 packed two per register.
+// Prefetched raw inputs of one staging lane: 4 tokens x CPT channels.
 template <int DT, int N>
-struct RawVec;
+struct Raw;
 template <int N>
-struct RawVec<KDA_F32, N> {
+struct Raw<KDA_F32, N> {
     float v[N];
-    __device__ __forceinline__ void load(const void* p, int i, int64_t e, bool ok) {
-        v[i] = ok ? static_cast<const float*>(p)[e] : 0.f;
-    }
     __device__ __forceinline__ float get(int i) const { return v[i]; }
 };
 template <int N>
-struct RawVec<KDA_BF16, N> {
-    uint32_t v[(N + 1) / 2];
-    __device__ __forceinline__ void load(const void* p, int i, int64_t e, bool ok) {
-        const uint32_t b = ok ? static_cast<uint32_t>(static_cast<const uint16_t*>(p)[e]) : 0u;
-        if (i & 1) v[i / 2] = (v[i / 2] & 0xffffu) | (b << 16);
-        else v[i / 2] = b;
-    }
+struct Raw<KDA_BF16, N> {
+    uint32_t v[N / 2];
     __device__ __forceinline__ float get(int i) const {
         return (i & 1) ? __uint_as_float(v[i / 2] & 0xffff0000u) : __uint_as_float(v[i / 2] << 16);
     }
 };
 
-__device__ __forceinline__ void ld4(const float* p, float* dst) {
-    const float4 x = *reinterpret_cast<const float4*>(p);
-    dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
+// Load CPT consecutive (channel-contiguous) elements at element offset e into row slot i.
+template <int DT, int CPT, int N>
+__device__ __forceinline__ void load_row(Raw<DT, N>& dst, int slot, const void* base, int64_t e,
+                                         bool ok) {
+    if constexpr (DT == KDA_F32) {
+        const float* src = static_cast<const float*>(base) + e;
+#pragma unroll
+        for (int u = 0; u < CPT / 4; ++u) {
+            const float4 x = ok ? *reinterpret_cast<const float4*>(src + 4 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
+            dst.v[slot * CPT + 4 * u + 0] = x.x;
+            dst.v[slot * CPT + 4 * u + 1] = x.y;
+            dst.v[slot * CPT + 4 * u + 2] = x.z;
+            dst.v[slot * CPT + 4 * u + 3] = x.w;
+        }
+    } else {
+        const uint16_t* src = static_cast<const uint16_t*>(base) + e;
+        if constexpr (CPT == 8) {
+            const uint4 x = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
+            dst.v[slot * 4 + 0] = x.x; dst.v[slot * 4 + 1] = x.y;
+            dst.v[slot * 4 + 2] = x.z; dst.v[slot * 4 + 3] = x.w;
+        } else {
+            const uint2 x = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
+            dst.v[slot * 2 + 0] = x.x; dst.v[slot * 2 + 1] = x.y;
+        }
+    }
+}
+
+template <int CPT>
+__device__ __forceinline__ void store_row16(uint16_t* dst, const uint16_t (&v)[CPT]) {
+    if constexpr (CPT == 8) {
+        uint4 w;
+        w.x = v[0] | (uint32_t(v[1]) << 16); w.y = v[2] | (uint32_t(v[3]) << 16);
+        w.z = v[4] | (uint32_t(v[5]) << 16); w.w = v[6] | (uint32_t(v[7]) << 16);
+        *reinterpret_cast<uint4*>(dst) = w;
+    } else {
+        uint2 w;
+        w.x = v[0] | (uint32_t(v[1]) << 16); w.y = v[2] | (uint32_t(v[3]) << 16);
+        *reinterpret_cast<uint2*>(dst) = w;
+    }
 }
 
 // ---- the fused kernel -----------------------------------------------------------------------
 template <int DK, int IDT, int GDT, int ODT, bool PRECISE>
 __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t n_vblk) {
-    constexpr int LDK = DK + 4;          // padded row length of the [64][DK] staging arrays
-    constexpr int KSTEPS = DK / 32;      // 32-channel K-steps
+    constexpr int KS = DK / 32;          // 32-channel K-steps
     constexpr int CT = DK / 16;          // 16-channel tiles of the state
-    constexpr int TPC = NTHR / DK;       // staging lanes per channel (2 or 4)
-    constexpr int TPT = CH / TPC;        // tokens per staging lane (32 or 16)
-    constexpr int BPT = TPT / 16;        // 16-token blocks per staging lane (2 or 1)
-    constexpr int REG4 = (CH * LDK > 2 * CH * LA) ? CH * LDK : 2 * CH * LA;
+    constexpr int CPT = DK / 16;         // channels per staging lane (8 or 4)
+    constexpr int NEL = 4 * CPT;         // elements per staging lane per chunk
+    constexpr float LOG2E = 1.4426950408889634f;
 
-    __shared__ __attribute__((aligned(16))) float sm[3 * CH * LDK + REG4];
-    __shared__ __attribute__((aligned(16))) float sTbb[4][16][16];
-    __shared__ float sRb[5][DK];         // R_0 .. R_3 (block references), G_63
-    __shared__ float sE[4][DK];          // e^{R_b}
-    __shared__ float sF[3][DK];          // e^{R_b - R_{j+1}} for (b, j) = (2,0), (3,0), (3,1)
-    __shared__ float sH[4][DK];          // e^{G_63 - R_{j+1}}
-    __shared__ float sGam[DK];           // e^{G_63}
-    __shared__ float sSeg[TPC][DK];      // per-segment g totals
+    // MFMA-ready operands of one chunk (16-bit; layouts tok_major / ch_major)
+    __shared__ __attribute__((aligned(16))) uint16_t sKh[CH * DK], sKl[CH * DK];   // Kt  bf16 hi/lo
+    __shared__ __attribute__((aligned(16))) uint16_t sQh[CH * DK], sQl[CH * DK];   // Qt  bf16 hi/lo
+    __shared__ __attribute__((aligned(16))) uint16_t sDh[CH * DK], sDl[CH * DK];   // Kd  bf16 hi/lo
+    // fast path: sX0 = Kt fp16, sX1 = Qt fp16 (token-major), sX2 = Kb^T fp16 (channel-major);
+    // precise path: sX0 / sX1 = Kb^T bf16 hi / lo (channel-major), sX2 unused.
+    __shared__ __attribute__((aligned(16))) uint16_t sX0[CH * DK], sX1[CH * DK];
+    __shared__ __attribute__((aligned(16))) uint16_t sX2[PRECISE ? 8 : CH * DK];
+    __shared__ __attribute__((aligned(16))) float sA[4][16][16];                   // beta-scaled A_b
+    __shared__ __attribute__((aligned(16))) uint16_t sPh[4][16][16], sPl[4][16][16];
+    __shared__ __attribute__((aligned(16))) uint16_t sTh[4][16][16], sTl[4][16][16];
+    __shared__ __attribute__((aligned(16))) float sGam[4][DK];                     // e^{G_15}
     __shared__ float sBeta[CH];
-
-    float* const sKR = sm;                    // k_r e^{G_r - R_b}
-    float* const sQR = sm + CH * LDK;         // q_r e^{G_r - R_b}
-    float* const sKB = sm + 2 * CH * LDK;     // k_s e^{R_{j+1} - G_s}
-    float* const sKD = sm + 3 * CH * LDK;     // k_s e^{R_j - G_s}   (A/P phase only)
-    float* const sA = sm + 3 * CH * LDK;      // beta-scaled strict-lower A (after the A/P phase)
-    float* const sP = sA + CH * LA;           // lower P
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int ln = lane & 15, lq = lane >> 4;
+    const int ln = lane & 15, lq = lane >> 4;        // MFMA lane coordinates
+    const int cg = lane >> 2, sub = lane & 3;        // staging lane: channel group, token quad
 
-    // Workgroup -> (unit, column block).  The column blocks of one unit are placed 8 workgroup
-    // ids apart so they land on the same XCD and share its L2 for the unit's q/k/g reads.
+    // Workgroup -> (unit, column block).  The column blocks of one unit sit 8 workgroup ids
+    // apart so they land on the same XCD and share its L2 for the unit's q / k / g reads.
     const int64_t units = static_cast<int64_t>(p.n_seqs) * p.H;
     const int64_t bid = blockIdx.x;
     const int64_t grp = bid / (8 * n_vblk), rem = bid % (8 * n_vblk);
@@ -187,7 +202,8 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
     if (unit >= units) return;
     const int n = static_cast<int>(unit / p.H), h = static_cast<int>(unit % p.H);
     const int DV = p.dv;
-    const int n0 = vb * BV + wave * 16;        // this wave's first state column
+    const int n0 = vb * BV + wave * 16;              // this wave's first state column
+    const int64_t H = p.H;
 
     int64_t bos, len;
     if (p.cu) {
@@ -197,34 +213,42 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
         bos = static_cast<int64_t>(n) * p.T;
         len = p.T;
     }
-    const int64_t H = p.H;
 
-    // ---- state tiles: lane (ln, lq) of tile i holds S[16i + 4lq + r][n0 + ln]
+    // state tiles: lane (ln, lq) of tile i holds S[16i + 4lq + r][n0 + ln]
     f32x4 S[CT];
     const int64_t sbase = unit * DK * DV;
 #pragma unroll
-    for (int i = 0; i < CT; ++i) {
+    for (int i = 0; i < CT; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             S[i][r] = p.h0 ? p.h0[sbase + static_cast<int64_t>(16 * i + 4 * lq + r) * DV + n0 + ln] : 0.f;
-    }
 
-    // staging lane identity
-    const int sc = tid % DK;          // channel
-    const int seg = tid / DK;         // token segment [seg*TPT, seg*TPT + TPT)
-
-    RawVec<GDT, TPT> pg;              // prefetched raw inputs of the next chunk
-    RawVec<IDT, TPT> pk, pq;
+    // ---- prefetched inputs of the next chunk
+    Raw<GDT, NEL> pg;
+    Raw<IDT, NEL> pk, pq;
+    float pbeta = 0.f;
+    float pv[16];
     auto prefetch = [&](int64_t t0, int nt) {
 #pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            const int r = seg * TPT + i;
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * wave + 4 * sub + i;
             const bool ok = r < nt;
-            const int64_t e = ok ? ((bos + t0 + r) * H + h) * DK + sc : 0;
-            pg.load(p.g, i, e, ok);
-            pk.load(p.k, i, e, ok);
-            pq.load(p.q, i, e, ok);
+            const int64_t e = ok ? ((bos + t0 + r) * H + h) * DK + CPT * cg : 0;
+            load_row<GDT, CPT>(pg, i, p.g, e, ok);
+            load_row<IDT, CPT>(pk, i, p.k, e, ok);
+            load_row<IDT, CPT>(pq, i, p.q, e, ok);
         }
+        {
+            const int r = 16 * wave + lane;
+            pbeta = (lane < 16 && r < nt) ? load_as_f32<IDT>(p.beta, (bos + t0 + r) * H + h) : 0.f;
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * b + 4 * lq + i;
+                pv[4 * b + i] = (r < nt) ? load_as_f32<IDT>(p.v, ((bos + t0 + r) * H + h) * DV + n0 + ln) : 0.f;
+            }
     };
 
     const int64_t nchunks = (len + CH - 1) / CH;
@@ -233,267 +257,249 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
     for (int64_t ci = 0; ci < nchunks; ++ci) {
         const int64_t t0 = ci * CH;
         const int nt = static_cast<int>((len - t0) < CH ? (len - t0) : CH);
+        const int blk = wave;                         // this wave stages / prepares block blk
 
-        // ---------------- staging 1: chunk cumsum per (channel, segment)
-        float G[TPT];
+        // ============ phase 1: staging of block blk (lane: 4 tokens x CPT channels) ==========
         {
-            float run = 0.f;
+            // block-local cumsum along tokens in log2 units: the lane's own 4 tokens, then a scan
+            // across the 4 adjacent lanes that hold the same channel group
+            float G2[NEL];
 #pragma unroll
-            for (int i = 0; i < TPT; ++i) { run += pg.get(i); G[i] = run; }
-            sSeg[seg][sc] = run;
-        }
-        if (tid < CH) sBeta[tid] = (tid < nt) ? load_as_f32<IDT>(p.beta, (bos + t0 + tid) * H + h) : 0.f;
-        // this wave's V values for the state phase: V[16b + 4lq + r][n0 + ln]
-        float vpre[16];
+            for (int j = 0; j < CPT; ++j) {
+                float run = 0.f;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+                for (int i = 0; i < 4; ++i) {
+                    run += pg.get(i * CPT + j) * LOG2E;
+                    G2[i * CPT + j] = run;
+                }
+                float incl = run;
+                float up = __shfl_up(incl, 1, 4);
+                if (sub >= 1) incl += up;
+                up = __shfl_up(incl, 2, 4);
+                if (sub >= 2) incl += up;
+                const float excl = incl - run;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * b + 4 * lq + r;
-                vpre[4 * b + r] = (row < nt)
-                    ? load_as_f32<IDT>(p.v, ((bos + t0 + row) * H + h) * DV + n0 + ln) : 0.f;
+                for (int i = 0; i < 4; ++i) G2[i * CPT + j] += excl;
             }
-        __syncthreads();
+            float G15[CPT];
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) G15[j] = __shfl(G2[3 * CPT + j], (lane & ~3) | 3, 64);
 
-        // ---------------- staging 2: chunk-global prefix, block references
-        {
-            float base = 0.f, total = 0.f;
+            const int r0 = 16 * blk + 4 * sub;
+            if (sub == 0) {
 #pragma unroll
-            for (int s = 0; s < TPC; ++s) {
-                const float x = sSeg[s][sc];
-                if (s < seg) base += x;
-                total += x;
+                for (int j = 0; j < CPT; ++j) sGam[blk][CPT * cg + j] = exp2f(G15[j]);
             }
+            if (lane < 16) sBeta[16 * blk + lane] = pbeta;
+
+            float kb[NEL];
 #pragma unroll
-            for (int i = 0; i < TPT; ++i) G[i] += base;
-            // R_{j+1} = G at the last token of block j
+            for (int i = 0; i < 4; ++i) {
+                float kt[CPT], qt[CPT], kd[CPT];
 #pragma unroll
-            for (int bl = 0; bl < BPT; ++bl) sRb[seg * BPT + bl + 1][sc] = G[16 * bl + 15];
-            if (seg == 0) sRb[0][sc] = 0.f;
-            // sRb[4] (= G_63) is written by the last segment above
-            (void)total;
+                for (int j = 0; j < CPT; ++j) {
+                    const float g2 = G2[i * CPT + j];
+                    const float e1 = exp2f(g2);                   // e^{G}        <= 1
+                    const float e2 = exp2f(G15[j] - g2);          // e^{G15 - G}  <= 1
+                    const float kv = pk.get(i * CPT + j);
+                    kt[j] = kv * e1;
+                    qt[j] = pq.get(i * CPT + j) * e1;
+                    kb[i * CPT + j] = kv * e2;
+                    kd[j] = kv * (e2 * exp2f(-G15[j]));           // e^{-G} <= e^80
+                }
+                uint16_t bKh[CPT], bKl[CPT], bQh[CPT], bQl[CPT], bDh[CPT], bDl[CPT], bK16[CPT], bQ16[CPT];
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) {
+                    bKh[j] = bf16_bits(kt[j]); bKl[j] = bf16_bits(kt[j] - bf16_val(bKh[j]));
+                    bQh[j] = bf16_bits(qt[j]); bQl[j] = bf16_bits(qt[j] - bf16_val(bQh[j]));
+                    bDh[j] = bf16_bits(kd[j]); bDl[j] = bf16_bits(kd[j] - bf16_val(bDh[j]));
+                    bK16[j] = f16_bits(kt[j]); bQ16[j] = f16_bits(qt[j]);
+                }
+                const int off = tok_major<DK>(r0 + i, CPT * cg);
+                store_row16<CPT>(sKh + off, bKh); store_row16<CPT>(sKl + off, bKl);
+                store_row16<CPT>(sQh + off, bQh); store_row16<CPT>(sQl + off, bQl);
+                store_row16<CPT>(sDh + off, bDh); store_row16<CPT>(sDl + off, bDl);
+                if constexpr (!PRECISE) {
+                    store_row16<CPT>(sX0 + off, bK16);
+                    store_row16<CPT>(sX1 + off, bQ16);
+                }
+            }
+            // channel-major Kb^T: the lane's 4 tokens of each channel are contiguous
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const int off = ch_major(CPT * cg + j, r0);
+                if constexpr (!PRECISE) {
+                    uint2 w;
+                    w.x = f16_bits(kb[0 * CPT + j]) | (uint32_t(f16_bits(kb[1 * CPT + j])) << 16);
+                    w.y = f16_bits(kb[2 * CPT + j]) | (uint32_t(f16_bits(kb[3 * CPT + j])) << 16);
+                    *reinterpret_cast<uint2*>(sX2 + off) = w;
+                } else {
+                    uint16_t hi[4], lo[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        hi[i] = bf16_bits(kb[i * CPT + j]);
+                        lo[i] = bf16_bits(kb[i * CPT + j] - bf16_val(hi[i]));
+                    }
+                    *reinterpret_cast<uint2*>(sX0 + off) =
+                        make_uint2(hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16));
+                    *reinterpret_cast<uint2*>(sX1 + off) =
+                        make_uint2(lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16));
+                }
+            }
         }
-        // next chunk's raw inputs: issue now, consumed at the next iteration
-        const RawVec<IDT, TPT> kcur = pk, qcur = pq;
+        // next chunk's inputs: issue now (the staging registers are free), consumed next chunk
+        float vcur[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vcur[i] = pv[i];
         if (ci + 1 < nchunks) {
             const int64_t t1 = t0 + CH;
             prefetch(t1, static_cast<int>((len - t1) < CH ? (len - t1) : CH));
         }
-        __syncthreads();
 
-        // ---------------- staging 3: scaled operands (2 exps per element) and small factors
+        // ---- A_b and P_b (16 x 16, contraction over d_k) on MFMA; this wave's block only
+        {
+            f32x4 accA = zero4(), accP = zero4();
+            const int row = 16 * blk + ln;
 #pragma unroll
-        for (int bl = 0; bl < BPT; ++bl) {
-            const int j = seg * BPT + bl;                 // block index of these 16 tokens
-            const float Rj = sRb[j][sc];
-            const float Ge = sRb[j + 1][sc];
-            const float invD = __expf(Rj - Ge);           // e^{R_j - G_{e_j}} in [1, e^80]
+            for (int kk = 0; kk < KS; ++kk) {
+                const int off = tok_major<DK>(row, 32 * kk + 8 * lq);
+                const bf16x8 kh = *reinterpret_cast<const bf16x8*>(sKh + off);
+                const bf16x8 kl = *reinterpret_cast<const bf16x8*>(sKl + off);
+                const bf16x8 qh = *reinterpret_cast<const bf16x8*>(sQh + off);
+                const bf16x8 ql = *reinterpret_cast<const bf16x8*>(sQl + off);
+                const bf16x8 dh = *reinterpret_cast<const bf16x8*>(sDh + off);
+                const bf16x8 dl = *reinterpret_cast<const bf16x8*>(sDl + off);
+                accA = mfma32_bf16_x3(kh, kl, dh, dl, accA);
+                accP = mfma32_bf16_x3(qh, ql, dh, dl, accP);
+            }
+            // lane (ln, lq) holds rows 4lq + i of column ln of the block
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int ti = 16 * bl + i;
-                const int r = 16 * j + i;
-                const float gr = G[ti];
-                const float er = __expf(gr - Rj);         // <= 1
-                const float eb = __expf(Ge - gr);         // <= 1
-                const float kv = kcur.get(ti);
-                const float kb = kv * eb;
-                sKR[r * LDK + sc] = kv * er;
-                sQR[r * LDK + sc] = qcur.get(ti) * er;
-                sKB[r * LDK + sc] = kb;
-                sKD[r * LDK + sc] = kb * invD;
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lq + i, s = ln;
+                sA[blk][r][s] = (s < r) ? accA[i] * sBeta[16 * blk + r] : 0.f;
+                const float pval = (s <= r) ? accP[i] : 0.f;
+                const uint16_t ph = bf16_bits(pval);
+                sPh[blk][r][s] = ph;
+                sPl[blk][r][s] = bf16_bits(pval - bf16_val(ph));
             }
         }
-        if (tid < DK) {
-            const int c = tid;
-            const float R0 = 0.f, R1 = sRb[1][c], R2 = sRb[2][c], R3 = sRb[3][c], G63 = sRb[4][c];
-            sE[0][c] = 1.f;
-            sE[1][c] = __expf(R1);
-            sE[2][c] = __expf(R2);
-            sE[3][c] = __expf(R3);
-            sF[0][c] = __expf(R2 - R1);   // (b, j) = (2, 0)
-            sF[1][c] = __expf(R3 - R1);   // (3, 0)
-            sF[2][c] = __expf(R3 - R2);   // (3, 1)
-            sH[0][c] = __expf(G63 - R1);
-            sH[1][c] = __expf(G63 - R2);
-            sH[2][c] = __expf(G63 - R3);
-            sH[3][c] = 1.f;
-            sGam[c] = __expf(G63 - R0);
-        }
-        __syncthreads();
-
-        // ---------------- A / P tiles.  Diagonal tiles first: they are the only readers of sKD,
-        // which A and P overwrite.  Wave w owns the diagonal tiles (mat, b) = (w & 1, w >> 1) and
-        // (w & 1, (w >> 1) + 2), then the off-diagonal tiles w, w + 4, w + 8 of the twelve.
-        auto ap_tile = [&](int mat, int b, int j) -> f32x4 {
-            const float* rowp = (mat ? sQR : sKR) + (16 * b + ln) * LDK;
-            const float* colp = (j == b ? sKD : sKB) + (16 * j + ln) * LDK;
-            const float* fp = (j + 1 < b) ? sF[(b == 2) ? 0 : (j == 0 ? 1 : 2)] : nullptr;
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                const int c0 = 32 * kk + 4 * lq, c1 = c0 + 16;
-                float a[8], bb[8];
-                ld4(rowp + c0, a);
-                ld4(rowp + c1, a + 4);
-                if (fp) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) { a[i] *= fp[c0 + i]; a[4 + i] *= fp[c1 + i]; }
-                }
-                ld4(colp + c0, bb);
-                ld4(colp + c1, bb + 4);
-                if (PRECISE || j == b) acc = mma32_x3(a, bb, acc);
-                else acc = mma32_f16(a, bb, acc);
-            }
-            return acc;
-        };
-        auto ap_store = [&](int mat, int b, int j, const f32x4& acc) {
-            float* dst = mat ? sP : sA;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * b + 4 * lq + r;      // token r of the chunk
-                const int col = 16 * j + ln;              // token s
-                float x = acc[r];
-                if (mat == 0) x = (col < row) ? x * sBeta[row] : 0.f;
-                else x = (col <= row) ? x : 0.f;
-                dst[row * LA + col] = x;
-            }
-        };
-        const int dmat = wave & 1, db0 = wave >> 1;
-        const f32x4 dacc0 = ap_tile(dmat, db0, db0);
-        const f32x4 dacc1 = ap_tile(dmat, db0 + 2, db0 + 2);
-        __syncthreads();   // everyone is done with sKD: A and P may overwrite it
-        ap_store(dmat, db0, db0, dacc0);
-        ap_store(dmat, db0 + 2, db0 + 2, dacc1);
-#pragma unroll 1
-        for (int t = wave; t < 12; t += 4) {
-            const int mat = t & 1, pr = t >> 1;        // pr -> (b, j): (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-            const int b = pr < 1 ? 1 : pr < 3 ? 2 : 3;
-            const int j = pr - (b * (b - 1)) / 2;
-            ap_store(mat, b, j, ap_tile(mat, b, j));
-        }
-        // P tiles above the diagonal that the 32-token K-steps of P W read: (0,1) and (2,3)
-        if (wave == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sP[(4 * lq + r) * LA + 16 + ln] = 0.f;
-                sP[(32 + 4 * lq + r) * LA + 48 + ln] = 0.f;
-            }
-        }
-        __syncthreads();
-
-        // ---------------- T_bb = (I + A_bb)^{-1} (wave 0) ; Y = Kt S and O = Qt S (all waves)
-        if (wave == 0) {
-            const int b = lq, jc = ln;                     // block, column of T_bb
+        // ---- T'_b = (I + A_b)^{-1} Diag(beta_b): forward substitution, lane j = column j
+        if (lane < 16) {
+            const int j = lane;
             float t[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float s = (r == jc) ? 1.f : 0.f;
-                const float* arow = sA + (16 * b + r) * LA + 16 * b;
+                float s = (r == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int sp = 0; sp < r; ++sp) s -= arow[sp] * t[sp];
+                for (int sp = 0; sp < r; ++sp) s -= sA[blk][r][sp] * t[sp];
                 t[r] = s;
             }
+            const float bj = sBeta[16 * blk + j];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sTbb[b][r][jc] = t[r];
-        }
-
-        // S as the B operand of 32-channel K-steps: c-tiles 2kk and 2kk+1
-        f32x4 Y[4], O[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) { Y[b] = zero4(); O[b] = zero4(); }
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            float sb[8];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) { sb[r] = S[2 * kk][r]; sb[4 + r] = S[2 * kk + 1][r]; }
-            const int c0 = 32 * kk + 4 * lq, c1 = c0 + 16;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                float ak[8], aq[8];
-                ld4(sKR + (16 * b + ln) * LDK + c0, ak);
-                ld4(sKR + (16 * b + ln) * LDK + c1, ak + 4);
-                ld4(sQR + (16 * b + ln) * LDK + c0, aq);
-                ld4(sQR + (16 * b + ln) * LDK + c1, aq + 4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e0 = sE[b][c0 + i], e1 = sE[b][c1 + i];
-                    ak[i] *= e0; ak[4 + i] *= e1;
-                    aq[i] *= e0; aq[4 + i] *= e1;
-                }
-                Y[b] = mma32<PRECISE>(ak, sb, Y[b]);
-                O[b] = mma32<PRECISE>(aq, sb, O[b]);
+            for (int r = 0; r < 16; ++r) {
+                const float x = t[r] * bj;
+                const uint16_t th = bf16_bits(x);
+                sTh[blk][r][j] = th;
+                sTl[blk][r][j] = bf16_bits(x - bf16_val(th));
             }
         }
-        __syncthreads();   // sTbb ready
+        __syncthreads();
 
-        // ---------------- W by blocked forward substitution (per wave, its 16 columns)
-        f32x4 W[4];
+        // ============ phase 2: the state pass over the four blocks, this wave's 16 columns =======
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            f32x4 R;
+            const int row = 16 * b + ln;
+            f32x4 Y = zero4(), O = zero4();
+            if constexpr (!PRECISE) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * b + 4 * lq + r;
-                R[r] = sBeta[row] * (vpre[4 * b + r] - Y[b][r]);
-            }
+                for (int kk = 0; kk < KS; ++kk) {
+                    // B = S (channels 32kk.. as two 16-channel tiles); A rows read in the same K order
+                    f16x8 sb;
 #pragma unroll
-            for (int j = 0; j < b; ++j) {
-                float a4[4], w4[4];
-                ld4(sA + (16 * b + ln) * LA + 16 * j + 4 * lq, a4);
+                    for (int i = 0; i < 4; ++i) {
+                        sb[i] = static_cast<_Float16>(S[2 * kk][i]);
+                        sb[4 + i] = static_cast<_Float16>(S[2 * kk + 1][i]);
+                    }
+                    const int o0 = tok_major<DK>(row, 32 * kk + 4 * lq);
+                    const int o1 = tok_major<DK>(row, 32 * kk + 16 + 4 * lq);
+                    const f16x4 k0 = *reinterpret_cast<const f16x4*>(sX0 + o0);
+                    const f16x4 k1 = *reinterpret_cast<const f16x4*>(sX0 + o1);
+                    const f16x4 q0 = *reinterpret_cast<const f16x4*>(sX1 + o0);
+                    const f16x4 q1 = *reinterpret_cast<const f16x4*>(sX1 + o1);
+                    f16x8 ka, qa;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { a4[i] = -a4[i]; w4[i] = W[j][i]; }
-                R = mma16_x3(a4, w4, R);
-            }
-            float t4[4], r4[4];
-            ld4(&sTbb[b][ln][4 * lq], t4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r4[i] = R[i];
-            W[b] = mma16_x3(t4, r4, zero4());
-        }
-
-        // ---------------- O += P W, store o
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-#pragma unroll
-            for (int kk = 0; kk <= b / 2; ++kk) {
-                float pa[8], wb[8];
-                ld4(sP + (16 * b + ln) * LA + 32 * kk + 4 * lq, pa);
-                ld4(sP + (16 * b + ln) * LA + 32 * kk + 16 + 4 * lq, pa + 4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) { wb[r] = W[2 * kk][r]; wb[4 + r] = W[2 * kk + 1][r]; }
-                O[b] = mma32_x3(pa, wb, O[b]);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * b + 4 * lq + r;
-                if (row < nt)
-                    store_from_f32<ODT>(p.o, ((bos + t0 + row) * H + h) * DV + n0 + ln, p.scale * O[b][r]);
-            }
-        }
-
-        // ---------------- S <- e^{G_n} S + Kb^T W
-#pragma unroll
-        for (int i = 0; i < CT; ++i) {
-            f32x4 acc;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = S[i][r] * sGam[16 * i + 4 * lq + r];
-            const int c = 16 * i + ln;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                float ka[8], wb[8];
-                const float h0 = sH[2 * kk][c], h1 = sH[2 * kk + 1][c];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    ka[r] = sKB[(32 * kk + 4 * lq + r) * LDK + c] * h0;
-                    ka[4 + r] = sKB[(32 * kk + 16 + 4 * lq + r) * LDK + c] * h1;
-                    wb[r] = W[2 * kk][r];
-                    wb[4 + r] = W[2 * kk + 1][r];
+                    for (int i = 0; i < 4; ++i) { ka[i] = k0[i]; ka[4 + i] = k1[i]; qa[i] = q0[i]; qa[4 + i] = q1[i]; }
+                    Y = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, sb, Y, 0, 0, 0);
+                    O = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, sb, O, 0, 0, 0);
                 }
-                acc = mma32<PRECISE>(ka, wb, acc);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) {
+                    float sv[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) { sv[i] = S[2 * kk][i]; sv[4 + i] = S[2 * kk + 1][i]; }
+                    bf16x8 sbh, sbl;
+                    split8(sv, sbh, sbl);
+                    const int o0 = tok_major<DK>(row, 32 * kk + 4 * lq);
+                    const int o1 = tok_major<DK>(row, 32 * kk + 16 + 4 * lq);
+                    const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(sKh + o0), a1 = *reinterpret_cast<const bf16x4*>(sKh + o1);
+                    const bf16x4 b0 = *reinterpret_cast<const bf16x4*>(sKl + o0), b1 = *reinterpret_cast<const bf16x4*>(sKl + o1);
+                    const bf16x4 c0 = *reinterpret_cast<const bf16x4*>(sQh + o0), c1 = *reinterpret_cast<const bf16x4*>(sQh + o1);
+                    const bf16x4 d0 = *reinterpret_cast<const bf16x4*>(sQl + o0), d1 = *reinterpret_cast<const bf16x4*>(sQl + o1);
+                    bf16x8 kh, kl, qh, ql;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        kh[i] = a0[i]; kh[4 + i] = a1[i]; kl[i] = b0[i]; kl[4 + i] = b1[i];
+                        qh[i] = c0[i]; qh[4 + i] = c1[i]; ql[i] = d0[i]; ql[4 + i] = d1[i];
+                    }
+                    Y = mfma32_bf16_x3(kh, kl, sbh, sbl, Y);
+                    O = mfma32_bf16_x3(qh, ql, sbh, sbl, O);
+                }
             }
-            S[i] = acc;
+            // X = V - Y (the beta scaling sits in T'), W = T' X
+            f32x4 X;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X[i] = vcur[4 * b + i] - Y[i];
+            s16x4 xh, xl;
+            split4(X, xh, xl);
+            const s16x4 th = *reinterpret_cast<const s16x4*>(&sTh[b][ln][4 * lq]);
+            const s16x4 tl = *reinterpret_cast<const s16x4*>(&sTl[b][ln][4 * lq]);
+            const f32x4 W = mfma16_bf16_x3(th, tl, xh, xl, zero4());
+            // O += P W
+            s16x4 wh, wl;
+            split4(W, wh, wl);
+            const s16x4 ph = *reinterpret_cast<const s16x4*>(&sPh[b][ln][4 * lq]);
+            const s16x4 pl = *reinterpret_cast<const s16x4*>(&sPl[b][ln][4 * lq]);
+            O = mfma16_bf16_x3(ph, pl, wh, wl, O);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * b + 4 * lq + i;
+                if (r < nt)
+                    store_from_f32<ODT>(p.o, ((bos + t0 + r) * H + h) * DV + n0 + ln, p.scale * O[i]);
+            }
+            // S <- Diag(e^{G_15}) S + Kb^T W   (contraction over the block's 16 tokens)
+            f16x4 w16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w16[i] = static_cast<_Float16>(W[i]);
+#pragma unroll
+            for (int i = 0; i < CT; ++i) {
+                const float4 gm = *reinterpret_cast<const float4*>(&sGam[b][16 * i + 4 * lq]);
+                f32x4 acc;
+                acc[0] = S[i][0] * gm.x; acc[1] = S[i][1] * gm.y;
+                acc[2] = S[i][2] * gm.z; acc[3] = S[i][3] * gm.w;
+                const int off = ch_major(16 * i + ln, 16 * b + 4 * lq);
+                if constexpr (!PRECISE) {
+                    const f16x4 ka = *reinterpret_cast<const f16x4*>(sX2 + off);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(ka, w16, acc, 0, 0, 0);
+                } else {
+                    const s16x4 kh = *reinterpret_cast<const s16x4*>(sX0 + off);
+                    const s16x4 kl = *reinterpret_cast<const s16x4*>(sX1 + off);
+                    acc = mfma16_bf16_x3(kh, kl, wh, wl, acc);
+                }
+                S[i] = acc;
+            }
         }
-        __syncthreads();   // LDS is rewritten by the next chunk's staging
+        __syncthreads();   // the next chunk's staging rewrites the operand arrays
     }
 
     if (p.hT) {

@@ -154,8 +154,10 @@ def test_split_invariance_and_inplace_state():
     o2, h2 = K.kda_chunk_fwd(*qs, g[:, T1:].contiguous().to(DEV), initial_state=h1,
                              final_state=h1, o_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert rel_err(torch.cat([o1, o2], 1), o_full.double().cpu().numpy()) <= 1e-4
-    assert rel_err(h2, h_full.double().cpu().numpy()) <= 1e-4
+    # a split at a token that is not a block boundary changes the blocking, so the two runs agree
+    # to the kernel's rounding, not bit for bit
+    assert rel_err(torch.cat([o1, o2], 1), o_full.double().cpu().numpy()) <= TOL["bf16"]
+    assert rel_err(h2, h_full.double().cpu().numpy()) <= TOL["bf16"]
 
 
 def test_decode_steps_equal_prefill():
