@@ -12,7 +12,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for all device code; hipcc's host pass warns that it does
 # not know the feature, which is harmless.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # keep MFMA accumulators in VGPRs (no AGPR round trips when VALU touches them)
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def lib_path() -> str:

@@ -32,7 +32,7 @@
 //           MFMA; T'_b by substitution.  No workgroup barrier: a wave only reads what it wrote.
 //   phase 2 (every wave, its 16 columns, blocks 0..3 in order): Y = Kt S, O = Qt S, W, O += P W,
 //           o stored from registers, S <- e^{G_15} S + Kb^T W.
-// The next chunk's raw inputs are loaded into registers during phases 1 and 2.
+// The next chunk's raw inputs are loaded into registers while the state pass runs.
 // Precision: operands that are range-bounded use fp16 (11-bit significand) in one pass; the
 // diagonal products (factors up to e^80), T' X and P W use split bf16 (hi*hi + hi*lo + lo*hi).
 // For fp32 inputs every product is split bf16.
@@ -67,6 +67,10 @@ __device__ __forceinline__ int ch_major(int c, int t) {
     return c * CH + ((((t >> 3) ^ (c & 7))) << 3) + (t & 7);
 }
 
+// 2^x with one v_exp_f32.  Every factor formed here lies in [2^-116, 2^116] (a 16-token span
+// decays by at most e^-80), so the instruction's denormal flush never applies.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
@@ -87,6 +91,22 @@ __device__ __forceinline__ f32x4 mfma16_bf16_x3(const s16x4& ah, const s16x4& al
     c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> packed bf16 hi word and packed bf16 lo word (x = hi + lo to ~16 bits).
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    const bf16x2 h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
+    hi = __builtin_bit_cast(uint32_t, h);
+    const float r0 = x0 - __uint_as_float(hi << 16);
+    const float r1 = x1 - __uint_as_float(hi & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+}
+__device__ __forceinline__ uint32_t f16_pair(float x0, float x1) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, f16x2));
 }
 
 // four fp32 values -> bf16 hi/lo pairs (16x16x16 operand layout)
@@ -125,7 +145,7 @@ struct Raw<KDA_BF16, N> {
 
 // Load CPT consecutive (channel-contiguous) elements at element offset e into row slot i.
 template <int DT, int CPT, int N>
-__device__ __forceinline__ void load_row(Raw<DT, N>& dst, int slot, const void* base, int64_t e,
+__device__ __forceinline__ void load_row(Raw<DT, N>& dst, int slot, const void* base, int32_t e,
                                          bool ok) {
     if constexpr (DT == KDA_F32) {
         const float* src = static_cast<const float*>(base) + e;
@@ -150,18 +170,10 @@ __device__ __forceinline__ void load_row(Raw<DT, N>& dst, int slot, const void* 
     }
 }
 
-template <int CPT>
-__device__ __forceinline__ void store_row16(uint16_t* dst, const uint16_t (&v)[CPT]) {
-    if constexpr (CPT == 8) {
-        uint4 w;
-        w.x = v[0] | (uint32_t(v[1]) << 16); w.y = v[2] | (uint32_t(v[3]) << 16);
-        w.z = v[4] | (uint32_t(v[5]) << 16); w.w = v[6] | (uint32_t(v[7]) << 16);
-        *reinterpret_cast<uint4*>(dst) = w;
-    } else {
-        uint2 w;
-        w.x = v[0] | (uint32_t(v[1]) << 16); w.y = v[2] | (uint32_t(v[3]) << 16);
-        *reinterpret_cast<uint2*>(dst) = w;
-    }
+template <int NP>
+__device__ __forceinline__ void store_words(uint16_t* dst, const uint32_t (&w)[NP]) {
+    if constexpr (NP == 4) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    else *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
 }
 
 // ---- the fused kernel -----------------------------------------------------------------------
@@ -185,6 +197,9 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
     __shared__ __attribute__((aligned(16))) uint16_t sPh[4][16][16], sPl[4][16][16];
     __shared__ __attribute__((aligned(16))) uint16_t sTh[4][16][16], sTl[4][16][16];
     __shared__ __attribute__((aligned(16))) float sGam[4][DK];                     // e^{G_15}
+    // V of the chunk as fp32 [4 blocks][16 rows][64 columns]: for d_k = 128 it lives in the rows
+    // of sDh that the block's own A/P products have finished with; for d_k = 64 in sV64.
+    __shared__ __attribute__((aligned(16))) float sV64[DK == 64 ? 4 * 16 * BV : 4];
     __shared__ float sBeta[CH];
 
     const int tid = threadIdx.x;
@@ -227,28 +242,43 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
     Raw<GDT, NEL> pg;
     Raw<IDT, NEL> pk, pq;
     float pbeta = 0.f;
-    float pv[16];
+    // V rows of this wave's block for the workgroup's 64 columns: lane -> row lane/4, 16 columns
+    Raw<IDT, 16> pv;
+    auto vslab = [&](int b) -> float* {
+        if constexpr (DK == 128) return reinterpret_cast<float*>(sDh + 16 * b * DK);
+        else return sV64 + b * 16 * BV;
+    };
+    // Per-chunk base pointers are uniform (scalar registers); per-lane offsets stay 32-bit.
+    const int32_t kstride = static_cast<int32_t>(H) * DK;    // elements between tokens in q/k/g
+    const int32_t vstride = static_cast<int32_t>(H) * DV;    // ... in v and o
     auto prefetch = [&](int64_t t0, int nt) {
+        const int64_t row0 = (bos + t0) * H + h;             // token t0 of this head
+        const void* gbase = static_cast<const char*>(p.g) + row0 * DK * (GDT == KDA_F32 ? 4 : 2);
+        const void* kbase = static_cast<const char*>(p.k) + row0 * DK * (IDT == KDA_F32 ? 4 : 2);
+        const void* qbase = static_cast<const char*>(p.q) + row0 * DK * (IDT == KDA_F32 ? 4 : 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * wave + 4 * sub + i;
             const bool ok = r < nt;
-            const int64_t e = ok ? ((bos + t0 + r) * H + h) * DK + CPT * cg : 0;
-            load_row<GDT, CPT>(pg, i, p.g, e, ok);
-            load_row<IDT, CPT>(pk, i, p.k, e, ok);
-            load_row<IDT, CPT>(pq, i, p.q, e, ok);
+            const int32_t e = ok ? r * kstride + CPT * cg : 0;
+            load_row<GDT, CPT>(pg, i, gbase, e, ok);
+            load_row<IDT, CPT>(pk, i, kbase, e, ok);
+            load_row<IDT, CPT>(pq, i, qbase, e, ok);
         }
         {
+            const void* bbase = static_cast<const char*>(p.beta) + row0 * (IDT == KDA_F32 ? 4 : 2);
             const int r = 16 * wave + lane;
-            pbeta = (lane < 16 && r < nt) ? load_as_f32<IDT>(p.beta, (bos + t0 + r) * H + h) : 0.f;
+            pbeta = (lane < 16 && r < nt) ? load_as_f32<IDT>(bbase, r * static_cast<int32_t>(H)) : 0.f;
         }
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * b + 4 * lq + i;
-                pv[4 * b + i] = (r < nt) ? load_as_f32<IDT>(p.v, ((bos + t0 + r) * H + h) * DV + n0 + ln) : 0.f;
-            }
+        {
+            const void* vbase = static_cast<const char*>(p.v) +
+                                (row0 * DV + vb * BV) * (IDT == KDA_F32 ? 4 : 2);
+            const int r = 16 * wave + (lane >> 2);
+            const bool ok = r < nt;
+            const int32_t e = ok ? r * vstride + 16 * (lane & 3) : 0;
+            load_row<IDT, 8>(pv, 0, vbase, e, ok);
+            load_row<IDT, 8>(pv, 1, vbase, e + 8, ok);
+        }
     };
 
     const int64_t nchunks = (len + CH - 1) / CH;
@@ -288,7 +318,7 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
             const int r0 = 16 * blk + 4 * sub;
             if (sub == 0) {
 #pragma unroll
-                for (int j = 0; j < CPT; ++j) sGam[blk][CPT * cg + j] = exp2f(G15[j]);
+                for (int j = 0; j < CPT; ++j) sGam[blk][CPT * cg + j] = fexp2(G15[j]);
             }
             if (lane < 16) sBeta[16 * blk + lane] = pbeta;
 
@@ -299,29 +329,31 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
 #pragma unroll
                 for (int j = 0; j < CPT; ++j) {
                     const float g2 = G2[i * CPT + j];
-                    const float e1 = exp2f(g2);                   // e^{G}        <= 1
-                    const float e2 = exp2f(G15[j] - g2);          // e^{G15 - G}  <= 1
+                    const float e1 = fexp2(g2);                   // e^{G}        <= 1
+                    const float e2 = fexp2(G15[j] - g2);          // e^{G15 - G}  <= 1
                     const float kv = pk.get(i * CPT + j);
                     kt[j] = kv * e1;
                     qt[j] = pq.get(i * CPT + j) * e1;
                     kb[i * CPT + j] = kv * e2;
-                    kd[j] = kv * (e2 * exp2f(-G15[j]));           // e^{-G} <= e^80
+                    kd[j] = kv * (e2 * fexp2(-G15[j]));           // e^{-G} <= e^80
                 }
-                uint16_t bKh[CPT], bKl[CPT], bQh[CPT], bQl[CPT], bDh[CPT], bDl[CPT], bK16[CPT], bQ16[CPT];
+                constexpr int NP = CPT / 2;            // packed pairs per row segment
+                uint32_t wKh[NP], wKl[NP], wQh[NP], wQl[NP], wDh[NP], wDl[NP], wK16[NP], wQ16[NP];
 #pragma unroll
-                for (int j = 0; j < CPT; ++j) {
-                    bKh[j] = bf16_bits(kt[j]); bKl[j] = bf16_bits(kt[j] - bf16_val(bKh[j]));
-                    bQh[j] = bf16_bits(qt[j]); bQl[j] = bf16_bits(qt[j] - bf16_val(bQh[j]));
-                    bDh[j] = bf16_bits(kd[j]); bDl[j] = bf16_bits(kd[j] - bf16_val(bDh[j]));
-                    bK16[j] = f16_bits(kt[j]); bQ16[j] = f16_bits(qt[j]);
+                for (int u = 0; u < NP; ++u) {
+                    split_pair(kt[2 * u], kt[2 * u + 1], wKh[u], wKl[u]);
+                    split_pair(qt[2 * u], qt[2 * u + 1], wQh[u], wQl[u]);
+                    split_pair(kd[2 * u], kd[2 * u + 1], wDh[u], wDl[u]);
+                    wK16[u] = f16_pair(kt[2 * u], kt[2 * u + 1]);
+                    wQ16[u] = f16_pair(qt[2 * u], qt[2 * u + 1]);
                 }
                 const int off = tok_major<DK>(r0 + i, CPT * cg);
-                store_row16<CPT>(sKh + off, bKh); store_row16<CPT>(sKl + off, bKl);
-                store_row16<CPT>(sQh + off, bQh); store_row16<CPT>(sQl + off, bQl);
-                store_row16<CPT>(sDh + off, bDh); store_row16<CPT>(sDl + off, bDl);
+                store_words<NP>(sKh + off, wKh); store_words<NP>(sKl + off, wKl);
+                store_words<NP>(sQh + off, wQh); store_words<NP>(sQl + off, wQl);
+                store_words<NP>(sDh + off, wDh); store_words<NP>(sDl + off, wDl);
                 if constexpr (!PRECISE) {
-                    store_row16<CPT>(sX0 + off, bK16);
-                    store_row16<CPT>(sX1 + off, bQ16);
+                    store_words<NP>(sX0 + off, wK16);
+                    store_words<NP>(sX1 + off, wQ16);
                 }
             }
             // channel-major Kb^T: the lane's 4 tokens of each channel are contiguous
@@ -329,33 +361,18 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
             for (int j = 0; j < CPT; ++j) {
                 const int off = ch_major(CPT * cg + j, r0);
                 if constexpr (!PRECISE) {
-                    uint2 w;
-                    w.x = f16_bits(kb[0 * CPT + j]) | (uint32_t(f16_bits(kb[1 * CPT + j])) << 16);
-                    w.y = f16_bits(kb[2 * CPT + j]) | (uint32_t(f16_bits(kb[3 * CPT + j])) << 16);
-                    *reinterpret_cast<uint2*>(sX2 + off) = w;
+                    *reinterpret_cast<uint2*>(sX2 + off) =
+                        make_uint2(f16_pair(kb[0 * CPT + j], kb[1 * CPT + j]),
+                                   f16_pair(kb[2 * CPT + j], kb[3 * CPT + j]));
                 } else {
-                    uint16_t hi[4], lo[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        hi[i] = bf16_bits(kb[i * CPT + j]);
-                        lo[i] = bf16_bits(kb[i * CPT + j] - bf16_val(hi[i]));
-                    }
-                    *reinterpret_cast<uint2*>(sX0 + off) =
-                        make_uint2(hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16));
-                    *reinterpret_cast<uint2*>(sX1 + off) =
-                        make_uint2(lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16));
+                    uint32_t h0, l0, h1, l1;
+                    split_pair(kb[0 * CPT + j], kb[1 * CPT + j], h0, l0);
+                    split_pair(kb[2 * CPT + j], kb[3 * CPT + j], h1, l1);
+                    *reinterpret_cast<uint2*>(sX0 + off) = make_uint2(h0, h1);
+                    *reinterpret_cast<uint2*>(sX1 + off) = make_uint2(l0, l1);
                 }
             }
         }
-        // next chunk's inputs: issue now (the staging registers are free), consumed next chunk
-        float vcur[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) vcur[i] = pv[i];
-        if (ci + 1 < nchunks) {
-            const int64_t t1 = t0 + CH;
-            prefetch(t1, static_cast<int>((len - t1) < CH ? (len - t1) : CH));
-        }
-
         // ---- A_b and P_b (16 x 16, contraction over d_k) on MFMA; this wave's block only
         {
             f32x4 accA = zero4(), accP = zero4();
@@ -383,6 +400,14 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
                 sPl[blk][r][s] = bf16_bits(pval - bf16_val(ph));
             }
         }
+        // ---- this block's V rows into the slab (the block's sDh rows are no longer needed)
+        {
+            float* dst = vslab(blk) + (lane >> 2) * BV + 16 * (lane & 3);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                *reinterpret_cast<float4*>(dst + 4 * u) =
+                    make_float4(pv.get(4 * u), pv.get(4 * u + 1), pv.get(4 * u + 2), pv.get(4 * u + 3));
+        }
         // ---- T'_b = (I + A_b)^{-1} Diag(beta_b): forward substitution, lane j = column j
         if (lane < 16) {
             const int j = lane;
@@ -404,6 +429,15 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
             }
         }
         __syncthreads();
+
+        // next chunk's inputs: issued here, consumed by the next chunk's staging
+        if (ci + 1 < nchunks) {
+            const int64_t t1 = t0 + CH;
+            prefetch(t1, static_cast<int>((len - t1) < CH ? (len - t1) : CH));
+        }
+        const bool full = nt == CH;                   // uniform: no per-row guards needed
+        void* const obase = static_cast<char*>(p.o) +
+                            (((bos + t0) * H + h) * DV + n0) * (ODT == KDA_F32 ? 4 : 2);
 
         // ============ phase 2: the state pass over the four blocks, this wave's 16 columns =======
 #pragma unroll
@@ -459,7 +493,7 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
             // X = V - Y (the beta scaling sits in T'), W = T' X
             f32x4 X;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) X[i] = vcur[4 * b + i] - Y[i];
+            for (int i = 0; i < 4; ++i) X[i] = vslab(b)[(4 * lq + i) * BV + 16 * wave + ln] - Y[i];
             s16x4 xh, xl;
             split4(X, xh, xl);
             const s16x4 th = *reinterpret_cast<const s16x4*>(&sTh[b][ln][4 * lq]);
@@ -474,29 +508,42 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * b + 4 * lq + i;
-                if (r < nt)
-                    store_from_f32<ODT>(p.o, ((bos + t0 + r) * H + h) * DV + n0 + ln, p.scale * O[i]);
+                if (full || r < nt) {
+                    const int32_t e = r * vstride + ln;
+                    if constexpr (ODT == KDA_F32) static_cast<float*>(obase)[e] = p.scale * O[i];
+                    else static_cast<uint16_t*>(obase)[e] = bf16_bits(p.scale * O[i]);
+                }
             }
             // S <- Diag(e^{G_15}) S + Kb^T W   (contraction over the block's 16 tokens)
             f16x4 w16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) w16[i] = static_cast<_Float16>(W[i]);
+            float4 gm[CT];
 #pragma unroll
-            for (int i = 0; i < CT; ++i) {
-                const float4 gm = *reinterpret_cast<const float4*>(&sGam[b][16 * i + 4 * lq]);
-                f32x4 acc;
-                acc[0] = S[i][0] * gm.x; acc[1] = S[i][1] * gm.y;
-                acc[2] = S[i][2] * gm.z; acc[3] = S[i][3] * gm.w;
-                const int off = ch_major(16 * i + ln, 16 * b + 4 * lq);
-                if constexpr (!PRECISE) {
-                    const f16x4 ka = *reinterpret_cast<const f16x4*>(sX2 + off);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(ka, w16, acc, 0, 0, 0);
-                } else {
+            for (int i = 0; i < CT; ++i) gm[i] = *reinterpret_cast<const float4*>(&sGam[b][16 * i + 4 * lq]);
+            if constexpr (!PRECISE) {
+                f16x4 ka[CT];
+#pragma unroll
+                for (int i = 0; i < CT; ++i)
+                    ka[i] = *reinterpret_cast<const f16x4*>(sX2 + ch_major(16 * i + ln, 16 * b + 4 * lq));
+#pragma unroll
+                for (int i = 0; i < CT; ++i) {
+                    f32x4 acc;
+                    acc[0] = S[i][0] * gm[i].x; acc[1] = S[i][1] * gm[i].y;
+                    acc[2] = S[i][2] * gm[i].z; acc[3] = S[i][3] * gm[i].w;
+                    S[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(ka[i], w16, acc, 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < CT; ++i) {
+                    const int off = ch_major(16 * i + ln, 16 * b + 4 * lq);
                     const s16x4 kh = *reinterpret_cast<const s16x4*>(sX0 + off);
                     const s16x4 kl = *reinterpret_cast<const s16x4*>(sX1 + off);
-                    acc = mfma16_bf16_x3(kh, kl, wh, wl, acc);
+                    f32x4 acc;
+                    acc[0] = S[i][0] * gm[i].x; acc[1] = S[i][1] * gm[i].y;
+                    acc[2] = S[i][2] * gm[i].z; acc[3] = S[i][3] * gm[i].w;
+                    S[i] = mfma16_bf16_x3(kh, kl, wh, wl, acc);
                 }
-                S[i] = acc;
             }
         }
         __syncthreads();   // the next chunk's staging rewrites the operand arrays
