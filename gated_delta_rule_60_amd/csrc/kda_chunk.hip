@@ -241,7 +241,7 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
     // ---- prefetched inputs of the next chunk
     Raw<GDT, NEL> pg;
     Raw<IDT, NEL> pk, pq;
-    float pbeta = 0.f;
+    uint32_t pbeta = 0u;              // raw bits of this lane's beta (converted when used)
     // V rows of this wave's block for the workgroup's 64 columns: lane -> row lane/4, 16 columns
     Raw<IDT, 16> pv;
     auto vslab = [&](int b) -> float* {
@@ -268,7 +268,11 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
         {
             const void* bbase = static_cast<const char*>(p.beta) + row0 * (IDT == KDA_F32 ? 4 : 2);
             const int r = 16 * wave + lane;
-            pbeta = (lane < 16 && r < nt) ? load_as_f32<IDT>(bbase, r * static_cast<int32_t>(H)) : 0.f;
+            const int32_t e = r * static_cast<int32_t>(H);
+            if constexpr (IDT == KDA_F32)
+                pbeta = (lane < 16 && r < nt) ? static_cast<const uint32_t*>(bbase)[e] : 0u;
+            else
+                pbeta = (lane < 16 && r < nt) ? uint32_t(static_cast<const uint16_t*>(bbase)[e]) : 0u;
         }
         {
             const void* vbase = static_cast<const char*>(p.v) +
@@ -320,7 +324,8 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
 #pragma unroll
                 for (int j = 0; j < CPT; ++j) sGam[blk][CPT * cg + j] = fexp2(G15[j]);
             }
-            if (lane < 16) sBeta[16 * blk + lane] = pbeta;
+            if (lane < 16)
+                sBeta[16 * blk + lane] = (IDT == KDA_F32) ? __uint_as_float(pbeta) : __uint_as_float(pbeta << 16);
 
             float kb[NEL];
 #pragma unroll
@@ -410,14 +415,31 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
         }
         // ---- T'_b = (I + A_b)^{-1} Diag(beta_b): forward substitution, lane j = column j
         if (lane < 16) {
+            // rows are read one ahead of their use; each row's dot product runs as four
+            // independent partial sums, so the dependent chain per row is short
             const int j = lane;
             float t[16];
+            float4 nxt[4], cur[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = (r == j) ? 1.f : 0.f;
+            for (int u = 0; u < 4; ++u) nxt[u] = *reinterpret_cast<const float4*>(&sA[blk][1][4 * u]);
+            t[0] = (j == 0) ? 1.f : 0.f;
 #pragma unroll
-                for (int sp = 0; sp < r; ++sp) s -= sA[blk][r][sp] * t[sp];
-                t[r] = s;
+            for (int r = 1; r < 16; ++r) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+                if (r + 1 < 16) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (4 * u < r + 1) nxt[u] = *reinterpret_cast<const float4*>(&sA[blk][r + 1][4 * u]);
+                }
+                float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sp = 0; sp < r; ++sp) {
+                    const float4& c4 = cur[sp >> 2];
+                    const float a = (sp & 3) == 0 ? c4.x : (sp & 3) == 1 ? c4.y : (sp & 3) == 2 ? c4.z : c4.w;
+                    part[sp & 3] += a * t[sp];
+                }
+                t[r] = ((r == j) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
             }
             const float bj = sBeta[16 * blk + j];
 #pragma unroll
