@@ -8,8 +8,9 @@ and distributions) and resident in HBM before the timed region starts.  The deco
 "decode".
 
 Prints ONE JSON line.  ``value`` is prefill tokens/s (B*T tokens per step / step time).
-``roofline`` describes the dominant kernel (the fused chunk kernel) with its algorithmic bytes
-per launch divided by its mean launch time, measured with HIP events on the launch stream.
+``roofline`` describes the dominant operation, kda_chunk_fwd (its two kernels: the intra-block
+kernel and the state-passing kernel, launched back to back on one stream), with its algorithmic
+bytes per call divided by its mean call time, measured with HIP events on the launch stream.
 ``cpu_baseline`` is the fp64 oracle (test infrastructure) timed on this host's cores on the same
 workload.
 """
@@ -76,6 +77,8 @@ def main():
     g = torch.empty(z.shape, dtype=torch.float32, device=dev)
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     hT = torch.empty_like(S0)
+    ws = torch.empty(K.kda_chunk_fwd_workspace_size(B, B * T, H, dk, dv, in_dtype=q.dtype),
+                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -87,7 +90,8 @@ def main():
         K.kda_gate(A, z, g=g, stream=stream)
         if timed:
             ev[1].record(stream)
-        K.kda_chunk_fwd(q, k, v, beta, g, initial_state=S0, final_state=hT, o=o, stream=stream)
+        K.kda_chunk_fwd(q, k, v, beta, g, initial_state=S0, final_state=hT, o=o, workspace=ws,
+                        stream=stream)
         if timed:
             ev[2].record(stream)
             ev[2].synchronize()
@@ -178,8 +182,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
-                     "kernel": "chunk_fwd_kernel", "kernel_ms": round(chunk_avg, 4),
-                     "bytes_per_launch": chunk_bytes},
+                     "kernel": "kda_chunk_fwd = chunk_intra_kernel + chunk_state_kernel",
+                     "kernel_ms": round(chunk_avg, 4), "bytes_per_launch": chunk_bytes,
+                     "workspace_bytes": ws.numel()},
         "mfma": {"canonical_tflops": round(chunk_flop / (chunk_avg * 1e-3) / 1e12, 2),
                  "frac_bf16_peak": round(chunk_flop / (chunk_avg * 1e-3) / BF16_PEAK, 4)},
         "gate_ms": round(gate_avg, 4),

@@ -63,11 +63,11 @@ int kda_gate(const float* A, const void* z, int z_dtype, void* g, int g_dtype, i
 }
 
 size_t kda_chunk_fwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
-                                    int32_t dv, int32_t chunk) {
+                                    int32_t dv, int32_t chunk, int in_dtype) {
     if (n_seqs < 1 || total_tokens < 0 || H < 1 || !supported_d(dk) || !supported_d(dv) ||
-        chunk != 64)
+        chunk != 64 || !valid_dtype(in_dtype))
         return 0;
-    return kda::chunk_workspace_bytes(n_seqs, total_tokens, H, dk, dv);
+    return kda::chunk_workspace_bytes(n_seqs, total_tokens, H, dk, in_dtype);
 }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, int in_dtype,
@@ -83,7 +83,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
     if (!supported_d(dk) || !supported_d(dv) || chunk != 64) return KDA_ERR_UNSUPPORTED;
     const int64_t ntok = int64_t(B) * T;
     if (ntok > 0 && (!q || !k || !v || !beta || !g || !o)) return KDA_ERR_INVALID_ARGUMENT;
-    const size_t need = kda::chunk_workspace_bytes(n_seqs, ntok, H, dk, dv);
+    const size_t need = kda::chunk_workspace_bytes(n_seqs, ntok, H, dk, in_dtype);
     if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE;
 
     const int64_t state_bytes = int64_t(n_seqs) * H * dk * dv * 4;
@@ -104,6 +104,8 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
         return KDA_ERR_INVALID_ARGUMENT;
     for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_cu, r_ws})
         if (overlap(r_hT, x)) return KDA_ERR_INVALID_ARGUMENT;
+    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_h0, r_cu})
+        if (overlap(r_ws, x)) return KDA_ERR_INVALID_ARGUMENT;
 
     kda::ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;

@@ -1,11 +1,11 @@
-// kda_chunk.hip -- chunked KDA prefill on gfx950: one fused kernel per call.
+// kda_chunk.hip -- chunked KDA prefill on gfx950: an intra-block kernel and a state-passing kernel.
 //
 // Pages (titles as published):
 //   [bagrov] "Архитектура Kimi K3: как открытая модель с миллионным контекстом конкурирует с
 //            лидерами рынка" (bagrov.by): § "Как архитектура Kimi K3 удерживает миллион токенов
 //            контекста" (fixed state, delta rule, bounded forget factor), § "Уровень чипа:
-//            специализированное ядро FlashKDA" (the tokens of a block are processed together,
-//            then the state is passed on, spread over independent heads).
+//            специализированное ядро FlashKDA" (two steps: the tokens of a block are processed
+//            fully in parallel, then the state is passed on, spread over independent heads).
 //   [habr]   "Как устроена Kimi K3: …" (savepearlharbor.com), § "Последовательность: три KDA на
 //            один глобальный MLA" (g = g_min*sigmoid(exp(A) z) with g_min = -5 keeps the running
 //            decay inside the bf16 range, so every causal 16-token block, diagonal ones included,
@@ -20,19 +20,17 @@
 //   O  = scale * (Qt S + P W),          S <- Diag(e^{G_15}) S + Kb^T W
 // Kt, Qt, Kb lie in [-1, 1] (factors <= 1); Kd's factor is at most e^{16*5} = e^80, inside the
 // bf16 / fp32 range (e^88.7): the bound on g is what makes the diagonal block a plain dense
-// product.  Successive blocks are chained through S, so the 64-token chunk of the interface is
-// four blocks: its 64 x 64 triangular system is solved blockwise, the coupling between blocks
-// going through the state.
+// product.  Successive blocks are chained through S, so a 64-token chunk is four blocks and its
+// 64 x 64 triangular system is solved blockwise, the coupling going through the state.
 //
-// Work split: one 256-lane workgroup per (sequence, head, 64 state columns).  Each of the four
-// waves owns 16 state columns for the whole sequence, kept in fp32 MFMA accumulators.  Per
-// 64-token chunk:
-//   phase 1 (wave b handles block b): block-local cumsum by lane shuffles, decay factors and
-//           every MFMA operand written once to LDS in its final 16-bit format; A_b and P_b on
-//           MFMA; T'_b by substitution.  No workgroup barrier: a wave only reads what it wrote.
-//   phase 2 (every wave, its 16 columns, blocks 0..3 in order): Y = Kt S, O = Qt S, W, O += P W,
-//           o stored from registers, S <- e^{G_15} S + Kb^T W.
-// The next chunk's raw inputs are loaded into registers while the state pass runs.
+// 1. Intra-block kernel (everything that does not depend on S; fully parallel): one wave per
+//    (16-token block, head).  Block cumsum by quad-lane DPP moves, decay factors, A and P on
+//    MFMA from split-bf16 operands staged in LDS, T' by substitution; writes one record per
+//    (head, block) to the workspace: Kt, Qt, Kb^T in their MFMA formats, T', P, e^{G_15}.
+// 2. State-passing kernel (the sequential part): one 256-lane workgroup per (sequence, head,
+//    64 state columns); each wave owns 16 state columns in fp32 accumulators for the whole
+//    sequence.  A chunk's four records and its V rows stream into double-buffered LDS while the
+//    previous chunk is processed.
 // Precision: operands that are range-bounded use fp16 (11-bit significand) in one pass; the
 // diagonal products (factors up to e^80), T' X and P W use split bf16 (hi*hi + hi*lo + lo*hi).
 // For fp32 inputs every product is split bf16.
@@ -44,27 +42,27 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int CH = 64;      // tokens per chunk (four 16-token blocks)
-constexpr int BV = 64;      // state columns per workgroup (16 per wave)
-constexpr int NTHR = 256;
+constexpr int BLK = 16;     // tokens per block (one state step)
+constexpr int CH = 64;      // tokens per chunk streamed by the state kernel (four blocks)
+constexpr int STATE_WAVES = 2;   // waves per state-kernel workgroup (16 state columns each)
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// ---- LDS layouts ---------------------------------------------------------------------------
-// [64][DK] 16-bit arrays (token-major): 16-byte units of 8 channels, unit index XOR (row & 7)
-// so that the 16 rows of an MFMA fragment read fall in different banks.
-template <int DK>
-__device__ __forceinline__ int tok_major(int r, int c) {
-    return r * DK + ((((c >> 3) ^ (r & 7))) << 3) + (c & 7);
-}
-// [DK][64] 16-bit arrays (channel-major), same swizzle on units of 8 tokens.
-__device__ __forceinline__ int ch_major(int c, int t) {
-    return c * CH + ((((t >> 3) ^ (c & 7))) << 3) + (t & 7);
+// Buffer resource over [base, base + bytes): raw (unswizzled, stride 0) accesses whose byte offset
+// lies outside the range read 0 and write nothing, so loads and stores need no branches and the
+// compiler can count outstanding memory operations exactly.  Word 3 selects 32-bit data format.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
 }
 
 // 2^x with one v_exp_f32.  Every factor formed here lies in [2^-116, 2^116] (a 16-token span
@@ -75,32 +73,10 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 __device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
-__device__ __forceinline__ uint16_t f16_bits(float x) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-}
-
-// ---- MFMA wrappers (operands already in their 16-bit format) --------------------------------
-__device__ __forceinline__ f32x4 mfma32_bf16_x3(const bf16x8& ah, const bf16x8& al,
-                                                const bf16x8& bh, const bf16x8& bl, f32x4 c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16_bf16_x3(const s16x4& ah, const s16x4& al,
-                                                const s16x4& bh, const s16x4& bl, f32x4 c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Two fp32 values -> packed bf16 hi word and packed bf16 lo word (x = hi + lo to ~16 bits).
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-    const bf16x2 h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
-    hi = __builtin_bit_cast(uint32_t, h);
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
     const float r0 = x0 - __uint_as_float(hi << 16);
     const float r1 = x1 - __uint_as_float(hi & 0xffff0000u);
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
@@ -108,8 +84,6 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
 __device__ __forceinline__ uint32_t f16_pair(float x0, float x1) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, f16x2));
 }
-
-// four fp32 values -> bf16 hi/lo pairs (16x16x16 operand layout)
 __device__ __forceinline__ void split4(const f32x4& x, s16x4& hi, s16x4& lo) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -127,7 +101,68 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& 
     }
 }
 
-// Prefetched raw inputs of one staging lane: 4 tokens x CPT channels.
+// ---- MFMA wrappers (operands already in their 16-bit format) --------------------------------
+__device__ __forceinline__ f32x4 mfma32_bf16_x3(const bf16x8& ah, const bf16x8& al,
+                                                const bf16x8& bh, const bf16x8& bl, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_bf16_x3(const s16x4& ah, const s16x4& al,
+                                                const s16x4& bh, const s16x4& bl, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+}
+
+// ---- quad-lane moves (lanes 4k..4k+3) -------------------------------------------------------
+// DPP quad_perm: lane 4k+i receives the value of lane 4k+perm[i].
+template <int PERM>
+__device__ __forceinline__ float quad_perm(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), PERM, 0xf, 0xf, false));
+}
+constexpr int QP_PREV1 = 0 | (0 << 2) | (1 << 4) | (2 << 6);   // [0,0,1,2]
+constexpr int QP_PREV2 = 0 | (0 << 2) | (0 << 4) | (1 << 6);   // [0,0,0,1]
+constexpr int QP_LAST = 3 | (3 << 2) | (3 << 4) | (3 << 6);    // [3,3,3,3]
+
+// ---- layouts ---------------------------------------------------------------------------------
+// [16][DK] 16-bit arrays (token-major): 16-byte units of 8 channels, unit index XOR (row & 7)
+// so that the 16 rows of an MFMA fragment read fall in different banks.
+template <int DK>
+__device__ __forceinline__ int tok_major(int r, int c) {
+    return r * DK + ((((c >> 3) ^ (r & 7))) << 3) + (c & 7);
+}
+// Record arrays are stored in MFMA fragment order, so that the state pass reads each operand
+// with one contiguous 16- or 8-byte load per lane (1 KB / 512 B per wave, no bank conflicts):
+//   frag32: [16][DK] operand of a 16x16x32 product (row = token, K = channel): fragment kk,
+//           lane (m, q) holds channels 32kk + 4q + {0..3} in slots 0..3 and 32kk + 16 + 4q + {0..3}
+//           in slots 4..7 -- the K order in which the state tiles are packed as the B operand.
+//   frag16: [DK][16] operand of a 16x16x16 product (row = channel, K = token): tile i, lane
+//           (m, q) holds channel 16i + m, tokens 4q .. 4q + 3.
+//   fragT : [16][16] operand of a 16x16x16 product: lane (m, q) holds row m, columns 4q .. 4q + 3.
+__device__ __forceinline__ int frag32(int r, int c) {
+    return ((c >> 5) * 64 + r + 16 * ((c & 15) >> 2)) * 8 + ((c & 16) >> 2) + (c & 3);
+}
+__device__ __forceinline__ int frag16(int c, int t) { return ((c >> 4) * 64 + (c & 15) + 16 * (t >> 2)) * 4 + (t & 3); }
+__device__ __forceinline__ int fragT(int r, int s) { return (r + 16 * (s >> 2)) * 4 + (s & 3); }
+
+// Record of one (head, block) in the workspace (byte offsets).  E = 16 * DK elements per array.
+//   fast   : [Kt fp16 frag32][Qt fp16 frag32][Kb^T fp16 frag16]
+//   precise: [Kt hi][Kt lo][Qt hi][Qt lo] (bf16 frag32) [Kb^T hi][Kb^T lo] (bf16 frag16)
+//   then T' hi, T' lo, P hi, P lo (bf16 fragT), then e^{G_15} - 1 (DK fp32).
+// An all-zero record is the identity step (W = 0, S unchanged), which lets the state pass run
+// every chunk as four blocks without branches: blocks past a sequence's end read zeros.
+template <int DK, bool PRECISE>
+struct Rec {
+    static constexpr int E = BLK * DK;
+    static constexpr int NA = PRECISE ? 6 : 3;
+    static constexpr int OFF_T = NA * E * 2;
+    static constexpr int OFF_G = OFF_T + 4 * 256 * 2;
+    static constexpr int BYTES = OFF_G + DK * 4;
+    static_assert(BYTES % 16 == 0, "record alignment");
+};
+
+// Raw inputs held by one staging lane: 4 tokens x CPT channels; bf16 packed two per register.
 template <int DT, int N>
 struct Raw;
 template <int N>
@@ -142,8 +177,6 @@ struct Raw<KDA_BF16, N> {
         return (i & 1) ? __uint_as_float(v[i / 2] & 0xffff0000u) : __uint_as_float(v[i / 2] << 16);
     }
 };
-
-// Load CPT consecutive (channel-contiguous) elements at element offset e into row slot i.
 template <int DT, int CPT, int N>
 __device__ __forceinline__ void load_row(Raw<DT, N>& dst, int slot, const void* base, int32_t e,
                                          bool ok) {
@@ -171,320 +204,394 @@ __device__ __forceinline__ void load_row(Raw<DT, N>& dst, int slot, const void* 
 }
 
 template <int NP>
-__device__ __forceinline__ void store_words(uint16_t* dst, const uint32_t (&w)[NP]) {
+__device__ __forceinline__ void store_words(void* dst, const uint32_t (&w)[NP]) {
     if constexpr (NP == 4) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     else *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
 }
 
-// ---- the fused kernel -----------------------------------------------------------------------
-template <int DK, int IDT, int GDT, int ODT, bool PRECISE>
-__global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t n_vblk) {
-    constexpr int KS = DK / 32;          // 32-channel K-steps
-    constexpr int CT = DK / 16;          // 16-channel tiles of the state
-    constexpr int CPT = DK / 16;         // channels per staging lane (8 or 4)
-    constexpr int NEL = 4 * CPT;         // elements per staging lane per chunk
-    constexpr float LOG2E = 1.4426950408889634f;
-
-    // MFMA-ready operands of one chunk (16-bit; layouts tok_major / ch_major)
-    __shared__ __attribute__((aligned(16))) uint16_t sKh[CH * DK], sKl[CH * DK];   // Kt  bf16 hi/lo
-    __shared__ __attribute__((aligned(16))) uint16_t sQh[CH * DK], sQl[CH * DK];   // Qt  bf16 hi/lo
-    __shared__ __attribute__((aligned(16))) uint16_t sDh[CH * DK], sDl[CH * DK];   // Kd  bf16 hi/lo
-    // fast path: sX0 = Kt fp16, sX1 = Qt fp16 (token-major), sX2 = Kb^T fp16 (channel-major);
-    // precise path: sX0 / sX1 = Kb^T bf16 hi / lo (channel-major), sX2 unused.
-    __shared__ __attribute__((aligned(16))) uint16_t sX0[CH * DK], sX1[CH * DK];
-    __shared__ __attribute__((aligned(16))) uint16_t sX2[PRECISE ? 8 : CH * DK];
-    __shared__ __attribute__((aligned(16))) float sA[4][16][16];                   // beta-scaled A_b
-    __shared__ __attribute__((aligned(16))) uint16_t sPh[4][16][16], sPl[4][16][16];
-    __shared__ __attribute__((aligned(16))) uint16_t sTh[4][16][16], sTl[4][16][16];
-    __shared__ __attribute__((aligned(16))) float sGam[4][DK];                     // e^{G_15}
-    // V of the chunk as fp32 [4 blocks][16 rows][64 columns]: for d_k = 128 it lives in the rows
-    // of sDh that the block's own A/P products have finished with; for d_k = 64 in sV64.
-    __shared__ __attribute__((aligned(16))) float sV64[DK == 64 ? 4 * 16 * BV : 4];
-    __shared__ float sBeta[CH];
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int ln = lane & 15, lq = lane >> 4;        // MFMA lane coordinates
-    const int cg = lane >> 2, sub = lane & 3;        // staging lane: channel group, token quad
-
-    // Workgroup -> (unit, column block).  The column blocks of one unit sit 8 workgroup ids
-    // apart so they land on the same XCD and share its L2 for the unit's q / k / g reads.
-    const int64_t units = static_cast<int64_t>(p.n_seqs) * p.H;
-    const int64_t bid = blockIdx.x;
-    const int64_t grp = bid / (8 * n_vblk), rem = bid % (8 * n_vblk);
-    const int vb = static_cast<int>(rem / 8);
-    const int64_t unit = grp * 8 + rem % 8;
-    if (unit >= units) return;
-    const int n = static_cast<int>(unit / p.H), h = static_cast<int>(unit % p.H);
-    const int DV = p.dv;
-    const int n0 = vb * BV + wave * 16;              // this wave's first state column
-    const int64_t H = p.H;
-
-    int64_t bos, len;
+// Locate the block slot of a workgroup: sequence n, block j inside it, or false when the slot
+// is past its sequence's end.  Slot bases: n * ceil(T/16) for fixed-length batches,
+// floor(cu[n]/16) + n for packed ones (ceil(len/16) <= floor(len/16) + 1 keeps them disjoint).
+__device__ __forceinline__ bool locate_slot(const ChunkArgs& p, int64_t slot, int& n,
+                                            int64_t& j, int64_t& bos, int64_t& len) {
     if (p.cu) {
+        int lo = 0, hi = p.n_seqs - 1;
+        while (lo < hi) {                 // largest n with base(n) <= slot
+            const int mid = (lo + hi + 1) >> 1;
+            const int64_t base = static_cast<int64_t>(p.cu[mid] / BLK) + mid;
+            if (base <= slot) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
         bos = p.cu[n];
         len = static_cast<int64_t>(p.cu[n + 1]) - bos;
+        j = slot - (static_cast<int64_t>(p.cu[n] / BLK) + n);
     } else {
+        const int64_t nblk = (p.T + BLK - 1) / BLK;
+        if (nblk == 0) return false;
+        n = static_cast<int>(slot / nblk);
+        j = slot % nblk;
+        if (n >= p.n_seqs) return false;
         bos = static_cast<int64_t>(n) * p.T;
         len = p.T;
     }
+    return j >= 0 && BLK * j < len;
+}
 
-    // state tiles: lane (ln, lq) of tile i holds S[16i + 4lq + r][n0 + ln]
-    f32x4 S[CT];
-    const int64_t sbase = unit * DK * DV;
-#pragma unroll
-    for (int i = 0; i < CT; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S[i][r] = p.h0 ? p.h0[sbase + static_cast<int64_t>(16 * i + 4 * lq + r) * DV + n0 + ln] : 0.f;
+// ============================================================================================
+// 1. intra-block kernel: one wave per (block slot, head)
+// ============================================================================================
+template <int DK, int IDT, int GDT, bool PRECISE>
+__global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
+    using R = Rec<DK, PRECISE>;
+    constexpr int CPT = DK / 16;          // channels per lane (8 or 4)
+    constexpr int NEL = 4 * CPT;          // elements per lane
+    constexpr int KS = DK / 32;
+    constexpr float LOG2E = 1.4426950408889634f;
 
-    // ---- prefetched inputs of the next chunk
+    __shared__ __attribute__((aligned(16))) uint16_t sKh[R::E], sKl[R::E];   // Kt  hi/lo
+    __shared__ __attribute__((aligned(16))) uint16_t sQh[R::E], sQl[R::E];   // Qt  hi/lo
+    __shared__ __attribute__((aligned(16))) uint16_t sDh[R::E], sDl[R::E];   // Kd  hi/lo
+    __shared__ __attribute__((aligned(16))) float sA[16][16];
+    __shared__ float sBeta[16];
+
+    const int lane = threadIdx.x;
+    const int ln = lane & 15, lq = lane >> 4;
+    const int cg = lane >> 2, sub = lane & 3;
+
+    const int64_t H = p.H;
+    const int64_t slot = blockIdx.x / H;
+    const int h = static_cast<int>(blockIdx.x % H);
+    int n;
+    int64_t j, bos, len;
+    if (!locate_slot(p, slot, n, j, bos, len)) return;
+    const int64_t t0 = BLK * j;
+    const int nt = static_cast<int>((len - t0) < BLK ? (len - t0) : BLK);
+    uint8_t* rec = ws + (static_cast<int64_t>(h) * nslots + slot) * R::BYTES;
+
+    // ---- inputs: rows 4sub..4sub+3, channels CPT*cg.. ; beta in lanes 0..15
     Raw<GDT, NEL> pg;
     Raw<IDT, NEL> pk, pq;
-    uint32_t pbeta = 0u;              // raw bits of this lane's beta (converted when used)
-    // V rows of this wave's block for the workgroup's 64 columns: lane -> row lane/4, 16 columns
-    Raw<IDT, 16> pv;
-    auto vslab = [&](int b) -> float* {
-        if constexpr (DK == 128) return reinterpret_cast<float*>(sDh + 16 * b * DK);
-        else return sV64 + b * 16 * BV;
-    };
-    // Per-chunk base pointers are uniform (scalar registers); per-lane offsets stay 32-bit.
-    const int32_t kstride = static_cast<int32_t>(H) * DK;    // elements between tokens in q/k/g
-    const int32_t vstride = static_cast<int32_t>(H) * DV;    // ... in v and o
-    auto prefetch = [&](int64_t t0, int nt) {
-        const int64_t row0 = (bos + t0) * H + h;             // token t0 of this head
+    {
+        const int64_t row0 = (bos + t0) * H + h;
+        const int32_t kstride = static_cast<int32_t>(H) * DK;
         const void* gbase = static_cast<const char*>(p.g) + row0 * DK * (GDT == KDA_F32 ? 4 : 2);
         const void* kbase = static_cast<const char*>(p.k) + row0 * DK * (IDT == KDA_F32 ? 4 : 2);
         const void* qbase = static_cast<const char*>(p.q) + row0 * DK * (IDT == KDA_F32 ? 4 : 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 16 * wave + 4 * sub + i;
+            const int r = 4 * sub + i;
             const bool ok = r < nt;
             const int32_t e = ok ? r * kstride + CPT * cg : 0;
             load_row<GDT, CPT>(pg, i, gbase, e, ok);
             load_row<IDT, CPT>(pk, i, kbase, e, ok);
             load_row<IDT, CPT>(pq, i, qbase, e, ok);
         }
-        {
+        if (lane < 16) {
             const void* bbase = static_cast<const char*>(p.beta) + row0 * (IDT == KDA_F32 ? 4 : 2);
-            const int r = 16 * wave + lane;
-            const int32_t e = r * static_cast<int32_t>(H);
-            if constexpr (IDT == KDA_F32)
-                pbeta = (lane < 16 && r < nt) ? static_cast<const uint32_t*>(bbase)[e] : 0u;
-            else
-                pbeta = (lane < 16 && r < nt) ? uint32_t(static_cast<const uint16_t*>(bbase)[e]) : 0u;
+            sBeta[lane] = (lane < nt) ? load_as_f32<IDT>(bbase, lane * static_cast<int32_t>(H)) : 0.f;
         }
-        {
-            const void* vbase = static_cast<const char*>(p.v) +
-                                (row0 * DV + vb * BV) * (IDT == KDA_F32 ? 4 : 2);
-            const int r = 16 * wave + (lane >> 2);
-            const bool ok = r < nt;
-            const int32_t e = ok ? r * vstride + 16 * (lane & 3) : 0;
-            load_row<IDT, 8>(pv, 0, vbase, e, ok);
-            load_row<IDT, 8>(pv, 1, vbase, e + 8, ok);
+    }
+
+    // ---- block cumsum (log2 units): own 4 tokens, then a scan over the 4 lanes of the group
+    float G2[NEL];
+    float G15[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            run += pg.get(i * CPT + c) * LOG2E;
+            G2[i * CPT + c] = run;
+        }
+        float incl = run;
+        const float u1 = quad_perm<QP_PREV1>(incl);
+        if (sub >= 1) incl += u1;
+        const float u2 = quad_perm<QP_PREV2>(incl);
+        if (sub >= 2) incl += u2;
+        const float excl = incl - run;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) G2[i * CPT + c] += excl;
+        G15[c] = quad_perm<QP_LAST>(incl);
+    }
+
+    // ---- decay factors, operands
+    constexpr int NP = CPT / 2;
+    float kb[NEL];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * sub + i;
+        float kt[CPT], qt[CPT], kd[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const float g2 = G2[i * CPT + c];
+            const float e1 = fexp2(g2);                   // e^{G}        <= 1
+            const float e2 = fexp2(G15[c] - g2);          // e^{G15 - G}  <= 1
+            const float kv = pk.get(i * CPT + c);
+            kt[c] = kv * e1;
+            qt[c] = pq.get(i * CPT + c) * e1;
+            kb[i * CPT + c] = kv * e2;
+            kd[c] = kv * (e2 * fexp2(-G15[c]));           // e^{-G} <= e^80
+        }
+        uint32_t wKh[NP], wKl[NP], wQh[NP], wQl[NP], wDh[NP], wDl[NP];
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+            split_pair(kt[2 * u], kt[2 * u + 1], wKh[u], wKl[u]);
+            split_pair(qt[2 * u], qt[2 * u + 1], wQh[u], wQl[u]);
+            split_pair(kd[2 * u], kd[2 * u + 1], wDh[u], wDl[u]);
+        }
+        const int off = tok_major<DK>(r, CPT * cg);
+        store_words<NP>(sKh + off, wKh); store_words<NP>(sKl + off, wKl);
+        store_words<NP>(sQh + off, wQh); store_words<NP>(sQl + off, wQl);
+        store_words<NP>(sDh + off, wDh); store_words<NP>(sDl + off, wDl);
+        // record: the state pass's Kt, Qt operands (frag32: four channels = 8 contiguous bytes)
+#pragma unroll
+        for (int h4 = 0; h4 < CPT / 4; ++h4) {
+            const int fo = 2 * frag32(r, CPT * cg + 4 * h4);
+            if constexpr (!PRECISE) {
+                *reinterpret_cast<uint2*>(rec + fo) =
+                    make_uint2(f16_pair(kt[4 * h4], kt[4 * h4 + 1]), f16_pair(kt[4 * h4 + 2], kt[4 * h4 + 3]));
+                *reinterpret_cast<uint2*>(rec + 2 * R::E + fo) =
+                    make_uint2(f16_pair(qt[4 * h4], qt[4 * h4 + 1]), f16_pair(qt[4 * h4 + 2], qt[4 * h4 + 3]));
+            } else {
+                *reinterpret_cast<uint2*>(rec + fo) = make_uint2(wKh[2 * h4], wKh[2 * h4 + 1]);
+                *reinterpret_cast<uint2*>(rec + 2 * R::E + fo) = make_uint2(wKl[2 * h4], wKl[2 * h4 + 1]);
+                *reinterpret_cast<uint2*>(rec + 4 * R::E + fo) = make_uint2(wQh[2 * h4], wQh[2 * h4 + 1]);
+                *reinterpret_cast<uint2*>(rec + 6 * R::E + fo) = make_uint2(wQl[2 * h4], wQl[2 * h4 + 1]);
+            }
+        }
+    }
+    // record: Kb^T (frag16: the lane's 4 tokens of each channel are contiguous)
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int off = frag16(CPT * cg + c, 4 * sub);
+        if constexpr (!PRECISE) {
+            *reinterpret_cast<uint2*>(rec + 2 * (2 * R::E + off)) =
+                make_uint2(f16_pair(kb[0 * CPT + c], kb[1 * CPT + c]), f16_pair(kb[2 * CPT + c], kb[3 * CPT + c]));
+        } else {
+            uint32_t h0, l0, h1, l1;
+            split_pair(kb[0 * CPT + c], kb[1 * CPT + c], h0, l0);
+            split_pair(kb[2 * CPT + c], kb[3 * CPT + c], h1, l1);
+            *reinterpret_cast<uint2*>(rec + 2 * (4 * R::E + off)) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2*>(rec + 2 * (5 * R::E + off)) = make_uint2(l0, l1);
+        }
+    }
+    // record: e^{G_15} - 1 (same absolute precision as e^{G_15} in fp32)
+    if (sub == 0) {
+        float* gam = reinterpret_cast<float*>(rec + R::OFF_G) + CPT * cg;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) gam[c] = fexp2(G15[c]) - 1.f;
+    }
+
+    __syncthreads();   // the operand arrays and beta are read across lanes below
+
+    // ---- A and P (16 x 16, contraction over d_k) on MFMA
+    {
+        f32x4 accA = zero4(), accP = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const int off = tok_major<DK>(ln, 32 * kk + 8 * lq);
+            const bf16x8 kh = *reinterpret_cast<const bf16x8*>(sKh + off);
+            const bf16x8 kl = *reinterpret_cast<const bf16x8*>(sKl + off);
+            const bf16x8 qh = *reinterpret_cast<const bf16x8*>(sQh + off);
+            const bf16x8 ql = *reinterpret_cast<const bf16x8*>(sQl + off);
+            const bf16x8 dh = *reinterpret_cast<const bf16x8*>(sDh + off);
+            const bf16x8 dl = *reinterpret_cast<const bf16x8*>(sDl + off);
+            accA = mfma32_bf16_x3(kh, kl, dh, dl, accA);
+            accP = mfma32_bf16_x3(qh, ql, dh, dl, accP);
+        }
+        // lane (ln, lq) holds rows 4lq + i of column ln
+        uint16_t* Ph = reinterpret_cast<uint16_t*>(rec + R::OFF_T + 1024);
+        uint16_t* Pl = reinterpret_cast<uint16_t*>(rec + R::OFF_T + 1536);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lq + i, s = ln;
+            sA[r][s] = (s < r) ? accA[i] * sBeta[r] : 0.f;
+            const float pval = (s <= r) ? accP[i] : 0.f;
+            const uint16_t ph = bf16_bits(pval);
+            Ph[fragT(r, s)] = ph;
+            Pl[fragT(r, s)] = bf16_bits(pval - bf16_val(ph));
+        }
+    }
+    __syncthreads();   // sA rows are read by other lanes
+
+    // ---- T' = (I + A)^{-1} Diag(beta): forward substitution, lane j = column j; rows are read
+    // one ahead of use and each row's dot product runs as four independent partial sums
+    if (lane < 16) {
+        const int jc = lane;
+        float t[16];
+        float4 nxt[4], cur[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) nxt[u] = *reinterpret_cast<const float4*>(&sA[1][4 * u]);
+        t[0] = (jc == 0) ? 1.f : 0.f;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+            if (r + 1 < 16) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (4 * u < r + 1) nxt[u] = *reinterpret_cast<const float4*>(&sA[r + 1][4 * u]);
+            }
+            float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sp = 0; sp < r; ++sp) {
+                const float4& c4 = cur[sp >> 2];
+                const float a = (sp & 3) == 0 ? c4.x : (sp & 3) == 1 ? c4.y : (sp & 3) == 2 ? c4.z : c4.w;
+                part[sp & 3] += a * t[sp];
+            }
+            t[r] = ((r == jc) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
+        }
+        const float bj = sBeta[jc];
+        uint16_t* Th = reinterpret_cast<uint16_t*>(rec + R::OFF_T);
+        uint16_t* Tl = reinterpret_cast<uint16_t*>(rec + R::OFF_T + 512);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float x = t[r] * bj;
+            const uint16_t th = bf16_bits(x);
+            Th[fragT(r, jc)] = th;
+            Tl[fragT(r, jc)] = bf16_bits(x - bf16_val(th));
+        }
+    }
+}
+
+// ============================================================================================
+// 2. state-passing kernel: one workgroup of NW waves per (sequence, head, 16 NW state columns)
+// ============================================================================================
+// s_waitcnt immediate for "vmcnt <= n", other counters unconstrained.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+template <int DK, int IDT, int ODT, bool PRECISE, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, int32_t n_vblk,
+                                                                 int64_t nslots, const uint8_t* ws) {
+    using R = Rec<DK, PRECISE>;
+    constexpr int KS = DK / 32;
+    constexpr int CT = DK / 16;
+    constexpr int NB = PRECISE ? 2 : 4;                // 16-token blocks per streamed chunk
+    constexpr int CHT = NB * BLK;                      // tokens per chunk
+    constexpr int ESZ = (IDT == KDA_F32) ? 4 : 2;
+    constexpr int OSZ = (ODT == KDA_F32) ? 4 : 2;
+    constexpr int WKB = 64 * 16;                       // bytes one wave moves per DMA load
+    constexpr int ROUNDS = (NB * R::BYTES + NW * WKB - 1) / (NW * WKB);
+    constexpr int LBYTES = ROUNDS * NW * WKB;          // a chunk's records, padded to whole rounds
+    constexpr int BVW = 16 * NW;                       // state columns per workgroup
+    constexpr int NV = NB * 4;                         // V values per lane per chunk
+    constexpr int E2 = 2 * R::E;                       // bytes of one 16-bit operand array
+
+    // Two chunk buffers.  The loop below is unrolled by two so that every access names its
+    // buffer statically: the compiler then knows the records streaming into one buffer do not
+    // alias the reads of the other and inserts no waits for them.
+    __shared__ __attribute__((aligned(16))) uint8_t bufA[LBYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t bufB[LBYTES];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int ln = lane & 15, lq = lane >> 4;
+
+    // Workgroup -> (unit, column block).  The column blocks of one unit sit 8 workgroup ids
+    // apart so they land on the same XCD and share its L2 for the unit's records.
+    const int64_t units = static_cast<int64_t>(p.n_seqs) * p.H;
+    const int64_t bid = blockIdx.x;
+    const int64_t grp = bid / (8 * n_vblk), remv = bid % (8 * n_vblk);
+    const int vb = static_cast<int>(remv / 8);
+    const int64_t unit = grp * 8 + remv % 8;
+    if (unit >= units) return;
+    const int n = static_cast<int>(unit / p.H), h = static_cast<int>(unit % p.H);
+    const int DV = p.dv;
+    const int n0 = vb * BVW + wave * 16;               // this wave's first state column
+    const int64_t H = p.H;
+    const int32_t vstride = static_cast<int32_t>(H) * DV;
+
+    int64_t bos, len, base;
+    if (p.cu) {
+        bos = p.cu[n];
+        len = static_cast<int64_t>(p.cu[n + 1]) - bos;
+        base = static_cast<int64_t>(p.cu[n] / BLK) + n;
+    } else {
+        bos = static_cast<int64_t>(n) * p.T;
+        len = p.T;
+        base = static_cast<int64_t>(n) * ((p.T + BLK - 1) / BLK);
+    }
+    const uint8_t* recs = ws + (static_cast<int64_t>(h) * nslots + base) * R::BYTES;
+
+    // state tiles: lane (ln, lq) of tile i holds S[16i + 4lq + r][n0 + ln]
+    f32x4 S[CT];
+    const int64_t sbase = unit * DK * DV;
+    {
+        // an absent initial state is an empty range: every load reads 0
+        const __amdgpu_buffer_rsrc_t h0r =
+            make_rsrc(p.h0 ? p.h0 + sbase : nullptr, p.h0 ? static_cast<uint32_t>(DK * DV * 4) : 0u);
+#pragma unroll
+        for (int i = 0; i < CT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[i][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    h0r, ((16 * i + 4 * lq + r) * DV + n0 + ln) * 4, 0, 0));
+    }
+
+    auto tokens_in = [&](int64_t c) -> int {            // tokens of chunk c (0 past the end)
+        const int64_t rem = len - c * CHT;
+        return static_cast<int>(rem < 0 ? 0 : rem < CHT ? rem : CHT);
+    };
+    // Chunk c's records go straight from memory into an LDS buffer (records past the sequence's
+    // last block, and the padding, read as zeros: identity steps); its V entries go to registers.
+    auto fill = [&](uint8_t* buf, int64_t c) {
+        const int nt = tokens_in(c);
+        const int nbk = (nt + BLK - 1) / BLK;
+        const __amdgpu_buffer_rsrc_t rr =
+            make_rsrc(nt > 0 ? recs + c * NB * R::BYTES : ws, static_cast<uint32_t>(nbk * R::BYTES));
+#pragma unroll
+        for (int k = 0; k < ROUNDS; ++k) {
+            const int u = k * NW + wave;                // this wave's 1 KB unit of the buffer
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rr, (__attribute__((address_space(3))) void*)(buf + u * WKB), 16, u * WKB + 16 * lane,
+                0, 0, 0);
         }
     };
-
-    const int64_t nchunks = (len + CH - 1) / CH;
-    if (nchunks > 0) prefetch(0, static_cast<int>(len < CH ? len : CH));
-
-    for (int64_t ci = 0; ci < nchunks; ++ci) {
-        const int64_t t0 = ci * CH;
-        const int nt = static_cast<int>((len - t0) < CH ? (len - t0) : CH);
-        const int blk = wave;                         // this wave stages / prepares block blk
-
-        // ============ phase 1: staging of block blk (lane: 4 tokens x CPT channels) ==========
-        {
-            // block-local cumsum along tokens in log2 units: the lane's own 4 tokens, then a scan
-            // across the 4 adjacent lanes that hold the same channel group
-            float G2[NEL];
+    auto load_v = [&](uint32_t (&dst)[NV], int64_t c) {
+        const int nt = tokens_in(c);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(
+            nt > 0 ? static_cast<const uint8_t*>(p.v) + ((bos + c * CHT) * H + h) * DV * ESZ : p.v,
+            static_cast<uint32_t>(nt * vstride * ESZ));
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                float run = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    run += pg.get(i * CPT + j) * LOG2E;
-                    G2[i * CPT + j] = run;
-                }
-                float incl = run;
-                float up = __shfl_up(incl, 1, 4);
-                if (sub >= 1) incl += up;
-                up = __shfl_up(incl, 2, 4);
-                if (sub >= 2) incl += up;
-                const float excl = incl - run;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) G2[i * CPT + j] += excl;
-            }
-            float G15[CPT];
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) G15[j] = __shfl(G2[3 * CPT + j], (lane & ~3) | 3, 64);
-
-            const int r0 = 16 * blk + 4 * sub;
-            if (sub == 0) {
-#pragma unroll
-                for (int j = 0; j < CPT; ++j) sGam[blk][CPT * cg + j] = fexp2(G15[j]);
-            }
-            if (lane < 16)
-                sBeta[16 * blk + lane] = (IDT == KDA_F32) ? __uint_as_float(pbeta) : __uint_as_float(pbeta << 16);
-
-            float kb[NEL];
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float kt[CPT], qt[CPT], kd[CPT];
-#pragma unroll
-                for (int j = 0; j < CPT; ++j) {
-                    const float g2 = G2[i * CPT + j];
-                    const float e1 = fexp2(g2);                   // e^{G}        <= 1
-                    const float e2 = fexp2(G15[j] - g2);          // e^{G15 - G}  <= 1
-                    const float kv = pk.get(i * CPT + j);
-                    kt[j] = kv * e1;
-                    qt[j] = pq.get(i * CPT + j) * e1;
-                    kb[i * CPT + j] = kv * e2;
-                    kd[j] = kv * (e2 * fexp2(-G15[j]));           // e^{-G} <= e^80
-                }
-                constexpr int NP = CPT / 2;            // packed pairs per row segment
-                uint32_t wKh[NP], wKl[NP], wQh[NP], wQl[NP], wDh[NP], wDl[NP], wK16[NP], wQ16[NP];
-#pragma unroll
-                for (int u = 0; u < NP; ++u) {
-                    split_pair(kt[2 * u], kt[2 * u + 1], wKh[u], wKl[u]);
-                    split_pair(qt[2 * u], qt[2 * u + 1], wQh[u], wQl[u]);
-                    split_pair(kd[2 * u], kd[2 * u + 1], wDh[u], wDl[u]);
-                    wK16[u] = f16_pair(kt[2 * u], kt[2 * u + 1]);
-                    wQ16[u] = f16_pair(qt[2 * u], qt[2 * u + 1]);
-                }
-                const int off = tok_major<DK>(r0 + i, CPT * cg);
-                store_words<NP>(sKh + off, wKh); store_words<NP>(sKl + off, wKl);
-                store_words<NP>(sQh + off, wQh); store_words<NP>(sQl + off, wQl);
-                store_words<NP>(sDh + off, wDh); store_words<NP>(sDl + off, wDl);
-                if constexpr (!PRECISE) {
-                    store_words<NP>(sX0 + off, wK16);
-                    store_words<NP>(sX1 + off, wQ16);
-                }
+                const int off = ((16 * b + 4 * lq + i) * vstride + n0 + ln) * ESZ;
+                if constexpr (ESZ == 4) dst[4 * b + i] = __builtin_amdgcn_raw_buffer_load_b32(vr, off, 0, 0);
+                else dst[4 * b + i] = __builtin_amdgcn_raw_buffer_load_b16(vr, off, 0, 0);
             }
-            // channel-major Kb^T: the lane's 4 tokens of each channel are contiguous
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                const int off = ch_major(CPT * cg + j, r0);
-                if constexpr (!PRECISE) {
-                    *reinterpret_cast<uint2*>(sX2 + off) =
-                        make_uint2(f16_pair(kb[0 * CPT + j], kb[1 * CPT + j]),
-                                   f16_pair(kb[2 * CPT + j], kb[3 * CPT + j]));
-                } else {
-                    uint32_t h0, l0, h1, l1;
-                    split_pair(kb[0 * CPT + j], kb[1 * CPT + j], h0, l0);
-                    split_pair(kb[2 * CPT + j], kb[3 * CPT + j], h1, l1);
-                    *reinterpret_cast<uint2*>(sX0 + off) = make_uint2(h0, h1);
-                    *reinterpret_cast<uint2*>(sX1 + off) = make_uint2(l0, l1);
-                }
-            }
-        }
-        // ---- A_b and P_b (16 x 16, contraction over d_k) on MFMA; this wave's block only
-        {
-            f32x4 accA = zero4(), accP = zero4();
-            const int row = 16 * blk + ln;
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const int off = tok_major<DK>(row, 32 * kk + 8 * lq);
-                const bf16x8 kh = *reinterpret_cast<const bf16x8*>(sKh + off);
-                const bf16x8 kl = *reinterpret_cast<const bf16x8*>(sKl + off);
-                const bf16x8 qh = *reinterpret_cast<const bf16x8*>(sQh + off);
-                const bf16x8 ql = *reinterpret_cast<const bf16x8*>(sQl + off);
-                const bf16x8 dh = *reinterpret_cast<const bf16x8*>(sDh + off);
-                const bf16x8 dl = *reinterpret_cast<const bf16x8*>(sDl + off);
-                accA = mfma32_bf16_x3(kh, kl, dh, dl, accA);
-                accP = mfma32_bf16_x3(qh, ql, dh, dl, accP);
-            }
-            // lane (ln, lq) holds rows 4lq + i of column ln of the block
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * lq + i, s = ln;
-                sA[blk][r][s] = (s < r) ? accA[i] * sBeta[16 * blk + r] : 0.f;
-                const float pval = (s <= r) ? accP[i] : 0.f;
-                const uint16_t ph = bf16_bits(pval);
-                sPh[blk][r][s] = ph;
-                sPl[blk][r][s] = bf16_bits(pval - bf16_val(ph));
-            }
-        }
-        // ---- this block's V rows into the slab (the block's sDh rows are no longer needed)
-        {
-            float* dst = vslab(blk) + (lane >> 2) * BV + 16 * (lane & 3);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                *reinterpret_cast<float4*>(dst + 4 * u) =
-                    make_float4(pv.get(4 * u), pv.get(4 * u + 1), pv.get(4 * u + 2), pv.get(4 * u + 3));
-        }
-        // ---- T'_b = (I + A_b)^{-1} Diag(beta_b): forward substitution, lane j = column j
-        if (lane < 16) {
-            // rows are read one ahead of their use; each row's dot product runs as four
-            // independent partial sums, so the dependent chain per row is short
-            const int j = lane;
-            float t[16];
-            float4 nxt[4], cur[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) nxt[u] = *reinterpret_cast<const float4*>(&sA[blk][1][4 * u]);
-            t[0] = (j == 0) ? 1.f : 0.f;
-#pragma unroll
-            for (int r = 1; r < 16; ++r) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
-                if (r + 1 < 16) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (4 * u < r + 1) nxt[u] = *reinterpret_cast<const float4*>(&sA[blk][r + 1][4 * u]);
-                }
-                float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int sp = 0; sp < r; ++sp) {
-                    const float4& c4 = cur[sp >> 2];
-                    const float a = (sp & 3) == 0 ? c4.x : (sp & 3) == 1 ? c4.y : (sp & 3) == 2 ? c4.z : c4.w;
-                    part[sp & 3] += a * t[sp];
-                }
-                t[r] = ((r == j) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
-            }
-            const float bj = sBeta[16 * blk + j];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float x = t[r] * bj;
-                const uint16_t th = bf16_bits(x);
-                sTh[blk][r][j] = th;
-                sTl[blk][r][j] = bf16_bits(x - bf16_val(th));
-            }
-        }
-        __syncthreads();
+    };
 
-        // next chunk's inputs: issued here, consumed by the next chunk's staging
-        if (ci + 1 < nchunks) {
-            const int64_t t1 = t0 + CH;
-            prefetch(t1, static_cast<int>((len - t1) < CH ? (len - t1) : CH));
-        }
-        const bool full = nt == CH;                   // uniform: no per-row guards needed
-        void* const obase = static_cast<char*>(p.o) +
-                            (((bos + t0) * H + h) * DV + n0) * (ODT == KDA_F32 ? 4 : 2);
-
-        // ============ phase 2: the state pass over the four blocks, this wave's 16 columns =======
+    // One chunk: NB state steps of 16 tokens from the records in `buf`.
+    auto run = [&](const uint8_t* buf, int64_t c, const uint32_t (&vc)[NV]) {
+        const int nt = tokens_in(c);
+        // o rows of this chunk and head; rows past the chunk's tokens fall outside the range
+        const __amdgpu_buffer_rsrc_t orr =
+            make_rsrc(static_cast<char*>(p.o) + ((bos + c * CHT) * H + h) * DV * OSZ,
+                      static_cast<uint32_t>(nt * vstride * OSZ));
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int row = 16 * b + ln;
+        for (int b = 0; b < NB; ++b) {
+            const uint8_t* rb = buf + b * R::BYTES;
+            const uint8_t* fr = rb + 16 * lane;         // this lane's frag32 entries
+            const uint16_t* Th = reinterpret_cast<const uint16_t*>(rb + R::OFF_T) + 4 * lane;
+            const uint16_t* Tl = Th + 256;
+            const uint16_t* Ph = Th + 512;
+            const uint16_t* Pl = Th + 768;
+            const float* gam = reinterpret_cast<const float*>(rb + R::OFF_G);   // e^{G_15} - 1
+
+            // Y = Kt S and O = Qt S (contraction over d_k; S packed as the B operand)
             f32x4 Y = zero4(), O = zero4();
             if constexpr (!PRECISE) {
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
-                    // B = S (channels 32kk.. as two 16-channel tiles); A rows read in the same K order
                     f16x8 sb;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         sb[i] = static_cast<_Float16>(S[2 * kk][i]);
                         sb[4 + i] = static_cast<_Float16>(S[2 * kk + 1][i]);
                     }
-                    const int o0 = tok_major<DK>(row, 32 * kk + 4 * lq);
-                    const int o1 = tok_major<DK>(row, 32 * kk + 16 + 4 * lq);
-                    const f16x4 k0 = *reinterpret_cast<const f16x4*>(sX0 + o0);
-                    const f16x4 k1 = *reinterpret_cast<const f16x4*>(sX0 + o1);
-                    const f16x4 q0 = *reinterpret_cast<const f16x4*>(sX1 + o0);
-                    const f16x4 q1 = *reinterpret_cast<const f16x4*>(sX1 + o1);
-                    f16x8 ka, qa;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) { ka[i] = k0[i]; ka[4 + i] = k1[i]; qa[i] = q0[i]; qa[4 + i] = q1[i]; }
+                    const f16x8 ka = *reinterpret_cast<const f16x8*>(fr + 1024 * kk);
+                    const f16x8 qa = *reinterpret_cast<const f16x8*>(fr + E2 + 1024 * kk);
                     Y = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, sb, Y, 0, 0, 0);
                     O = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, sb, O, 0, 0, 0);
                 }
@@ -496,18 +603,10 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
                     for (int i = 0; i < 4; ++i) { sv[i] = S[2 * kk][i]; sv[4 + i] = S[2 * kk + 1][i]; }
                     bf16x8 sbh, sbl;
                     split8(sv, sbh, sbl);
-                    const int o0 = tok_major<DK>(row, 32 * kk + 4 * lq);
-                    const int o1 = tok_major<DK>(row, 32 * kk + 16 + 4 * lq);
-                    const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(sKh + o0), a1 = *reinterpret_cast<const bf16x4*>(sKh + o1);
-                    const bf16x4 b0 = *reinterpret_cast<const bf16x4*>(sKl + o0), b1 = *reinterpret_cast<const bf16x4*>(sKl + o1);
-                    const bf16x4 c0 = *reinterpret_cast<const bf16x4*>(sQh + o0), c1 = *reinterpret_cast<const bf16x4*>(sQh + o1);
-                    const bf16x4 d0 = *reinterpret_cast<const bf16x4*>(sQl + o0), d1 = *reinterpret_cast<const bf16x4*>(sQl + o1);
-                    bf16x8 kh, kl, qh, ql;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        kh[i] = a0[i]; kh[4 + i] = a1[i]; kl[i] = b0[i]; kl[4 + i] = b1[i];
-                        qh[i] = c0[i]; qh[4 + i] = c1[i]; ql[i] = d0[i]; ql[4 + i] = d1[i];
-                    }
+                    const bf16x8 kh = *reinterpret_cast<const bf16x8*>(fr + 1024 * kk);
+                    const bf16x8 kl = *reinterpret_cast<const bf16x8*>(fr + E2 + 1024 * kk);
+                    const bf16x8 qh = *reinterpret_cast<const bf16x8*>(fr + 2 * E2 + 1024 * kk);
+                    const bf16x8 ql = *reinterpret_cast<const bf16x8*>(fr + 3 * E2 + 1024 * kk);
                     Y = mfma32_bf16_x3(kh, kl, sbh, sbl, Y);
                     O = mfma32_bf16_x3(qh, ql, sbh, sbl, O);
                 }
@@ -515,60 +614,85 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
             // X = V - Y (the beta scaling sits in T'), W = T' X
             f32x4 X;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) X[i] = vslab(b)[(4 * lq + i) * BV + 16 * wave + ln] - Y[i];
+            for (int i = 0; i < 4; ++i) {
+                const float vv = (ESZ == 4) ? __uint_as_float(vc[4 * b + i]) : bf16_val(static_cast<uint16_t>(vc[4 * b + i]));
+                X[i] = vv - Y[i];
+            }
             s16x4 xh, xl;
             split4(X, xh, xl);
-            const s16x4 th = *reinterpret_cast<const s16x4*>(&sTh[b][ln][4 * lq]);
-            const s16x4 tl = *reinterpret_cast<const s16x4*>(&sTl[b][ln][4 * lq]);
-            const f32x4 W = mfma16_bf16_x3(th, tl, xh, xl, zero4());
+            const f32x4 W = mfma16_bf16_x3(*reinterpret_cast<const s16x4*>(Th), *reinterpret_cast<const s16x4*>(Tl),
+                                           xh, xl, zero4());
             // O += P W
             s16x4 wh, wl;
             split4(W, wh, wl);
-            const s16x4 ph = *reinterpret_cast<const s16x4*>(&sPh[b][ln][4 * lq]);
-            const s16x4 pl = *reinterpret_cast<const s16x4*>(&sPl[b][ln][4 * lq]);
-            O = mfma16_bf16_x3(ph, pl, wh, wl, O);
+            O = mfma16_bf16_x3(*reinterpret_cast<const s16x4*>(Ph), *reinterpret_cast<const s16x4*>(Pl), wh, wl, O);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * b + 4 * lq + i;
-                if (full || r < nt) {
-                    const int32_t e = r * vstride + ln;
-                    if constexpr (ODT == KDA_F32) static_cast<float*>(obase)[e] = p.scale * O[i];
-                    else static_cast<uint16_t*>(obase)[e] = bf16_bits(p.scale * O[i]);
-                }
+                const int off = ((16 * b + 4 * lq + i) * vstride + n0 + ln) * OSZ;
+                if constexpr (ODT == KDA_F32)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * O[i]), orr, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(p.scale * O[i]), orr, off, 0, 0);
             }
-            // S <- Diag(e^{G_15}) S + Kb^T W   (contraction over the block's 16 tokens)
-            f16x4 w16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w16[i] = static_cast<_Float16>(W[i]);
+            // S <- Diag(e^{G_15}) S + Kb^T W = S + Diag(e^{G_15} - 1) S + Kb^T W
             float4 gm[CT];
 #pragma unroll
-            for (int i = 0; i < CT; ++i) gm[i] = *reinterpret_cast<const float4*>(&sGam[b][16 * i + 4 * lq]);
+            for (int i = 0; i < CT; ++i) gm[i] = *reinterpret_cast<const float4*>(gam + 16 * i + 4 * lq);
             if constexpr (!PRECISE) {
-                f16x4 ka[CT];
+                const uint8_t* kbt = rb + 2 * E2 + 8 * lane;   // frag16 Kb^T
+                f16x4 w16;
 #pragma unroll
-                for (int i = 0; i < CT; ++i)
-                    ka[i] = *reinterpret_cast<const f16x4*>(sX2 + ch_major(16 * i + ln, 16 * b + 4 * lq));
+                for (int i = 0; i < 4; ++i) w16[i] = static_cast<_Float16>(W[i]);
 #pragma unroll
                 for (int i = 0; i < CT; ++i) {
+                    const f16x4 ka = *reinterpret_cast<const f16x4*>(kbt + 512 * i);
                     f32x4 acc;
-                    acc[0] = S[i][0] * gm[i].x; acc[1] = S[i][1] * gm[i].y;
-                    acc[2] = S[i][2] * gm[i].z; acc[3] = S[i][3] * gm[i].w;
-                    S[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(ka[i], w16, acc, 0, 0, 0);
+                    acc[0] = fmaf(S[i][0], gm[i].x, S[i][0]); acc[1] = fmaf(S[i][1], gm[i].y, S[i][1]);
+                    acc[2] = fmaf(S[i][2], gm[i].z, S[i][2]); acc[3] = fmaf(S[i][3], gm[i].w, S[i][3]);
+                    S[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(ka, w16, acc, 0, 0, 0);
                 }
             } else {
+                const uint8_t* kbh = rb + 4 * E2 + 8 * lane;
+                const uint8_t* kbl = rb + 5 * E2 + 8 * lane;
 #pragma unroll
                 for (int i = 0; i < CT; ++i) {
-                    const int off = ch_major(16 * i + ln, 16 * b + 4 * lq);
-                    const s16x4 kh = *reinterpret_cast<const s16x4*>(sX0 + off);
-                    const s16x4 kl = *reinterpret_cast<const s16x4*>(sX1 + off);
+                    const s16x4 kh = *reinterpret_cast<const s16x4*>(kbh + 512 * i);
+                    const s16x4 kl = *reinterpret_cast<const s16x4*>(kbl + 512 * i);
                     f32x4 acc;
-                    acc[0] = S[i][0] * gm[i].x; acc[1] = S[i][1] * gm[i].y;
-                    acc[2] = S[i][2] * gm[i].z; acc[3] = S[i][3] * gm[i].w;
+                    acc[0] = fmaf(S[i][0], gm[i].x, S[i][0]); acc[1] = fmaf(S[i][1], gm[i].y, S[i][1]);
+                    acc[2] = fmaf(S[i][2], gm[i].z, S[i][2]); acc[3] = fmaf(S[i][3], gm[i].w, S[i][3]);
                     S[i] = mfma16_bf16_x3(kh, kl, wh, wl, acc);
                 }
             }
         }
-        __syncthreads();   // the next chunk's staging rewrites the operand arrays
+    };
+
+    // Each half-iteration starts the next chunk's transfers, runs the current chunk, then waits
+    // for its own transfers -- the o stores of the chunk (4 per block) may stay in flight, the
+    // older loads may not -- and meets the other waves at the barrier.
+    constexpr int WAIT_LOADS = vmcnt_imm(4 * NB);
+    const int64_t nchunks = (len + CHT - 1) / CHT;
+    uint32_t vA[NV], vB[NV];
+    fill(bufA, 0);
+    load_v(vA, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    for (int64_t ci = 0; ci < nchunks; ci += 2) {
+        fill(bufB, ci + 1);
+        load_v(vB, ci + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        run(bufA, ci, vA);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(WAIT_LOADS);
+        __syncthreads();
+        if (ci + 1 >= nchunks) break;
+        fill(bufA, ci + 2);
+        load_v(vA, ci + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        run(bufB, ci + 1, vB);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(WAIT_LOADS);
+        __syncthreads();
     }
 
     if (p.hT) {
@@ -580,16 +704,36 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fwd_kernel(ChunkArgs p, int32_t
     }
 }
 
+// ---- host side --------------------------------------------------------------------------------
+int64_t slot_count(int32_t n_seqs, int64_t total_tokens, bool varlen, int32_t B, int64_t T) {
+    if (!varlen) return static_cast<int64_t>(B) * ((T + BLK - 1) / BLK);
+    return total_tokens / BLK + n_seqs + 1;
+}
+
+size_t record_bytes(int32_t dk, bool precise) {
+    if (dk == 128) return precise ? Rec<128, true>::BYTES : Rec<128, false>::BYTES;
+    return precise ? Rec<64, true>::BYTES : Rec<64, false>::BYTES;
+}
+
 template <int DK, int IDT, int GDT, int ODT>
 hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
-    const int32_t n_vblk = a.dv / BV;
+    constexpr bool PRECISE = (IDT == KDA_F32);
+    const int64_t nslots = slot_count(a.n_seqs, static_cast<int64_t>(a.B) * a.T, a.cu != nullptr, a.B, a.T);
+    uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+    const int64_t intra_wgs = nslots * a.H;
+    if (intra_wgs > 0) {
+        hipLaunchKernelGGL((chunk_intra_kernel<DK, IDT, GDT, PRECISE>), dim3(static_cast<unsigned>(intra_wgs)),
+                           dim3(64), 0, stream, a, nslots, ws);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    constexpr int NW = STATE_WAVES;
+    const int32_t n_vblk = a.dv / (16 * NW);
     const int64_t units = static_cast<int64_t>(a.n_seqs) * a.H;
     const int64_t groups = (units + 7) / 8;
-    const dim3 grid(static_cast<unsigned>(groups * 8 * n_vblk));
-    if (IDT == KDA_F32)
-        hipLaunchKernelGGL((chunk_fwd_kernel<DK, IDT, GDT, ODT, true>), grid, dim3(NTHR), 0, stream, a, n_vblk);
-    else
-        hipLaunchKernelGGL((chunk_fwd_kernel<DK, IDT, GDT, ODT, false>), grid, dim3(NTHR), 0, stream, a, n_vblk);
+    hipLaunchKernelGGL((chunk_state_kernel<DK, IDT, ODT, PRECISE, NW>),
+                       dim3(static_cast<unsigned>(groups * 8 * n_vblk)), dim3(64 * NW), 0, stream, a, n_vblk,
+                       nslots, static_cast<const uint8_t*>(ws));
     return hipGetLastError();
 }
 
@@ -611,7 +755,12 @@ hipError_t dispatch(const ChunkArgs& a, hipStream_t s) {
 
 }  // namespace
 
-size_t chunk_workspace_bytes(int32_t, int64_t, int32_t, int32_t, int32_t) { return 0; }
+// Workspace: one record per (head, 16-token block slot).
+size_t chunk_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
+                             int32_t in_dtype) {
+    const int64_t slots = total_tokens / BLK + n_seqs + 1;   // bound for packed and fixed batches
+    return static_cast<size_t>(slots) * static_cast<size_t>(H) * record_bytes(dk, in_dtype == KDA_F32);
+}
 
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream) {
     if (a.dk == 128) return dispatch<128>(a, stream);

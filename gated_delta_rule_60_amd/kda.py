@@ -46,7 +46,7 @@ def load_library(path: Optional[str] = None):
     lib.kda_version.restype = ctypes.c_int
     lib.kda_gate.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, i64, i32, i32, f32, vp]
     lib.kda_gate.restype = ctypes.c_int
-    lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.c_int]
     lib.kda_chunk_fwd_workspace_size.restype = sz
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp,
                                   ctypes.c_int, i32, i64, i32, i32, i32, i32, i32, f32, vp, sz, vp]
@@ -112,9 +112,9 @@ def kda_gate(A: torch.Tensor, z: torch.Tensor, g: Optional[torch.Tensor] = None,
 
 
 def kda_chunk_fwd_workspace_size(n_seqs: int, total_tokens: int, H: int, dk: int, dv: int,
-                                 chunk: int = 64) -> int:
+                                 chunk: int = 64, in_dtype: torch.dtype = torch.bfloat16) -> int:
     return int(load_library().kda_chunk_fwd_workspace_size(n_seqs, total_tokens, H, dk, dv,
-                                                            chunk))
+                                                            chunk, _DT[in_dtype]))
 
 
 def kda_chunk_fwd(q, k, v, beta, g, initial_state=None, final_state=None, cu_seqlens=None,
@@ -130,7 +130,7 @@ def kda_chunk_fwd(q, k, v, beta, g, initial_state=None, final_state=None, cu_seq
         o = torch.empty((B, T, H, dv), dtype=o_dtype or q.dtype, device=q.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
-    need = kda_chunk_fwd_workspace_size(N, B * T, H, dk, dv)
+    need = kda_chunk_fwd_workspace_size(N, B * T, H, dk, dv, in_dtype=q.dtype)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

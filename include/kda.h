@@ -75,11 +75,15 @@ int kda_gate(const float *A, const void *z, int z_dtype, void *g, int g_dtype, i
              int32_t H, int32_t dk, float g_min, void *stream);
 
 /*
- * Workspace bytes kda_chunk_fwd needs for these sizes (0 when none).  Never fails; returns 0
- * for invalid sizes (kda_chunk_fwd then reports the error).
+ * Workspace bytes kda_chunk_fwd needs for a batch of n_seqs sequences holding total_tokens tokens
+ * (B*T for fixed-length batches) with inputs in in_dtype.  The prefill runs in two kernels: the
+ * first computes, for every (head, 16-token block), everything that does not depend on the state
+ * and writes it to the workspace; the second passes the state along each sequence reading it.
+ * The size is about 14.5 KiB per (head, block) at d_k = 128 for bf16 inputs (26.5 KiB for fp32).
+ * Never fails; returns 0 for invalid sizes (kda_chunk_fwd then reports the error).
  */
 size_t kda_chunk_fwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
-                                    int32_t dv, int32_t chunk);
+                                    int32_t dv, int32_t chunk, int in_dtype);
 
 /*
  * kda_chunk_fwd -- chunked prefill of the recurrence above over whole sequences.
@@ -101,8 +105,10 @@ size_t kda_chunk_fwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_
  *   o             : [B, T, H, d_v] in o_dtype (KDA_F32 or KDA_BF16); must not overlap any input.
  *   T             : >= 0 (T = 0 only copies initial_state to final_state, or zeroes it).
  *   dk, dv        : 64 or 128 each.  chunk: must be 64.  scale: any finite value (1 = none).
- *   workspace     : device buffer of at least kda_chunk_fwd_workspace_size(...) bytes (may be
- *                   NULL when that size is 0).
+ *   workspace     : device buffer of at least kda_chunk_fwd_workspace_size(...) bytes, owned
+ *                   by the caller; its contents on entry do not matter and on return are
+ *                   unspecified.  It must not overlap any other argument.  Calls that share
+ *                   a workspace must not overlap in time.
  * Results match the token-by-token definition up to rounding: the kernels evaluate the chunked
  * form with fp32 accumulation and split-precision matrix products.
  */

@@ -50,12 +50,17 @@ def P(x):
 
 def chunk(lib, q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, beta=FAKE + 0x30000000,
           in_dt=1, g=FAKE + 0x40000000, g_dt=0, h0=0, hT=0, cu=0, o=FAKE + 0x50000000, o_dt=1,
-          B=1, T=128, N=1, H=2, dk=128, dv=128, chunk=64, scale=1.0, ws=0, ws_bytes=0):
+          B=1, T=128, N=1, H=2, dk=128, dv=128, chunk=64, scale=1.0, ws=FAKE + 0x80000000,
+          ws_bytes=1 << 30):
     return lib.kda_chunk_fwd(P(q), P(k), P(v), P(beta), in_dt, P(g), g_dt, P(h0), P(hT), P(cu),
                              P(o), o_dt, B, T, N, H, dk, dv, chunk, scale, P(ws), ws_bytes, None)
 
 
 def test_chunk_fwd_rejects(lib):
+    ws_need = K.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128)
+    assert chunk(lib, ws=FAKE + 0x80000000, ws_bytes=ws_need - 1) == WS   # undersized workspace
+    assert chunk(lib, ws=0, ws_bytes=0) == WS                             # missing workspace
+    assert chunk(lib, ws=FAKE + 0x20000000 + 64) == INV                   # workspace overlaps v
     assert chunk(lib, in_dt=7) == INV
     assert chunk(lib, g_dt=-1) == INV
     assert chunk(lib, o_dt=2) == INV
@@ -76,9 +81,15 @@ def test_chunk_fwd_rejects(lib):
 
 
 def test_workspace_size(lib):
-    assert K.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128) >= 0
+    import torch
+    bf = K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128)
+    f32 = K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128, in_dtype=torch.float32)
+    # one record per (head, 16-token block slot), slots bounded by tokens/16 + sequences + 1
+    assert bf == (4 * 4096 // 16 + 4 + 1) * 16 * 14848
+    assert f32 > bf
     assert K.kda_chunk_fwd_workspace_size(1, 4096, 16, 96, 128) == 0
     assert K.kda_chunk_fwd_workspace_size(0, 4096, 16, 128, 128) == 0
+    assert lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 64, 7) == 0
 
 
 def test_gate_rejects(lib):
