@@ -17,8 +17,10 @@ workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -37,6 +39,11 @@ STATE_BYTES = 128 * 128 * 4
 DECODE_BYTES_PER_UNIT = 2 * STATE_BYTES + 4 * 128 * 2 + 2 + 128 * 2
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "gated_delta_rule_60_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -45,18 +52,91 @@ def parse():
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--mode", choices=("all", "prefill", "decode"), default="all",
+                    help="prefill / decode: run only that workload and print no JSON line "
+                         "(for profiler counter passes)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first copy this many MiB device-to-device (a plain copy kernel of known "
+                         "size, the calibration for HBM byte counters)")
     return ap.parse_args()
+
+
+def source_digest(*names):
+    """sha256 over the kernel sources a counter measurement was taken with."""
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(summary: str, digest: str):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE + WRITE_SIZE scaled by a
+    copy kernel of known size), or None when the summary is missing or was taken with other
+    kernel sources than the ones built now."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"<!-- traffic (\{.*?\}) -->", open(path).read())
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256") != digest:
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def run_decode(args, dev, inputs, K, stream):
+    """The decode workload: 64 in-place steps over 256 sequences x 32 heads, timed with HIP events
+    on the launch stream over args.decode_passes passes."""
+    dcfg = inputs.config("decode")
+    log("generating", dcfg)
+    dd = inputs.make_decode(dcfg)
+    N, steps = dcfg.B, dcfg.decode_steps
+    dq, dk_, dv_, db, dz = (dd[x].to(dev) for x in ("q", "k", "v", "beta", "z"))
+    dA = dd["A"].to(dev)
+    dg = K.kda_gate(dA, dz, g_dtype=torch.bfloat16)     # inputs prepared before timing
+    Sd = dd["S0"].to(dev)
+    od = torch.empty((N, dcfg.H, dcfg.dv), dtype=torch.bfloat16, device=dev)
+
+    def decode_pass():
+        for t in range(steps):
+            K.kda_decode_step(dq[t], dk_[t], dv_[t], db[t], dg[t], Sd, o=od, stream=stream)
+
+    decode_pass()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.decode_passes):
+        decode_pass()
+    e1.record(stream)
+    e1.synchronize()
+    dec_ms_step = e0.elapsed_time(e1) / (args.decode_passes * steps)
+    dec_units = N * dcfg.H
+    dec_gbs = dec_units * DECODE_BYTES_PER_UNIT / (dec_ms_step * 1e-3)
+
+    return {"seq_steps_per_s": round(N / (dec_ms_step * 1e-3), 1),
+            "ms_per_step": round(dec_ms_step, 4),
+            "roofline": {"bound": "hbm", "achieved": round(dec_gbs / 1e9, 1),
+                         "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                         "frac": round(dec_gbs / HBM_PEAK, 4),
+                         "traffic": measured_traffic("decode_kernel_256x32_d128.md",
+                                                     source_digest("kda_decode.hip", "kda_common.hpp")),
+                         "kernel": "decode_kernel",
+                         "bytes_per_launch": dec_units * DECODE_BYTES_PER_UNIT},
+            "config": "256 sequences x 32 heads, d_k=d_v=128, fp32 state in place, "
+                      "bf16 q/k/v/beta/g, 64 steps"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 "
-              "(the path would shard over sequences and heads, see the design notes)",
+              "(sequences and heads are independent: several GPUs would each run their own share)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -66,6 +146,19 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     K.load_library()
+
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if args.mode == "decode":
+        r = run_decode(args, dev, inputs, K, torch.cuda.current_stream())
+        log(f"decode: {r['ms_per_step']:.4f} ms/step")
+        return
 
     # ------------------------------------------------------------------ prefill workload
     cfg = inputs.config("prefill_bf16")
@@ -113,6 +206,9 @@ def main():
         step(True)
     chunk_avg = sum(chunk_ms) / len(chunk_ms)
     gate_avg = sum(gate_ms) / len(gate_ms)
+    if args.mode == "prefill":
+        log(f"prefill: {ms_per_step:.4f} ms/step, kda_chunk_fwd {chunk_avg:.4f} ms")
+        return
 
     tokens = B * T
     th = tokens * H
@@ -121,32 +217,7 @@ def main():
     achieved = chunk_bytes / (chunk_avg * 1e-3)
     value = tokens / (ms_per_step * 1e-3)
 
-    # ------------------------------------------------------------------ decode workload
-    dcfg = inputs.config("decode")
-    log("generating", dcfg)
-    dd = inputs.make_decode(dcfg)
-    N, steps = dcfg.B, dcfg.decode_steps
-    dq, dk_, dv_, db, dz = (dd[x].to(dev) for x in ("q", "k", "v", "beta", "z"))
-    dA = dd["A"].to(dev)
-    dg = K.kda_gate(dA, dz, g_dtype=torch.bfloat16)     # inputs prepared before timing
-    Sd = dd["S0"].to(dev)
-    od = torch.empty((N, dcfg.H, dcfg.dv), dtype=torch.bfloat16, device=dev)
-
-    def decode_pass():
-        for t in range(steps):
-            K.kda_decode_step(dq[t], dk_[t], dv_[t], db[t], dg[t], Sd, o=od, stream=stream)
-
-    decode_pass()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.decode_passes):
-        decode_pass()
-    e1.record(stream)
-    e1.synchronize()
-    dec_ms_step = e0.elapsed_time(e1) / (args.decode_passes * steps)
-    dec_units = N * dcfg.H
-    dec_gbs = dec_units * DECODE_BYTES_PER_UNIT / (dec_ms_step * 1e-3)
+    dec = run_decode(args, dev, inputs, K, stream)
 
     # ------------------------------------------------------------------ CPU baseline (oracle)
     cpu = None
@@ -181,22 +252,17 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK, 4),
+                     "traffic": measured_traffic(
+                         "chunk_fwd_prefill_bf16_B4_H16_T4096.md",
+                         source_digest("kda_chunk.hip", "kda_common.hpp", "kda_internal.hpp")),
                      "kernel": "kda_chunk_fwd = chunk_intra_kernel + chunk_state_kernel",
                      "kernel_ms": round(chunk_avg, 4), "bytes_per_launch": chunk_bytes,
                      "workspace_bytes": ws.numel()},
         "mfma": {"canonical_tflops": round(chunk_flop / (chunk_avg * 1e-3) / 1e12, 2),
                  "frac_bf16_peak": round(chunk_flop / (chunk_avg * 1e-3) / BF16_PEAK, 4)},
         "gate_ms": round(gate_avg, 4),
-        "decode": {"seq_steps_per_s": round(N / (dec_ms_step * 1e-3), 1),
-                   "ms_per_step": round(dec_ms_step, 4),
-                   "roofline": {"bound": "hbm", "achieved": round(dec_gbs / 1e9, 1),
-                                "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                                "frac": round(dec_gbs / HBM_PEAK, 4), "traffic": None,
-                                "kernel": "decode_kernel",
-                                "bytes_per_launch": dec_units * DECODE_BYTES_PER_UNIT},
-                   "config": "256 sequences x 32 heads, d_k=d_v=128, fp32 state in place, "
-                             "bf16 q/k/v/beta/g, 64 steps"},
+        "decode": dec,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
