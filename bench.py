@@ -1,16 +1,19 @@
 """Benchmark of the KDA forward pass on one MI355X.
 
 One step = one pass of the prefill hot path over the bf16 prefill workload (B=4, H=16, T=4096,
-d_k=d_v=128, chunk 64, random fp32 initial state): kda_gate (z -> fp32 g) then kda_chunk_fwd
-(o in bf16, final state in fp32).  Inputs are synthetic (seeded generators, the workload's shapes
+d_k=d_v=128, chunk 64, random fp32 initial state): kda_chunk_fwd_gated, i.e. the forget gate,
+the intra-block work and the state pass, from A and z (bf16) to o (bf16) and the final state
+(fp32).  The same step through the separate kda_gate + kda_chunk_fwd entry points is timed too
+and reported under "unfused".  Inputs are synthetic (seeded generators, the workload's shapes
 and distributions) and resident in HBM before the timed region starts.  The decode workload
 (256 sequences x 32 heads, 64 in-place steps) is timed in the same run and reported under
 "decode".
 
 Prints ONE JSON line.  ``value`` is prefill tokens/s (B*T tokens per step / step time).
-``roofline`` describes the dominant operation, kda_chunk_fwd (its two kernels: the intra-block
-kernel and the state-passing kernel, launched back to back on one stream), with its algorithmic
-bytes per call divided by its mean call time, measured with HIP events on the launch stream.
+``roofline`` describes the step's one operation, kda_chunk_fwd_gated (its two kernels: the
+intra-block kernel with the gate fused, and the state-passing kernel, launched back to back on
+one stream), with its algorithmic bytes per call divided by its mean call time, measured with
+HIP events on the launch stream.
 ``cpu_baseline`` is the fp64 oracle (test infrastructure) timed on this host's cores on the same
 workload.
 """
@@ -30,8 +33,10 @@ HBM_PEAK = 8.0e12           # B/s, MI355X HBM3E
 BF16_PEAK = 2516.6e12       # FLOP/s dense
 # Algorithmic work per (token, head) at d_k = d_v = 128, chunk 64 (what the method must move and
 # compute, not what the kernels execute):
-#   bytes: q, k, v bf16 (3*256) + g fp32 (512) + beta bf16 (2) + o bf16 (256) = 1538
+#   bytes, gate fused: q, k, v, z bf16 (4*256) + beta bf16 (2) + o bf16 (256) = 1282
+#   bytes, g given   : q, k, v bf16 (3*256) + g fp32 (512) + beta bf16 (2) + o bf16 (256) = 1538
 #   FLOP : 6 dk dv + C (3 dk + 2 dv) + C^2 / 3 = 140,629
+FUSED_BYTES_PER_TH = 1282
 PREFILL_BYTES_PER_TH = 1538
 PREFILL_FLOP_PER_TH = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128) + 64 * 64 / 3
 STATE_BYTES = 128 * 128 * 4
@@ -174,47 +179,60 @@ def main():
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    gate_ms, chunk_ms = [], []
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
 
-    def step(timed):
-        if timed:
-            ev[0].record(stream)
+    def fused_step():
+        K.kda_chunk_fwd_gated(q, k, v, beta, A, z, initial_state=S0, final_state=hT, o=o,
+                              workspace=ws, stream=stream)
+
+    def unfused_step():
         K.kda_gate(A, z, g=g, stream=stream)
-        if timed:
-            ev[1].record(stream)
         K.kda_chunk_fwd(q, k, v, beta, g, initial_state=S0, final_state=hT, o=o, workspace=ws,
                         stream=stream)
-        if timed:
-            ev[2].record(stream)
-            ev[2].synchronize()
-            gate_ms.append(ev[0].elapsed_time(ev[1]))
-            chunk_ms.append(ev[1].elapsed_time(ev[2]))
 
     for _ in range(args.warmup):
-        step(False)
+        fused_step()
+        unfused_step()
     torch.cuda.synchronize()
-    # wall-clock over exactly K steps
+    # wall clock over exactly K steps
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(False)
+        fused_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    # per-kernel durations with HIP events on the launch stream (separate pass, same work)
+    # per-call durations with HIP events on the launch stream (separate passes, same work)
+    fused_ms, gate_ms, chunk_ms = [], [], []
     for _ in range(args.steps):
-        step(True)
+        e = [ev() for _ in range(4)]
+        e[0].record(stream)
+        fused_step()
+        e[1].record(stream)
+        K.kda_gate(A, z, g=g, stream=stream)
+        e[2].record(stream)
+        K.kda_chunk_fwd(q, k, v, beta, g, initial_state=S0, final_state=hT, o=o, workspace=ws,
+                        stream=stream)
+        e[3].record(stream)
+        e[3].synchronize()
+        fused_ms.append(e[0].elapsed_time(e[1]))
+        gate_ms.append(e[1].elapsed_time(e[2]))
+        chunk_ms.append(e[2].elapsed_time(e[3]))
+    fused_avg = sum(fused_ms) / len(fused_ms)
     chunk_avg = sum(chunk_ms) / len(chunk_ms)
     gate_avg = sum(gate_ms) / len(gate_ms)
     if args.mode == "prefill":
-        log(f"prefill: {ms_per_step:.4f} ms/step, kda_chunk_fwd {chunk_avg:.4f} ms")
+        log(f"prefill: {ms_per_step:.4f} ms/step, kda_chunk_fwd_gated {fused_avg:.4f} ms, "
+            f"kda_gate {gate_avg:.4f} ms + kda_chunk_fwd {chunk_avg:.4f} ms")
         return
 
     tokens = B * T
     th = tokens * H
-    chunk_bytes = th * PREFILL_BYTES_PER_TH + 2 * B * H * STATE_BYTES
+    state_io = 2 * B * H * STATE_BYTES
+    fused_bytes = th * FUSED_BYTES_PER_TH + H * dk * 4 + state_io
+    chunk_bytes = th * PREFILL_BYTES_PER_TH + state_io
     chunk_flop = th * PREFILL_FLOP_PER_TH
-    achieved = chunk_bytes / (chunk_avg * 1e-3)
+    achieved = fused_bytes / (fused_avg * 1e-3)
     value = tokens / (ms_per_step * 1e-3)
 
     dec = run_decode(args, dev, inputs, K, stream)
@@ -247,21 +265,25 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "KDA chunked prefill, bf16 inputs / fp32 state, B=4 H=16 T=4096 "
-                               "d_k=d_v=128 chunk=64, gate included",
+                               "d_k=d_v=128 chunk=64, gate fused (A, z in)",
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": dk,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4),
                      "traffic": measured_traffic(
-                         "chunk_fwd_prefill_bf16_B4_H16_T4096.md",
+                         "chunk_fwd_gated_prefill_bf16_B4_H16_T4096.md",
                          source_digest("kda_chunk.hip", "kda_common.hpp", "kda_internal.hpp")),
-                     "kernel": "kda_chunk_fwd = chunk_intra_kernel + chunk_state_kernel",
-                     "kernel_ms": round(chunk_avg, 4), "bytes_per_launch": chunk_bytes,
+                     "kernel": "kda_chunk_fwd_gated = chunk_intra_kernel (gate fused) + "
+                               "chunk_state_kernel",
+                     "kernel_ms": round(fused_avg, 4), "bytes_per_launch": fused_bytes,
                      "workspace_bytes": ws.numel()},
-        "mfma": {"canonical_tflops": round(chunk_flop / (chunk_avg * 1e-3) / 1e12, 2),
-                 "frac_bf16_peak": round(chunk_flop / (chunk_avg * 1e-3) / BF16_PEAK, 4)},
-        "gate_ms": round(gate_avg, 4),
+        "mfma": {"canonical_tflops": round(chunk_flop / (fused_avg * 1e-3) / 1e12, 2),
+                 "frac_bf16_peak": round(chunk_flop / (fused_avg * 1e-3) / BF16_PEAK, 4)},
+        "unfused": {"kda_gate_ms": round(gate_avg, 4), "kda_chunk_fwd_ms": round(chunk_avg, 4),
+                    "kda_chunk_fwd_bytes": chunk_bytes,
+                    "kda_chunk_fwd_frac_hbm": round(chunk_bytes / (chunk_avg * 1e-3) / HBM_PEAK, 4),
+                    "tokens_per_s": round(tokens / ((gate_avg + chunk_avg) * 1e-3), 1)},
         "decode": dec,
         "cpu_baseline": cpu,
     }

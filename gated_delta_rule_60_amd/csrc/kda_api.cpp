@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 bool valid_dtype(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
 int64_t esize(int dt) { return dt == KDA_F32 ? 4 : 2; }
@@ -70,19 +70,29 @@ size_t kda_chunk_fwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_
     return kda::chunk_workspace_bytes(n_seqs, total_tokens, H, dk, in_dtype);
 }
 
-int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, int in_dtype,
-                  const void* g, int g_dtype, const float* initial_state, float* final_state,
-                  const int32_t* cu_seqlens, void* o, int o_dtype, int32_t B, int64_t T,
-                  int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, int32_t chunk, float scale,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and dispatch shared by kda_chunk_fwd (g given) and kda_chunk_fwd_gated (A, z given:
+// gate_A != nullptr, g = z, g_dtype = z's dtype).
+int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* beta, int in_dtype,
+                   const void* g, int g_dtype, const float* gate_A, float g_min,
+                   const float* initial_state, float* final_state, const int32_t* cu_seqlens,
+                   void* o, int o_dtype, int32_t B, int64_t T, int32_t n_seqs, int32_t H,
+                   int32_t dk, int32_t dv, int32_t chunk, float scale, void* workspace,
+                   size_t workspace_bytes, void* stream, bool gated) {
     if (!valid_dtype(in_dtype) || !valid_dtype(g_dtype) || !valid_dtype(o_dtype))
         return KDA_ERR_INVALID_ARGUMENT;
     if (B < 1 || T < 0 || n_seqs < 1 || H < 1 || dk < 1 || dv < 1 || !std::isfinite(scale))
         return KDA_ERR_INVALID_ARGUMENT;
     if (cu_seqlens ? (B != 1) : (n_seqs != B)) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_d(dk) || !supported_d(dv) || chunk != 64) return KDA_ERR_UNSUPPORTED;
+    if (gated && (!std::isfinite(g_min) || !(g_min >= -5.0f && g_min < 0.0f)))
+        return KDA_ERR_UNSUPPORTED;
     const int64_t ntok = int64_t(B) * T;
-    if (ntok > 0 && (!q || !k || !v || !beta || !g || !o)) return KDA_ERR_INVALID_ARGUMENT;
+    if (ntok > 0 && (!q || !k || !v || !beta || !g || !o || (gated && !gate_A)))
+        return KDA_ERR_INVALID_ARGUMENT;
     const size_t need = kda::chunk_workspace_bytes(n_seqs, ntok, H, dk, in_dtype);
     if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE;
 
@@ -92,28 +102,55 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
     const Range r_v = range(v, ntok * H * dv * esize(in_dtype));
     const Range r_b = range(beta, ntok * H * esize(in_dtype));
     const Range r_g = range(g, ntok * H * dk * esize(g_dtype));
+    const Range r_a = range(gate_A, gated && ntok > 0 ? int64_t(H) * dk * 4 : 0);
     const Range r_o = range(o, ntok * H * dv * esize(o_dtype));
     const Range r_h0 = range(initial_state, initial_state ? state_bytes : 0);
     const Range r_hT = range(final_state, final_state ? state_bytes : 0);
     const Range r_cu = range(cu_seqlens, cu_seqlens ? int64_t(n_seqs + 1) * 4 : 0);
     const Range r_ws = range(workspace, int64_t(workspace_bytes));
-    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_h0, r_hT, r_cu, r_ws})
+    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_a, r_h0, r_hT, r_cu, r_ws})
         if (overlap(r_o, x)) return KDA_ERR_INVALID_ARGUMENT;
     // the final state may be the initial state itself, but must not partly overlap it
     if (initial_state && final_state && initial_state != final_state && overlap(r_h0, r_hT))
         return KDA_ERR_INVALID_ARGUMENT;
-    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_cu, r_ws})
+    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_a, r_cu, r_ws})
         if (overlap(r_hT, x)) return KDA_ERR_INVALID_ARGUMENT;
-    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_h0, r_cu})
+    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_a, r_h0, r_cu})
         if (overlap(r_ws, x)) return KDA_ERR_INVALID_ARGUMENT;
 
     kda::ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
+    a.gate_A = gated ? gate_A : nullptr; a.g_min = g_min;
     a.h0 = initial_state; a.hT = final_state; a.cu = cu_seqlens; a.o = o;
     a.in_dtype = in_dtype; a.g_dtype = g_dtype; a.o_dtype = o_dtype;
     a.B = B; a.T = T; a.n_seqs = n_seqs; a.H = H; a.dk = dk; a.dv = dv;
     a.scale = scale; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     return from_hip(kda::launch_chunk(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, int in_dtype,
+                  const void* g, int g_dtype, const float* initial_state, float* final_state,
+                  const int32_t* cu_seqlens, void* o, int o_dtype, int32_t B, int64_t T,
+                  int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, int32_t chunk, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    return chunk_fwd_impl(q, k, v, beta, in_dtype, g, g_dtype, nullptr, 0.0f, initial_state,
+                          final_state, cu_seqlens, o, o_dtype, B, T, n_seqs, H, dk, dv, chunk,
+                          scale, workspace, workspace_bytes, stream, false);
+}
+
+int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* beta,
+                        int in_dtype, const float* A, const void* z, int z_dtype, float g_min,
+                        const float* initial_state, float* final_state, const int32_t* cu_seqlens,
+                        void* o, int o_dtype, int32_t B, int64_t T, int32_t n_seqs, int32_t H,
+                        int32_t dk, int32_t dv, int32_t chunk, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    return chunk_fwd_impl(q, k, v, beta, in_dtype, z, z_dtype, A, g_min, initial_state,
+                          final_state, cu_seqlens, o, o_dtype, B, T, n_seqs, H, dk, dv, chunk,
+                          scale, workspace, workspace_bytes, stream, true);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const void* beta, int in_dtype,

@@ -51,7 +51,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BLK = 16;     // tokens per block (one state step)
-constexpr int CH = 64;      // tokens per chunk streamed by the state kernel (four blocks)
 constexpr int STATE_WAVES = 2;   // waves per state-kernel workgroup (16 state columns each)
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -240,7 +239,7 @@ __device__ __forceinline__ bool locate_slot(const ChunkArgs& p, int64_t slot, in
 // ============================================================================================
 // 1. intra-block kernel: one wave per (block slot, head)
 // ============================================================================================
-template <int DK, int IDT, int GDT, bool PRECISE>
+template <int DK, int IDT, int GDT, bool PRECISE, bool GATE>
 __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     using R = Rec<DK, PRECISE>;
     constexpr int CPT = DK / 16;          // channels per lane (8 or 4)
@@ -269,7 +268,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
     uint8_t* rec = ws + (static_cast<int64_t>(h) * nslots + slot) * R::BYTES;
 
     // ---- inputs: rows 4sub..4sub+3, channels CPT*cg.. ; beta in lanes 0..15
-    Raw<GDT, NEL> pg;
+    Raw<GDT, NEL> pg;                     // g, or z when the gate is fused
     Raw<IDT, NEL> pk, pq;
     {
         const int64_t row0 = (bos + t0) * H + h;
@@ -292,6 +291,19 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
         }
     }
 
+    // ---- fused gate: g = g_min * sigmoid(exp(A) z) from z, the same arithmetic as kda_gate;
+    // rows past the block's tokens get g = 0 like the zero-filled g of the unfused path
+    float ea[CPT];
+    if constexpr (GATE) {
+        const float* a = p.gate_A + static_cast<int64_t>(h) * DK + CPT * cg;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) ea[c] = expf(a[c]);
+    }
+    auto gval = [&](int i, int c) -> float {
+        if constexpr (GATE) return (4 * sub + i < nt) ? gate_log_decay(ea[c], pg.get(i * CPT + c), p.g_min) : 0.f;
+        else return pg.get(i * CPT + c);
+    };
+
     // ---- block cumsum (log2 units): own 4 tokens, then a scan over the 4 lanes of the group
     float G2[NEL];
     float G15[CPT];
@@ -300,7 +312,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
         float run = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            run += pg.get(i * CPT + c) * LOG2E;
+            run += gval(i, c) * LOG2E;
             G2[i * CPT + c] = run;
         }
         float incl = run;
@@ -722,8 +734,12 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
     const int64_t intra_wgs = nslots * a.H;
     if (intra_wgs > 0) {
-        hipLaunchKernelGGL((chunk_intra_kernel<DK, IDT, GDT, PRECISE>), dim3(static_cast<unsigned>(intra_wgs)),
-                           dim3(64), 0, stream, a, nslots, ws);
+        if (a.gate_A)
+            hipLaunchKernelGGL((chunk_intra_kernel<DK, IDT, GDT, PRECISE, true>),
+                               dim3(static_cast<unsigned>(intra_wgs)), dim3(64), 0, stream, a, nslots, ws);
+        else
+            hipLaunchKernelGGL((chunk_intra_kernel<DK, IDT, GDT, PRECISE, false>),
+                               dim3(static_cast<unsigned>(intra_wgs)), dim3(64), 0, stream, a, nslots, ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

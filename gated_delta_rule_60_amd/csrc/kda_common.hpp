@@ -8,6 +8,16 @@
 
 namespace kda {
 
+// ---------------------------------------------------------------- forget gate
+// g = g_min * sigmoid(exp(A) * z) for one element, given exp(A).  The separate gate kernel and
+// the chunk kernel's fused gate both call this, with contraction off, so the two paths produce
+// the same bits of g.
+__device__ __forceinline__ float gate_log_decay(float a_exp, float z, float g_min) {
+#pragma clang fp contract(off)
+    const float x = a_exp * z;
+    return g_min / (1.0f + expf(-x));
+}
+
 // ---------------------------------------------------------------- bf16 <-> fp32 (bit level)
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -20,12 +20,14 @@ struct ChunkArgs {
     const void* k;
     const void* v;
     const void* beta;
-    const void* g;
+    const void* g;         // log-decay g, or z when the gate is fused (gate_A != nullptr)
+    const float* gate_A;   // fused gate: A [H, dk] fp32; nullptr when g is given
+    float g_min;           // fused gate: g = g_min * sigmoid(exp(A) * z)
     const float* h0;       // initial state or nullptr
     float* hT;             // final state or nullptr
     const int32_t* cu;     // device cu_seqlens or nullptr
     void* o;
-    int in_dtype, g_dtype, o_dtype;
+    int in_dtype, g_dtype, o_dtype;   // g_dtype is z's dtype when the gate is fused
     int32_t B;
     int64_t T;
     int32_t n_seqs, H, dk, dv;

@@ -51,6 +51,10 @@ def load_library(path: Optional[str] = None):
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp,
                                   ctypes.c_int, i32, i64, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, f32,
+                                        vp, vp, vp, vp, ctypes.c_int, i32, i64, i32, i32, i32,
+                                        i32, i32, f32, vp, sz, vp]
+    lib.kda_chunk_fwd_gated.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
                                     ctypes.c_int, i32, i32, i32, i32, f32, vp]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -60,7 +64,7 @@ def load_library(path: Optional[str] = None):
 
 
 EXPORTED = ["kda_status_string", "kda_version", "kda_gate", "kda_chunk_fwd_workspace_size",
-            "kda_chunk_fwd", "kda_decode_step"]
+            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_decode_step"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -125,6 +129,18 @@ def kda_chunk_fwd(q, k, v, beta, g, initial_state=None, final_state=None, cu_seq
     Returns (o, final_state); final_state is allocated when output_final_state and not given."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    N, o, final_state, workspace, ws_bytes = _chunk_outputs(
+        q, v, cu_seqlens, o, o_dtype, final_state, output_final_state, workspace)
+    _check("kda_chunk_fwd", load_library().kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(g), _dt(g), _ptr(initial_state),
+        _ptr(final_state), _ptr(cu_seqlens), _ptr(o), _dt(o), B, T, N, H, dk, dv, 64,
+        float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
+    return o, final_state
+
+
+def _chunk_outputs(q, v, cu_seqlens, o, o_dtype, final_state, output_final_state, workspace):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=o_dtype or q.dtype, device=q.device)
@@ -134,10 +150,23 @@ def kda_chunk_fwd(q, k, v, beta, g, initial_state=None, final_state=None, cu_seq
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("kda_chunk_fwd", load_library().kda_chunk_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(g), _dt(g), _ptr(initial_state),
-        _ptr(final_state), _ptr(cu_seqlens), _ptr(o), _dt(o), B, T, N, H, dk, dv, 64,
-        float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
+    return N, o, final_state, workspace, ws_bytes
+
+
+def kda_chunk_fwd_gated(q, k, v, beta, A, z, g_min: float = -5.0, initial_state=None,
+                        final_state=None, cu_seqlens=None, o=None, o_dtype=None,
+                        scale: float = 1.0, output_final_state: bool = True, workspace=None,
+                        stream=None):
+    """Chunked prefill with the gate fused: A [H, dk] fp32 and z [B, T, H, dk] replace g.
+    Same outputs as kda_gate followed by kda_chunk_fwd (fp32 g)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N, o, final_state, workspace, ws_bytes = _chunk_outputs(
+        q, v, cu_seqlens, o, o_dtype, final_state, output_final_state, workspace)
+    _check("kda_chunk_fwd_gated", load_library().kda_chunk_fwd_gated(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(A), _ptr(z), _dt(z), float(g_min),
+        _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(o), _dt(o), B, T, N, H,
+        dk, dv, 64, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
     return o, final_state
 
 

@@ -119,6 +119,22 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_fwd_gated -- kda_chunk_fwd with the forget gate fused in: takes the gate's inputs
+ * A [H, d_k] fp32 and z [B, T, H, d_k] (z_dtype KDA_F32 or KDA_BF16) instead of g, and computes
+ * g = g_min * sigmoid(exp(A) * z) on the fly ([habr, § Последовательность]) with the same
+ * arithmetic as kda_gate, so that g never travels through memory.  The results equal
+ * kda_gate followed by kda_chunk_fwd on an fp32 g bit for bit.  g_min must lie in [-5, 0)
+ * (KDA_ERR_UNSUPPORTED otherwise); A and z must not overlap o, final_state or the workspace.
+ * Every other argument, the workspace size and the error behaviour are those of kda_chunk_fwd.
+ */
+int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const void *beta,
+                        int in_dtype, const float *A, const void *z, int z_dtype, float g_min,
+                        const float *initial_state, float *final_state, const int32_t *cu_seqlens,
+                        void *o, int o_dtype, int32_t B, int64_t T, int32_t n_seqs, int32_t H,
+                        int32_t dk, int32_t dv, int32_t chunk, float scale, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
  * kda_decode_step -- one token of the recurrence for N independent sequences, updating each
  * state in place.  One pass reads S once and writes it once: reading the large recurrent
  * state is this step's cost ([habr, § Как обслуживать два разных кеша]).

@@ -41,7 +41,7 @@ def test_status_strings(lib):
     assert K.kda_status_string(3) == "KDA_ERR_WORKSPACE"
     assert K.kda_status_string(4) == "KDA_ERR_HIP"
     assert K.kda_status_string(99) == "KDA_UNKNOWN_STATUS"
-    assert K.kda_version() >= 100
+    assert K.kda_version() >= 200
 
 
 def P(x):
@@ -78,6 +78,28 @@ def test_chunk_fwd_rejects(lib):
     assert chunk(lib, o=FAKE + 0x100) == INV            # o overlaps q
     assert chunk(lib, h0=FAKE + 0x70000000, hT=FAKE + 0x70000000 + 4096) == INV  # partial overlap
     assert chunk(lib, hT=FAKE + 0x10000010) == INV      # final state overlaps k
+
+
+def gated(lib, q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, beta=FAKE + 0x30000000,
+          in_dt=1, A=FAKE + 0x48000000, z=FAKE + 0x40000000, z_dt=1, gmin=-5.0, h0=0, hT=0, cu=0,
+          o=FAKE + 0x50000000, o_dt=1, B=1, T=128, N=1, H=2, dk=128, dv=128, chunk=64, scale=1.0,
+          ws=FAKE + 0x80000000, ws_bytes=1 << 30):
+    return lib.kda_chunk_fwd_gated(P(q), P(k), P(v), P(beta), in_dt, P(A), P(z), z_dt, gmin,
+                                   P(h0), P(hT), P(cu), P(o), o_dt, B, T, N, H, dk, dv, chunk,
+                                   scale, P(ws), ws_bytes, None)
+
+
+def test_chunk_fwd_gated_rejects(lib):
+    assert gated(lib, gmin=-6.0) == UNS                 # outside [-5, 0)
+    assert gated(lib, gmin=0.0) == UNS
+    assert gated(lib, gmin=float("nan")) == UNS
+    assert gated(lib, A=0) == INV                       # A required
+    assert gated(lib, z=0) == INV                       # z required
+    assert gated(lib, z_dt=4) == INV
+    assert gated(lib, o=FAKE + 0x48000000 + 64) == INV  # o overlaps A
+    assert gated(lib, ws=FAKE + 0x40000000 + 64) == INV  # workspace overlaps z
+    assert gated(lib, dk=96) == UNS
+    assert gated(lib, ws_bytes=16) == WS
 
 
 def test_workspace_size(lib):

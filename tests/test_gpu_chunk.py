@@ -206,3 +206,49 @@ def test_end_to_end_gate_then_chunk():
     g64 = oracle.gate(d["A"], d["z"])
     o_ref, S_ref, _ = oracle.forward(d["q"], d["k"], d["v"], d["beta"], g64, S0=d["S0"])
     assert rel_err(o, o_ref) <= TOL["bf16"] and rel_err(hT, S_ref) <= TOL["bf16"]
+
+
+def _gated(d, o_dtype=torch.float32):
+    cu = d["cu_seqlens"].to(DEV) if d["cu_seqlens"] is not None else None
+    h0 = d["S0"].to(DEV) if d["S0"] is not None else None
+    o, hT = K.kda_chunk_fwd_gated(*(d[x].to(DEV) for x in ("q", "k", "v", "beta", "A", "z")),
+                                  initial_state=h0, cu_seqlens=cu, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    return o, hT
+
+
+@pytest.mark.parametrize("case", ["fixed", "varlen", "f32"])
+def test_fused_gate_equals_gate_then_chunk(case):
+    """kda_chunk_fwd_gated = kda_gate (fp32 g) then kda_chunk_fwd, bit for bit (same gate
+    arithmetic, including the g = 0 padding of partial blocks)."""
+    if case == "fixed":
+        d = prefill_case("prefill_bf16", B=2, H=4, T=300)
+    elif case == "varlen":
+        d = prefill_case("prefill_varlen", seqlens=[0, 5, 64, 1, 200, 17], H=3)
+    else:
+        d = prefill_case("prefill_f32_small")
+    say("fused gate vs gate + chunk", case)
+    o1, h1 = _gated(d)
+    g = K.kda_gate(d["A"].to(DEV), d["z"].to(DEV))
+    o2, h2 = run_gpu(d, g)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_fused_gate_parity_full_size():
+    """The bf16 prefill workload through the fused entry point against the fp64 oracle."""
+    d = prefill_case("prefill_bf16")
+    say("fused gate parity full size", d["cfg"])
+    o, hT = _gated(d)
+    o_ref, S_ref, _ = oracle.forward(d["q"], d["k"], d["v"], d["beta"], oracle.gate(d["A"], d["z"]),
+                                     S0=d["S0"])
+    eo, es = rel_err(o, o_ref), rel_err(hT, S_ref)
+    say(f"  o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_fused_gate_f32_config():
+    d = prefill_case("prefill_f32_small")
+    o, hT = _gated(d)
+    o_ref, S_ref, _ = oracle.forward(d["q"], d["k"], d["v"], d["beta"], oracle.gate(d["A"], d["z"]),
+                                     S0=d["S0"])
+    assert rel_err(o, o_ref) <= TOL["f32"] and rel_err(hT, S_ref) <= TOL["f32"]
