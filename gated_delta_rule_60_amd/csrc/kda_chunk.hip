@@ -34,6 +34,8 @@
 // Precision: operands that are range-bounded use fp16 (11-bit significand) in one pass; the
 // diagonal products (factors up to e^80), T' X and P W use split bf16 (hi*hi + hi*lo + lo*hi).
 // For fp32 inputs every product is split bf16.
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -148,7 +150,8 @@ __device__ __forceinline__ int fragT(int r, int s) { return (r + 16 * (s >> 2)) 
 // Record of one (head, block) in the workspace (byte offsets).  E = 16 * DK elements per array.
 //   fast   : [Kt fp16 frag32][Qt fp16 frag32][Kb^T fp16 frag16]
 //   precise: [Kt hi][Kt lo][Qt hi][Qt lo] (bf16 frag32) [Kb^T hi][Kb^T lo] (bf16 frag16)
-//   then T' hi, T' lo, P hi, P lo (bf16 fragT), then e^{G_15} - 1 (DK fp32).
+//   then T' (fast: fp16; precise: bf16 hi, lo), P hi, P lo (bf16; all fragT),
+//   then e^{G_15} - 1 (DK fp32).  Qt and P carry the output scale.
 // An all-zero record is the identity step (W = 0, S unchanged), which lets the state pass run
 // every chunk as four blocks without branches: blocks past a sequence's end read zeros.
 template <int DK, bool PRECISE>
@@ -156,7 +159,8 @@ struct Rec {
     static constexpr int E = BLK * DK;
     static constexpr int NA = PRECISE ? 6 : 3;
     static constexpr int OFF_T = NA * E * 2;
-    static constexpr int OFF_G = OFF_T + 4 * 256 * 2;
+    static constexpr int OFF_P = OFF_T + (PRECISE ? 1024 : 512);
+    static constexpr int OFF_G = OFF_P + 1024;
     static constexpr int BYTES = OFF_G + DK * 4;
     static_assert(BYTES % 16 == 0, "record alignment");
 };
@@ -340,7 +344,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
             const float e2 = fexp2(G15[c] - g2);          // e^{G15 - G}  <= 1
             const float kv = pk.get(i * CPT + c);
             kt[c] = kv * e1;
-            qt[c] = pq.get(i * CPT + c) * e1;
+            qt[c] = pq.get(i * CPT + c) * (e1 * p.scale);   // the output scale rides on Qt and P
             kb[i * CPT + c] = kv * e2;
             kd[c] = kv * (e2 * fexp2(-G15[c]));           // e^{-G} <= e^80
         }
@@ -412,8 +416,8 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
             accP = mfma32_bf16_x3(qh, ql, dh, dl, accP);
         }
         // lane (ln, lq) holds rows 4lq + i of column ln
-        uint16_t* Ph = reinterpret_cast<uint16_t*>(rec + R::OFF_T + 1024);
-        uint16_t* Pl = reinterpret_cast<uint16_t*>(rec + R::OFF_T + 1536);
+        uint16_t* Ph = reinterpret_cast<uint16_t*>(rec + R::OFF_P);
+        uint16_t* Pl = reinterpret_cast<uint16_t*>(rec + R::OFF_P + 512);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * lq + i, s = ln;
@@ -455,13 +459,16 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
         }
         const float bj = sBeta[jc];
         uint16_t* Th = reinterpret_cast<uint16_t*>(rec + R::OFF_T);
-        uint16_t* Tl = reinterpret_cast<uint16_t*>(rec + R::OFF_T + 512);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float x = t[r] * bj;
-            const uint16_t th = bf16_bits(x);
-            Th[fragT(r, jc)] = th;
-            Tl[fragT(r, jc)] = bf16_bits(x - bf16_val(th));
+            if constexpr (!PRECISE) {
+                Th[fragT(r, jc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+            } else {
+                const uint16_t th = bf16_bits(x);
+                Th[fragT(r, jc)] = th;
+                Th[256 + fragT(r, jc)] = bf16_bits(x - bf16_val(th));
+            }
         }
     }
 }
@@ -581,15 +588,31 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
         const __amdgpu_buffer_rsrc_t orr =
             make_rsrc(static_cast<char*>(p.o) + ((bos + c * CHT) * H + h) * DV * OSZ,
                       static_cast<uint32_t>(nt * vstride * OSZ));
+        // The Kt / Qt fragments of block b + 1 are read from LDS while block b computes (they
+        // are needed first thing in a block); the rest of a block's operands are read at its
+        // start and consumed later in it.
+        using FragA = typename std::conditional<PRECISE, bf16x8, f16x8>::type;
+        constexpr int NFA = PRECISE ? 4 : 2;            // frag32 arrays: Kt (hi, lo), Qt (hi, lo)
+        FragA fa[NFA][KS], fn[NFA][KS];
+        auto load_fa = [&](const uint8_t* rb, FragA (&f)[NFA][KS]) {
+#pragma unroll
+            for (int a = 0; a < NFA; ++a)
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk)
+                    f[a][kk] = *reinterpret_cast<const FragA*>(rb + a * E2 + 1024 * kk + 16 * lane);
+        };
+        load_fa(buf, fa);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const uint8_t* rb = buf + b * R::BYTES;
-            const uint8_t* fr = rb + 16 * lane;         // this lane's frag32 entries
-            const uint16_t* Th = reinterpret_cast<const uint16_t*>(rb + R::OFF_T) + 4 * lane;
-            const uint16_t* Tl = Th + 256;
-            const uint16_t* Ph = Th + 512;
-            const uint16_t* Pl = Th + 768;
+            if (b + 1 < NB) load_fa(rb + R::BYTES, fn);
+            const uint16_t* Tp = reinterpret_cast<const uint16_t*>(rb + R::OFF_T) + 4 * lane;
+            const s16x4 ph = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 8 * lane);
+            const s16x4 pl = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 512 + 8 * lane);
             const float* gam = reinterpret_cast<const float*>(rb + R::OFF_G);   // e^{G_15} - 1
+            float4 gm[CT];
+#pragma unroll
+            for (int i = 0; i < CT; ++i) gm[i] = *reinterpret_cast<const float4*>(gam + 16 * i + 4 * lq);
 
             // Y = Kt S and O = Qt S (contraction over d_k; S packed as the B operand)
             f32x4 Y = zero4(), O = zero4();
@@ -602,10 +625,8 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                         sb[i] = static_cast<_Float16>(S[2 * kk][i]);
                         sb[4 + i] = static_cast<_Float16>(S[2 * kk + 1][i]);
                     }
-                    const f16x8 ka = *reinterpret_cast<const f16x8*>(fr + 1024 * kk);
-                    const f16x8 qa = *reinterpret_cast<const f16x8*>(fr + E2 + 1024 * kk);
-                    Y = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, sb, Y, 0, 0, 0);
-                    O = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, sb, O, 0, 0, 0);
+                    Y = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[0][kk], sb, Y, 0, 0, 0);
+                    O = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[1][kk], sb, O, 0, 0, 0);
                 }
             } else {
 #pragma unroll
@@ -615,12 +636,8 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                     for (int i = 0; i < 4; ++i) { sv[i] = S[2 * kk][i]; sv[4 + i] = S[2 * kk + 1][i]; }
                     bf16x8 sbh, sbl;
                     split8(sv, sbh, sbl);
-                    const bf16x8 kh = *reinterpret_cast<const bf16x8*>(fr + 1024 * kk);
-                    const bf16x8 kl = *reinterpret_cast<const bf16x8*>(fr + E2 + 1024 * kk);
-                    const bf16x8 qh = *reinterpret_cast<const bf16x8*>(fr + 2 * E2 + 1024 * kk);
-                    const bf16x8 ql = *reinterpret_cast<const bf16x8*>(fr + 3 * E2 + 1024 * kk);
-                    Y = mfma32_bf16_x3(kh, kl, sbh, sbl, Y);
-                    O = mfma32_bf16_x3(qh, ql, sbh, sbl, O);
+                    Y = mfma32_bf16_x3(fa[0][kk], fa[1][kk], sbh, sbl, Y);
+                    O = mfma32_bf16_x3(fa[2][kk], fa[3][kk], sbh, sbl, O);
                 }
             }
             // X = V - Y (the beta scaling sits in T'), W = T' X
@@ -630,26 +647,31 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                 const float vv = (ESZ == 4) ? __uint_as_float(vc[4 * b + i]) : bf16_val(static_cast<uint16_t>(vc[4 * b + i]));
                 X[i] = vv - Y[i];
             }
-            s16x4 xh, xl;
-            split4(X, xh, xl);
-            const f32x4 W = mfma16_bf16_x3(*reinterpret_cast<const s16x4*>(Th), *reinterpret_cast<const s16x4*>(Tl),
-                                           xh, xl, zero4());
-            // O += P W
+            f32x4 W;
+            if constexpr (!PRECISE) {
+                f16x4 x16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x16[i] = static_cast<_Float16>(X[i]);
+                W = __builtin_amdgcn_mfma_f32_16x16x16f16(*reinterpret_cast<const f16x4*>(Tp), x16, zero4(), 0, 0, 0);
+            } else {
+                s16x4 xh, xl;
+                split4(X, xh, xl);
+                W = mfma16_bf16_x3(*reinterpret_cast<const s16x4*>(Tp), *reinterpret_cast<const s16x4*>(Tp + 256),
+                                   xh, xl, zero4());
+            }
+            // O += P W (P and Qt carry the output scale)
             s16x4 wh, wl;
             split4(W, wh, wl);
-            O = mfma16_bf16_x3(*reinterpret_cast<const s16x4*>(Ph), *reinterpret_cast<const s16x4*>(Pl), wh, wl, O);
+            O = mfma16_bf16_x3(ph, pl, wh, wl, O);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int off = ((16 * b + 4 * lq + i) * vstride + n0 + ln) * OSZ;
                 if constexpr (ODT == KDA_F32)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * O[i]), orr, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i]), orr, off, 0, 0);
                 else
-                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(p.scale * O[i]), orr, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O[i]), orr, off, 0, 0);
             }
             // S <- Diag(e^{G_15}) S + Kb^T W = S + Diag(e^{G_15} - 1) S + Kb^T W
-            float4 gm[CT];
-#pragma unroll
-            for (int i = 0; i < CT; ++i) gm[i] = *reinterpret_cast<const float4*>(gam + 16 * i + 4 * lq);
             if constexpr (!PRECISE) {
                 const uint8_t* kbt = rb + 2 * E2 + 8 * lane;   // frag16 Kb^T
                 f16x4 w16;
@@ -675,6 +697,12 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                     acc[2] = fmaf(S[i][2], gm[i].z, S[i][2]); acc[3] = fmaf(S[i][3], gm[i].w, S[i][3]);
                     S[i] = mfma16_bf16_x3(kh, kl, wh, wl, acc);
                 }
+            }
+            if (b + 1 < NB) {
+#pragma unroll
+                for (int a = 0; a < NFA; ++a)
+#pragma unroll
+                    for (int kk = 0; kk < KS; ++kk) fa[a][kk] = fn[a][kk];
             }
         }
     };

@@ -110,7 +110,10 @@ size_t kda_chunk_fwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_
  *                   unspecified.  It must not overlap any other argument.  Calls that share
  *                   a workspace must not overlap in time.
  * Results match the token-by-token definition up to rounding: the kernels evaluate the chunked
- * form with fp32 accumulation and split-precision matrix products.
+ * form with fp32 accumulation and split-precision matrix products.  For bf16 inputs some
+ * range-bounded operands are staged in fp16; this assumes the usual KDA inputs -- q and k
+ * L2-normalised per head, beta in [0, 1], |v| and |scale * q| well below 65504 -- outside which
+ * intermediate values can leave the fp16 range.  fp32 inputs use bf16 hi/lo splits throughout.
  */
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *beta, int in_dtype,
                   const void *g, int g_dtype, const float *initial_state, float *final_state,
