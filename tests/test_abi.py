@@ -104,10 +104,15 @@ def test_chunk_fwd_gated_rejects(lib):
 
 def test_workspace_size(lib):
     import torch
+    # one fixed-size record per (head, 16-token block slot); slots <= tokens/16 + sequences + 1
+    for dt in (torch.bfloat16, torch.float32):
+        rec = K.kda_chunk_fwd_workspace_size(1, 0, 1, 128, 128, in_dtype=dt) // 2
+        assert rec > 0 and rec % 16 == 0
+        for n, tok, H in [(4, 4 * 4096, 16), (8, 1 << 20, 8), (3, 17, 5), (1, 15, 1)]:
+            assert K.kda_chunk_fwd_workspace_size(n, tok, H, 128, 128, in_dtype=dt) == \
+                (tok // 16 + n + 1) * H * rec
     bf = K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128)
     f32 = K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128, in_dtype=torch.float32)
-    # one record per (head, 16-token block slot), slots bounded by tokens/16 + sequences + 1
-    assert bf == (4 * 4096 // 16 + 4 + 1) * 16 * 14848
     assert f32 > bf
     assert K.kda_chunk_fwd_workspace_size(1, 4096, 16, 96, 128) == 0
     assert K.kda_chunk_fwd_workspace_size(0, 4096, 16, 128, 128) == 0
