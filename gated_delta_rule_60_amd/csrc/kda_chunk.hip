@@ -301,7 +301,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
     if constexpr (GATE) {
         const float* a = p.gate_A + static_cast<int64_t>(h) * DK + CPT * cg;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) ea[c] = expf(a[c]);
+        for (int c = 0; c < CPT; ++c) ea[c] = gate_rate(a[c]);
     }
     auto gval = [&](int i, int c) -> float {
         if constexpr (GATE) return (4 * sub + i < nt) ? gate_log_decay(ea[c], pg.get(i * CPT + c), p.g_min) : 0.f;
@@ -332,6 +332,9 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
 
     // ---- decay factors, operands
     constexpr int NP = CPT / 2;
+    float gam[CPT];                                       // e^{G15}
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) gam[c] = fexp2(G15[c]);
     float kb[NEL];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -340,13 +343,12 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const float g2 = G2[i * CPT + c];
-            const float e1 = fexp2(g2);                   // e^{G}        <= 1
-            const float e2 = fexp2(G15[c] - g2);          // e^{G15 - G}  <= 1
+            const float e1 = fexp2(g2);                   // e^{G}  <= 1
             const float kv = pk.get(i * CPT + c);
             kt[c] = kv * e1;
             qt[c] = pq.get(i * CPT + c) * (e1 * p.scale);   // the output scale rides on Qt and P
-            kb[i * CPT + c] = kv * e2;
-            kd[c] = kv * (e2 * fexp2(-G15[c]));           // e^{-G} <= e^80
+            kd[c] = kv * fexp2(-g2);                      // e^{-G} <= e^80
+            kb[i * CPT + c] = kd[c] * gam[c];             // e^{G15 - G} <= 1
         }
         uint32_t wKh[NP], wKl[NP], wQh[NP], wQl[NP], wDh[NP], wDl[NP];
 #pragma unroll
@@ -393,9 +395,9 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
     }
     // record: e^{G_15} - 1 (same absolute precision as e^{G_15} in fp32)
     if (sub == 0) {
-        float* gam = reinterpret_cast<float*>(rec + R::OFF_G) + CPT * cg;
+        float* gr = reinterpret_cast<float*>(rec + R::OFF_G) + CPT * cg;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) gam[c] = fexp2(G15[c]) - 1.f;
+        for (int c = 0; c < CPT; ++c) gr[c] = gam[c] - 1.f;
     }
 
     __syncthreads();   // the operand arrays and beta are read across lanes below

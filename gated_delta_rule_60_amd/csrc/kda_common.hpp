@@ -9,13 +9,19 @@
 namespace kda {
 
 // ---------------------------------------------------------------- forget gate
-// g = g_min * sigmoid(exp(A) * z) for one element, given exp(A).  The separate gate kernel and
-// the chunk kernel's fused gate both call this, with contraction off, so the two paths produce
-// the same bits of g.
-__device__ __forceinline__ float gate_log_decay(float a_exp, float z, float g_min) {
+// g = g_min * sigmoid(exp(A) * z) = g_min / (1 + 2^(-rate * z)) with rate = exp(A) * log2(e),
+// one per (head, key channel).  Hardware exp2 and reciprocal (about 1 ulp each) keep g within
+// 1e-6 of the exact value over g in [-5, 0]; saturation gives g_min and -0.  The separate gate
+// kernel and the chunk kernel's fused gate both call these, with contraction off, so the two
+// paths produce the same bits of g.
+__device__ __forceinline__ float gate_rate(float A) {
 #pragma clang fp contract(off)
-    const float x = a_exp * z;
-    return g_min / (1.0f + expf(-x));
+    return expf(A) * 1.4426950408889634f;
+}
+__device__ __forceinline__ float gate_log_decay(float rate, float z, float g_min) {
+#pragma clang fp contract(off)
+    const float e = __builtin_amdgcn_exp2f(-(rate * z));
+    return g_min * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // ---------------------------------------------------------------- bf16 <-> fp32 (bit level)

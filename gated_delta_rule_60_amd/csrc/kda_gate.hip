@@ -25,10 +25,10 @@ __global__ void __launch_bounds__(256) gate_kernel_vec4(const float* __restrict_
         const float4 zz = load4_as_f32<ZDT>(z, e);
         const float4 aa = *reinterpret_cast<const float4*>(A + ac);
         float4 out;
-        out.x = gate_log_decay(expf(aa.x), zz.x, g_min);
-        out.y = gate_log_decay(expf(aa.y), zz.y, g_min);
-        out.z = gate_log_decay(expf(aa.z), zz.z, g_min);
-        out.w = gate_log_decay(expf(aa.w), zz.w, g_min);
+        out.x = gate_log_decay(gate_rate(aa.x), zz.x, g_min);
+        out.y = gate_log_decay(gate_rate(aa.y), zz.y, g_min);
+        out.z = gate_log_decay(gate_rate(aa.z), zz.z, g_min);
+        out.w = gate_log_decay(gate_rate(aa.w), zz.w, g_min);
         store4_from_f32<GDT>(g, e, out);
     }
 }
@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(256) gate_kernel_scalar(const float* __restric
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
          e += stride) {
         const float a = A[e % hdk];
-        store_from_f32<GDT>(g, e, gate_log_decay(expf(a), load_as_f32<ZDT>(z, e), g_min));
+        store_from_f32<GDT>(g, e, gate_log_decay(gate_rate(a), load_as_f32<ZDT>(z, e), g_min));
     }
 }
 
