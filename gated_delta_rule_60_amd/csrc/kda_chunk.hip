@@ -246,14 +246,14 @@ __device__ __forceinline__ bool locate_slot(const ChunkArgs& p, int64_t slot, in
 template <int DK, int IDT, int GDT, bool PRECISE, bool GATE>
 __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     using R = Rec<DK, PRECISE>;
-    constexpr int CPT = DK / 16;          // channels per lane (8 or 4)
-    constexpr int NEL = 4 * CPT;          // elements per lane
-    constexpr int KS = DK / 32;
+    constexpr int PH = DK / 64;           // the channels are processed in phases of 64
+    constexpr int LE = BLK * 64;          // elements of one [16][64] LDS operand array
     constexpr float LOG2E = 1.4426950408889634f;
 
-    __shared__ __attribute__((aligned(16))) uint16_t sKh[R::E], sKl[R::E];   // Kt  hi/lo
-    __shared__ __attribute__((aligned(16))) uint16_t sQh[R::E], sQl[R::E];   // Qt  hi/lo
-    __shared__ __attribute__((aligned(16))) uint16_t sDh[R::E], sDl[R::E];   // Kd  hi/lo
+    // split operands of one phase (reused by the next): 12 KB, so that 12 waves fit a CU
+    __shared__ __attribute__((aligned(16))) uint16_t sKh[LE], sKl[LE];   // Kt  hi/lo
+    __shared__ __attribute__((aligned(16))) uint16_t sQh[LE], sQl[LE];   // Qt  hi/lo
+    __shared__ __attribute__((aligned(16))) uint16_t sDh[LE], sDl[LE];   // Kd  hi/lo
     __shared__ __attribute__((aligned(16))) float sA[16][16];
     __shared__ float sBeta[16];
 
@@ -271,9 +271,10 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
     const int nt = static_cast<int>((len - t0) < BLK ? (len - t0) : BLK);
     uint8_t* rec = ws + (static_cast<int64_t>(h) * nslots + slot) * R::BYTES;
 
-    // ---- inputs: rows 4sub..4sub+3, channels CPT*cg.. ; beta in lanes 0..15
-    Raw<GDT, NEL> pg;                     // g, or z when the gate is fused
-    Raw<IDT, NEL> pk, pq;
+    // ---- inputs of every phase, loaded up front: in phase ph, lane (cg, sub) holds rows
+    // 4sub .. 4sub+3, channels 64ph + 4cg .. +3; beta goes to LDS from lanes 0..15
+    Raw<GDT, 16> pg[PH];                  // g, or z when the gate is fused
+    Raw<IDT, 16> pk[PH], pq[PH];
     {
         const int64_t row0 = (bos + t0) * H + h;
         const int32_t kstride = static_cast<int32_t>(H) * DK;
@@ -281,133 +282,133 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
         const void* kbase = static_cast<const char*>(p.k) + row0 * DK * (IDT == KDA_F32 ? 4 : 2);
         const void* qbase = static_cast<const char*>(p.q) + row0 * DK * (IDT == KDA_F32 ? 4 : 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * sub + i;
-            const bool ok = r < nt;
-            const int32_t e = ok ? r * kstride + CPT * cg : 0;
-            load_row<GDT, CPT>(pg, i, gbase, e, ok);
-            load_row<IDT, CPT>(pk, i, kbase, e, ok);
-            load_row<IDT, CPT>(pq, i, qbase, e, ok);
-        }
+        for (int ph = 0; ph < PH; ++ph)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * sub + i;
+                const bool ok = r < nt;
+                const int32_t e = ok ? r * kstride + 64 * ph + 4 * cg : 0;
+                load_row<GDT, 4>(pg[ph], i, gbase, e, ok);
+                load_row<IDT, 4>(pk[ph], i, kbase, e, ok);
+                load_row<IDT, 4>(pq[ph], i, qbase, e, ok);
+            }
         if (lane < 16) {
             const void* bbase = static_cast<const char*>(p.beta) + row0 * (IDT == KDA_F32 ? 4 : 2);
             sBeta[lane] = (lane < nt) ? load_as_f32<IDT>(bbase, lane * static_cast<int32_t>(H)) : 0.f;
         }
     }
 
-    // ---- fused gate: g = g_min * sigmoid(exp(A) z) from z, the same arithmetic as kda_gate;
-    // rows past the block's tokens get g = 0 like the zero-filled g of the unfused path
-    float ea[CPT];
-    if constexpr (GATE) {
-        const float* a = p.gate_A + static_cast<int64_t>(h) * DK + CPT * cg;
+    f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) ea[c] = gate_rate(a[c]);
-    }
-    auto gval = [&](int i, int c) -> float {
-        if constexpr (GATE) return (4 * sub + i < nt) ? gate_log_decay(ea[c], pg.get(i * CPT + c), p.g_min) : 0.f;
-        else return pg.get(i * CPT + c);
-    };
+    for (int ph = 0; ph < PH; ++ph) {
+        const int c0 = 64 * ph + 4 * cg;                  // this lane's first channel
+        if (ph > 0) __syncthreads();                      // the previous phase's reads are done
 
-    // ---- block cumsum (log2 units): own 4 tokens, then a scan over the 4 lanes of the group
-    float G2[NEL];
-    float G15[CPT];
+        // ---- fused gate: g = g_min * sigmoid(exp(A) z) from z, the same arithmetic as kda_gate;
+        // rows past the block's tokens get g = 0 like the zero-filled g of the unfused path
+        float ea[4];
+        if constexpr (GATE) {
+            const float* a = p.gate_A + static_cast<int64_t>(h) * DK + c0;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        float run = 0.f;
+            for (int c = 0; c < 4; ++c) ea[c] = gate_rate(a[c]);
+        }
+        auto gval = [&](int i, int c) -> float {
+            if constexpr (GATE) return (4 * sub + i < nt) ? gate_log_decay(ea[c], pg[ph].get(i * 4 + c), p.g_min) : 0.f;
+            else return pg[ph].get(i * 4 + c);
+        };
+
+        // ---- block cumsum (log2 units): own 4 tokens, then a scan over the 4 lanes of the group
+        float G2[16];
+        float G15[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float run = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                run += gval(i, c) * LOG2E;
+                G2[i * 4 + c] = run;
+            }
+            float incl = run;
+            const float u1 = quad_perm<QP_PREV1>(incl);
+            if (sub >= 1) incl += u1;
+            const float u2 = quad_perm<QP_PREV2>(incl);
+            if (sub >= 2) incl += u2;
+            const float excl = incl - run;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G2[i * 4 + c] += excl;
+            G15[c] = quad_perm<QP_LAST>(incl);
+        }
+
+        // ---- decay factors, operands
+        float gam[4];                                     // e^{G15}
+#pragma unroll
+        for (int c = 0; c < 4; ++c) gam[c] = fexp2(G15[c]);
+        float kb[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            run += gval(i, c) * LOG2E;
-            G2[i * CPT + c] = run;
-        }
-        float incl = run;
-        const float u1 = quad_perm<QP_PREV1>(incl);
-        if (sub >= 1) incl += u1;
-        const float u2 = quad_perm<QP_PREV2>(incl);
-        if (sub >= 2) incl += u2;
-        const float excl = incl - run;
+            const int r = 4 * sub + i;
+            float kt[4], qt[4], kd[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) G2[i * CPT + c] += excl;
-        G15[c] = quad_perm<QP_LAST>(incl);
-    }
-
-    // ---- decay factors, operands
-    constexpr int NP = CPT / 2;
-    float gam[CPT];                                       // e^{G15}
+            for (int c = 0; c < 4; ++c) {
+                const float g2 = G2[i * 4 + c];
+                const float e1 = fexp2(g2);               // e^{G}  <= 1
+                const float kv = pk[ph].get(i * 4 + c);
+                kt[c] = kv * e1;
+                qt[c] = pq[ph].get(i * 4 + c) * (e1 * p.scale);   // the output scale rides on Qt and P
+                kd[c] = kv * fexp2(-g2);                  // e^{-G} <= e^80
+                kb[i * 4 + c] = kd[c] * gam[c];           // e^{G15 - G} <= 1
+            }
+            uint32_t wKh[2], wKl[2], wQh[2], wQl[2], wDh[2], wDl[2];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) gam[c] = fexp2(G15[c]);
-    float kb[NEL];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * sub + i;
-        float kt[CPT], qt[CPT], kd[CPT];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const float g2 = G2[i * CPT + c];
-            const float e1 = fexp2(g2);                   // e^{G}  <= 1
-            const float kv = pk.get(i * CPT + c);
-            kt[c] = kv * e1;
-            qt[c] = pq.get(i * CPT + c) * (e1 * p.scale);   // the output scale rides on Qt and P
-            kd[c] = kv * fexp2(-g2);                      // e^{-G} <= e^80
-            kb[i * CPT + c] = kd[c] * gam[c];             // e^{G15 - G} <= 1
-        }
-        uint32_t wKh[NP], wKl[NP], wQh[NP], wQl[NP], wDh[NP], wDl[NP];
-#pragma unroll
-        for (int u = 0; u < NP; ++u) {
-            split_pair(kt[2 * u], kt[2 * u + 1], wKh[u], wKl[u]);
-            split_pair(qt[2 * u], qt[2 * u + 1], wQh[u], wQl[u]);
-            split_pair(kd[2 * u], kd[2 * u + 1], wDh[u], wDl[u]);
-        }
-        const int off = tok_major<DK>(r, CPT * cg);
-        store_words<NP>(sKh + off, wKh); store_words<NP>(sKl + off, wKl);
-        store_words<NP>(sQh + off, wQh); store_words<NP>(sQl + off, wQl);
-        store_words<NP>(sDh + off, wDh); store_words<NP>(sDl + off, wDl);
-        // record: the state pass's Kt, Qt operands (frag32: four channels = 8 contiguous bytes)
-#pragma unroll
-        for (int h4 = 0; h4 < CPT / 4; ++h4) {
-            const int fo = 2 * frag32(r, CPT * cg + 4 * h4);
+            for (int u = 0; u < 2; ++u) {
+                split_pair(kt[2 * u], kt[2 * u + 1], wKh[u], wKl[u]);
+                split_pair(qt[2 * u], qt[2 * u + 1], wQh[u], wQl[u]);
+                split_pair(kd[2 * u], kd[2 * u + 1], wDh[u], wDl[u]);
+            }
+            const int off = tok_major<64>(r, 4 * cg);
+            store_words<2>(sKh + off, wKh); store_words<2>(sKl + off, wKl);
+            store_words<2>(sQh + off, wQh); store_words<2>(sQl + off, wQl);
+            store_words<2>(sDh + off, wDh); store_words<2>(sDl + off, wDl);
+            // record: the state pass's Kt, Qt operands (frag32: four channels = 8 contiguous bytes)
+            const int fo = 2 * frag32(r, c0);
             if constexpr (!PRECISE) {
-                *reinterpret_cast<uint2*>(rec + fo) =
-                    make_uint2(f16_pair(kt[4 * h4], kt[4 * h4 + 1]), f16_pair(kt[4 * h4 + 2], kt[4 * h4 + 3]));
-                *reinterpret_cast<uint2*>(rec + 2 * R::E + fo) =
-                    make_uint2(f16_pair(qt[4 * h4], qt[4 * h4 + 1]), f16_pair(qt[4 * h4 + 2], qt[4 * h4 + 3]));
+                *reinterpret_cast<uint2*>(rec + fo) = make_uint2(f16_pair(kt[0], kt[1]), f16_pair(kt[2], kt[3]));
+                *reinterpret_cast<uint2*>(rec + 2 * R::E + fo) = make_uint2(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]));
             } else {
-                *reinterpret_cast<uint2*>(rec + fo) = make_uint2(wKh[2 * h4], wKh[2 * h4 + 1]);
-                *reinterpret_cast<uint2*>(rec + 2 * R::E + fo) = make_uint2(wKl[2 * h4], wKl[2 * h4 + 1]);
-                *reinterpret_cast<uint2*>(rec + 4 * R::E + fo) = make_uint2(wQh[2 * h4], wQh[2 * h4 + 1]);
-                *reinterpret_cast<uint2*>(rec + 6 * R::E + fo) = make_uint2(wQl[2 * h4], wQl[2 * h4 + 1]);
+                *reinterpret_cast<uint2*>(rec + fo) = make_uint2(wKh[0], wKh[1]);
+                *reinterpret_cast<uint2*>(rec + 2 * R::E + fo) = make_uint2(wKl[0], wKl[1]);
+                *reinterpret_cast<uint2*>(rec + 4 * R::E + fo) = make_uint2(wQh[0], wQh[1]);
+                *reinterpret_cast<uint2*>(rec + 6 * R::E + fo) = make_uint2(wQl[0], wQl[1]);
             }
         }
-    }
-    // record: Kb^T (frag16: the lane's 4 tokens of each channel are contiguous)
+        // record: Kb^T (frag16: the lane's 4 tokens of each channel are contiguous)
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        const int off = frag16(CPT * cg + c, 4 * sub);
-        if constexpr (!PRECISE) {
-            *reinterpret_cast<uint2*>(rec + 2 * (2 * R::E + off)) =
-                make_uint2(f16_pair(kb[0 * CPT + c], kb[1 * CPT + c]), f16_pair(kb[2 * CPT + c], kb[3 * CPT + c]));
-        } else {
-            uint32_t h0, l0, h1, l1;
-            split_pair(kb[0 * CPT + c], kb[1 * CPT + c], h0, l0);
-            split_pair(kb[2 * CPT + c], kb[3 * CPT + c], h1, l1);
-            *reinterpret_cast<uint2*>(rec + 2 * (4 * R::E + off)) = make_uint2(h0, h1);
-            *reinterpret_cast<uint2*>(rec + 2 * (5 * R::E + off)) = make_uint2(l0, l1);
+        for (int c = 0; c < 4; ++c) {
+            const int off = frag16(c0 + c, 4 * sub);
+            if constexpr (!PRECISE) {
+                *reinterpret_cast<uint2*>(rec + 2 * (2 * R::E + off)) =
+                    make_uint2(f16_pair(kb[0 + c], kb[4 + c]), f16_pair(kb[8 + c], kb[12 + c]));
+            } else {
+                uint32_t h0, l0, h1, l1;
+                split_pair(kb[0 + c], kb[4 + c], h0, l0);
+                split_pair(kb[8 + c], kb[12 + c], h1, l1);
+                *reinterpret_cast<uint2*>(rec + 2 * (4 * R::E + off)) = make_uint2(h0, h1);
+                *reinterpret_cast<uint2*>(rec + 2 * (5 * R::E + off)) = make_uint2(l0, l1);
+            }
         }
-    }
-    // record: e^{G_15} - 1 (same absolute precision as e^{G_15} in fp32)
-    if (sub == 0) {
-        float* gr = reinterpret_cast<float*>(rec + R::OFF_G) + CPT * cg;
+        // record: e^{G_15} - 1 (same absolute precision as e^{G_15} in fp32)
+        if (sub == 0) {
+            float* gr = reinterpret_cast<float*>(rec + R::OFF_G) + c0;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) gr[c] = gam[c] - 1.f;
-    }
+            for (int c = 0; c < 4; ++c) gr[c] = gam[c] - 1.f;
+        }
 
-    __syncthreads();   // the operand arrays and beta are read across lanes below
+        __syncthreads();   // the operand arrays (and beta) are read across lanes below
 
-    // ---- A and P (16 x 16, contraction over d_k) on MFMA
-    {
-        f32x4 accA = zero4(), accP = zero4();
+        // ---- this phase's share of A and P (16 x 16, contraction over its 64 channels)
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int off = tok_major<DK>(ln, 32 * kk + 8 * lq);
+        for (int kk = 0; kk < 2; ++kk) {
+            const int off = tok_major<64>(ln, 32 * kk + 8 * lq);
             const bf16x8 kh = *reinterpret_cast<const bf16x8*>(sKh + off);
             const bf16x8 kl = *reinterpret_cast<const bf16x8*>(sKl + off);
             const bf16x8 qh = *reinterpret_cast<const bf16x8*>(sQh + off);
@@ -417,6 +418,8 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
             accA = mfma32_bf16_x3(kh, kl, dh, dl, accA);
             accP = mfma32_bf16_x3(qh, ql, dh, dl, accP);
         }
+    }
+    {
         // lane (ln, lq) holds rows 4lq + i of column ln
         uint16_t* Ph = reinterpret_cast<uint16_t*>(rec + R::OFF_P);
         uint16_t* Pl = reinterpret_cast<uint16_t*>(rec + R::OFF_P + 512);
@@ -493,10 +496,13 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     constexpr int OSZ = (ODT == KDA_F32) ? 4 : 2;
     constexpr int WKB = 64 * 16;                       // bytes one wave moves per DMA load
     constexpr int ROUNDS = (NB * R::BYTES + NW * WKB - 1) / (NW * WKB);
-    constexpr int LBYTES = ROUNDS * NW * WKB;          // a chunk's records, padded to whole rounds
+    constexpr int RBYTES = ROUNDS * NW * WKB;          // a chunk's records, padded to whole rounds
     constexpr int BVW = 16 * NW;                       // state columns per workgroup
-    constexpr int NV = NB * 4;                         // V values per lane per chunk
+    constexpr int VROW = BVW * ESZ;                    // bytes of one token's V slice
+    constexpr int VROUNDS = (CHT * VROW + NW * WKB - 1) / (NW * WKB);
+    constexpr int LBYTES = RBYTES + VROUNDS * NW * WKB;   // records, then V [CHT][BVW]
     constexpr int E2 = 2 * R::E;                       // bytes of one 16-bit operand array
+    static_assert(WKB % VROW == 0, "a DMA round covers whole V rows");
 
     // Two chunk buffers.  The loop below is unrolled by two so that every access names its
     // buffer statically: the compiler then knows the records streaming into one buffer do not
@@ -553,38 +559,42 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
         const int64_t rem = len - c * CHT;
         return static_cast<int>(rem < 0 ? 0 : rem < CHT ? rem : CHT);
     };
-    // Chunk c's records go straight from memory into an LDS buffer (records past the sequence's
-    // last block, and the padding, read as zeros: identity steps); its V entries go to registers.
-    auto fill = [&](uint8_t* buf, int64_t c) {
+    // Chunk c's records and its V slice go straight from memory into an LDS buffer (records past
+    // the sequence's last block, V rows past its last token, and the padding read as zeros:
+    // identity steps).  The transfers are issued in NB - 1 slices, one at the start of each
+    // block but the last, so that they do not queue up in front of the block computations.
+    constexpr int NITEM = ROUNDS + VROUNDS;
+    constexpr int NSLICE = NB - 1;
+    auto prefetch_slice = [&](uint8_t* buf, int64_t c, int slice) {
         const int nt = tokens_in(c);
         const int nbk = (nt + BLK - 1) / BLK;
         const __amdgpu_buffer_rsrc_t rr =
             make_rsrc(nt > 0 ? recs + c * NB * R::BYTES : ws, static_cast<uint32_t>(nbk * R::BYTES));
-#pragma unroll
-        for (int k = 0; k < ROUNDS; ++k) {
-            const int u = k * NW + wave;                // this wave's 1 KB unit of the buffer
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rr, (__attribute__((address_space(3))) void*)(buf + u * WKB), 16, u * WKB + 16 * lane,
-                0, 0, 0);
-        }
-    };
-    auto load_v = [&](uint32_t (&dst)[NV], int64_t c) {
-        const int nt = tokens_in(c);
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(
             nt > 0 ? static_cast<const uint8_t*>(p.v) + ((bos + c * CHT) * H + h) * DV * ESZ : p.v,
             static_cast<uint32_t>(nt * vstride * ESZ));
+        const int i0 = slice * NITEM / NSLICE, i1 = (slice + 1) * NITEM / NSLICE;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int off = ((16 * b + 4 * lq + i) * vstride + n0 + ln) * ESZ;
-                if constexpr (ESZ == 4) dst[4 * b + i] = __builtin_amdgcn_raw_buffer_load_b32(vr, off, 0, 0);
-                else dst[4 * b + i] = __builtin_amdgcn_raw_buffer_load_b16(vr, off, 0, 0);
+        for (int it = 0; it < NITEM; ++it) {
+            if (it < i0 || it >= i1) continue;
+            if (it < ROUNDS) {
+                const int u = it * NW + wave;           // this wave's 1 KB unit of the records
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rr, (__attribute__((address_space(3))) void*)(buf + u * WKB), 16,
+                    u * WKB + 16 * lane, 0, 0, 0);
+            } else {
+                const int u = (it - ROUNDS) * NW + wave;   // this wave's 1 KB unit of V
+                const int byte = u * WKB + 16 * lane;     // within the [CHT][BVW] slice
+                const int row = byte / VROW, col = byte % VROW;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    vr, (__attribute__((address_space(3))) void*)(buf + RBYTES + u * WKB), 16,
+                    row * vstride * ESZ + vb * VROW + col, 0, 0, 0);
             }
+        }
     };
 
     // One chunk: NB state steps of 16 tokens from the records in `buf`.
-    auto run = [&](const uint8_t* buf, int64_t c, const uint32_t (&vc)[NV]) {
+    auto run = [&](const uint8_t* buf, int64_t c, uint8_t* nbuf) {
         const int nt = tokens_in(c);
         // o rows of this chunk and head; rows past the chunk's tokens fall outside the range
         const __amdgpu_buffer_rsrc_t orr =
@@ -606,6 +616,12 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
         load_fa(buf, fa);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
+            if (b < NSLICE) {
+                prefetch_slice(nbuf, c + 1, b);
+                // memory instructions keep their order across this point (the end-of-chunk wait
+                // counts on every load being older than the last two blocks' o stores)
+                __builtin_amdgcn_sched_barrier(0x78F);
+            }
             const uint8_t* rb = buf + b * R::BYTES;
             if (b + 1 < NB) load_fa(rb + R::BYTES, fn);
             const uint16_t* Tp = reinterpret_cast<const uint16_t*>(rb + R::OFF_T) + 4 * lane;
@@ -646,7 +662,9 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
             f32x4 X;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float vv = (ESZ == 4) ? __uint_as_float(vc[4 * b + i]) : bf16_val(static_cast<uint16_t>(vc[4 * b + i]));
+                const int ve = (16 * b + 4 * lq + i) * BVW + 16 * wave + ln;   // V[token][column]
+                const float vv = (ESZ == 4) ? reinterpret_cast<const float*>(buf + RBYTES)[ve]
+                                            : bf16_val(reinterpret_cast<const uint16_t*>(buf + RBYTES)[ve]);
                 X[i] = vv - Y[i];
             }
             f32x4 W;
@@ -709,29 +727,23 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
         }
     };
 
-    // Each half-iteration starts the next chunk's transfers, runs the current chunk, then waits
-    // for its own transfers -- the o stores of the chunk (4 per block) may stay in flight, the
-    // older loads may not -- and meets the other waves at the barrier.
-    constexpr int WAIT_LOADS = vmcnt_imm(4 * NB);
+    // Each half-iteration runs the current chunk while the next chunk's transfers go out, then
+    // waits for those transfers -- the o stores of the chunk's last two blocks (4 each) may stay
+    // in flight, every load is older -- and meets the other waves at the barrier.
+    constexpr int WAIT_LOADS = vmcnt_imm(8);
     const int64_t nchunks = (len + CHT - 1) / CHT;
-    uint32_t vA[NV], vB[NV];
-    fill(bufA, 0);
-    load_v(vA, 0);
+#pragma unroll
+    for (int sl = 0; sl < NSLICE; ++sl) prefetch_slice(bufA, 0, sl);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     for (int64_t ci = 0; ci < nchunks; ci += 2) {
-        fill(bufB, ci + 1);
-        load_v(vB, ci + 1);
         __builtin_amdgcn_sched_barrier(0);
-        run(bufA, ci, vA);
+        run(bufA, ci, bufB);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAIT_LOADS);
         __syncthreads();
         if (ci + 1 >= nchunks) break;
-        fill(bufA, ci + 2);
-        load_v(vA, ci + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        run(bufB, ci + 1, vB);
+        run(bufB, ci + 1, bufA);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAIT_LOADS);
         __syncthreads();
