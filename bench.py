@@ -95,6 +95,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def copy_ceiling(dev, stream, mib=1024, reps=10):
+    """Device-to-device copy of `mib` MiB (torch copy_), the practical HBM ceiling: bytes read
+    plus bytes written per second, best of `reps` timed with HIP events on the stream."""
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2 * (mib << 20) / (best * 1e-3)
+
+
 def run_decode(args, dev, inputs, K, stream):
     """The decode workload: 64 in-place steps over 256 sequences x 32 heads, timed with HIP events
     on the launch stream over args.decode_passes passes."""
@@ -236,6 +254,8 @@ def main():
     value = tokens / (ms_per_step * 1e-3)
 
     dec = run_decode(args, dev, inputs, K, stream)
+    copy_bps = copy_ceiling(dev, stream)
+    dec["roofline"]["frac_of_copy"] = round(dec["roofline"]["achieved"] * 1e9 / copy_bps, 4)
 
     # ------------------------------------------------------------------ CPU baseline (oracle)
     cpu = None
@@ -285,6 +305,7 @@ def main():
                     "kda_chunk_fwd_frac_hbm": round(chunk_bytes / (chunk_avg * 1e-3) / HBM_PEAK, 4),
                     "tokens_per_s": round(tokens / ((gate_avg + chunk_avg) * 1e-3), 1)},
         "decode": dec,
+        "copy_ceiling_gbs": round(copy_bps / 1e9, 1),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -15,11 +15,24 @@
 // Layout: one 256-lane workgroup per (sequence, head).  Lane t owns four consecutive state
 // columns (16-byte loads/stores) of d_k / (256 / (d_v / 4)) consecutive rows, so each row is
 // read by d_v/4 lanes as one contiguous segment.  Partial column sums meet in LDS.  The state
-// stays in registers between the read and the write; HBM sees it exactly once each way.
+// stays in registers between the read and the write; HBM sees it exactly once each way.  The
+// state is streamed with non-temporal loads and stores: a decode step touches each state once,
+// so keeping it out of the caches leaves them to the small per-token inputs.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 stream_load4(const float* p) {
+    const f32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void stream_store4(float* p, float4 x) {
+    const f32x4_t y = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(y, reinterpret_cast<f32x4_t*>(p));
+}
 
 template <int DK, int DV, int IDT, int GDT, int ODT>
 __global__ void __launch_bounds__(256) decode_kernel(const void* __restrict__ q,
@@ -48,7 +61,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const void* __restrict__ q,
     float4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-        s[i] = *reinterpret_cast<const float4*>(S + (rg * RPT + i) * DV + 4 * cg);
+        s[i] = stream_load4(S + (rg * RPT + i) * DV + 4 * cg);
 
     float kq = 0.0f;
     if (t < DK) {
@@ -105,7 +118,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const void* __restrict__ q,
         x.y = al * x.y + bk * u.y;
         x.z = al * x.z + bk * u.z;
         x.w = al * x.w + bk * u.w;
-        *reinterpret_cast<float4*>(S + r * DV + 4 * cg) = x;
+        stream_store4(S + r * DV + 4 * cg, x);
     }
 }
 
