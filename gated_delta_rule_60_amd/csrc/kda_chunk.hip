@@ -61,6 +61,7 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // lies outside the range read 0 and write nothing, so loads and stores need no branches and the
 // compiler can count outstanding memory operations exactly.  Word 3 selects 32-bit data format.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int CP_NT = 2;   // buffer cache policy: non-temporal (data used once)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                              static_cast<int>(bytes), 0x00020000);
@@ -180,6 +181,10 @@ struct Raw<KDA_BF16, N> {
         return (i & 1) ? __uint_as_float(v[i / 2] & 0xffff0000u) : __uint_as_float(v[i / 2] << 16);
     }
 };
+// Inputs are read exactly once: non-temporal loads keep them out of the caches, which are
+// better spent on the workspace records that the state pass reads back.
+typedef unsigned int u32x4nt __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2nt __attribute__((ext_vector_type(2)));
 template <int DT, int CPT, int N>
 __device__ __forceinline__ void load_row(Raw<DT, N>& dst, int slot, const void* base, int32_t e,
                                          bool ok) {
@@ -187,21 +192,24 @@ __device__ __forceinline__ void load_row(Raw<DT, N>& dst, int slot, const void* 
         const float* src = static_cast<const float*>(base) + e;
 #pragma unroll
         for (int u = 0; u < CPT / 4; ++u) {
-            const float4 x = ok ? *reinterpret_cast<const float4*>(src + 4 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
-            dst.v[slot * CPT + 4 * u + 0] = x.x;
-            dst.v[slot * CPT + 4 * u + 1] = x.y;
-            dst.v[slot * CPT + 4 * u + 2] = x.z;
-            dst.v[slot * CPT + 4 * u + 3] = x.w;
+            u32x4nt x = {0u, 0u, 0u, 0u};
+            if (ok) x = __builtin_nontemporal_load(reinterpret_cast<const u32x4nt*>(src + 4 * u));
+            dst.v[slot * CPT + 4 * u + 0] = __uint_as_float(x[0]);
+            dst.v[slot * CPT + 4 * u + 1] = __uint_as_float(x[1]);
+            dst.v[slot * CPT + 4 * u + 2] = __uint_as_float(x[2]);
+            dst.v[slot * CPT + 4 * u + 3] = __uint_as_float(x[3]);
         }
     } else {
         const uint16_t* src = static_cast<const uint16_t*>(base) + e;
         if constexpr (CPT == 8) {
-            const uint4 x = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
-            dst.v[slot * 4 + 0] = x.x; dst.v[slot * 4 + 1] = x.y;
-            dst.v[slot * 4 + 2] = x.z; dst.v[slot * 4 + 3] = x.w;
+            u32x4nt x = {0u, 0u, 0u, 0u};
+            if (ok) x = __builtin_nontemporal_load(reinterpret_cast<const u32x4nt*>(src));
+            dst.v[slot * 4 + 0] = x[0]; dst.v[slot * 4 + 1] = x[1];
+            dst.v[slot * 4 + 2] = x[2]; dst.v[slot * 4 + 3] = x[3];
         } else {
-            const uint2 x = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
-            dst.v[slot * 2 + 0] = x.x; dst.v[slot * 2 + 1] = x.y;
+            u32x2nt x = {0u, 0u};
+            if (ok) x = __builtin_nontemporal_load(reinterpret_cast<const u32x2nt*>(src));
+            dst.v[slot * 2 + 0] = x[0]; dst.v[slot * 2 + 1] = x[1];
         }
     }
 }
@@ -325,7 +333,9 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
             float run = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                run += gval(i, c) * LOG2E;
+                // one explicit rounding: the fused-gate and g-given variants must not differ in
+                // whether the compiler contracts this into an fma
+                run = fmaf(gval(i, c), LOG2E, run);
                 G2[i * 4 + c] = run;
             }
             float incl = run;
@@ -588,7 +598,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                 const int row = byte / VROW, col = byte % VROW;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     vr, (__attribute__((address_space(3))) void*)(buf + RBYTES + u * WKB), 16,
-                    row * vstride * ESZ + vb * VROW + col, 0, 0, 0);
+                    row * vstride * ESZ + vb * VROW + col, 0, 0, CP_NT);
             }
         }
     };
@@ -687,9 +697,9 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
             for (int i = 0; i < 4; ++i) {
                 const int off = ((16 * b + 4 * lq + i) * vstride + n0 + ln) * OSZ;
                 if constexpr (ODT == KDA_F32)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i]), orr, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i]), orr, off, 0, CP_NT);
                 else
-                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O[i]), orr, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O[i]), orr, off, 0, CP_NT);
             }
             // S <- Diag(e^{G_15}) S + Kb^T W = S + Diag(e^{G_15} - 1) S + Kb^T W
             if constexpr (!PRECISE) {
