@@ -53,7 +53,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BLK = 16;     // tokens per block (one state step)
-constexpr int STATE_WAVES = 2;   // waves per state-kernel workgroup (16 state columns each)
+constexpr int STATE_WAVES = 4;   // waves per state-kernel workgroup (16 state columns each)
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
