@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 210;  // 0.2.1
 
 bool valid_dtype(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
 int64_t esize(int dt) { return dt == KDA_F32 ? 4 : 2; }
@@ -81,7 +81,8 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* beta
                    const float* initial_state, float* final_state, const int32_t* cu_seqlens,
                    void* o, int o_dtype, int32_t B, int64_t T, int32_t n_seqs, int32_t H,
                    int32_t dk, int32_t dv, int32_t chunk, float scale, void* workspace,
-                   size_t workspace_bytes, void* stream, bool gated) {
+                   size_t workspace_bytes, void* stream, bool gated, float* ckpt = nullptr,
+                   int32_t ckpt_every = 0, int64_t ckpt_slots = 0) {
     if (!valid_dtype(in_dtype) || !valid_dtype(g_dtype) || !valid_dtype(o_dtype))
         return KDA_ERR_INVALID_ARGUMENT;
     if (B < 1 || T < 0 || n_seqs < 1 || H < 1 || dk < 1 || dv < 1 || !std::isfinite(scale))
@@ -108,8 +109,11 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* beta
     const Range r_hT = range(final_state, final_state ? state_bytes : 0);
     const Range r_cu = range(cu_seqlens, cu_seqlens ? int64_t(n_seqs + 1) * 4 : 0);
     const Range r_ws = range(workspace, int64_t(workspace_bytes));
-    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_a, r_h0, r_hT, r_cu, r_ws})
+    const Range r_ck = range(ckpt, ckpt ? ckpt_slots * H * dk * dv * 4 : 0);
+    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_a, r_h0, r_hT, r_cu, r_ws, r_ck})
         if (overlap(r_o, x)) return KDA_ERR_INVALID_ARGUMENT;
+    for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_a, r_h0, r_hT, r_cu, r_ws})
+        if (overlap(r_ck, x)) return KDA_ERR_INVALID_ARGUMENT;
     // the final state may be the initial state itself, but must not partly overlap it
     if (initial_state && final_state && initial_state != final_state && overlap(r_h0, r_hT))
         return KDA_ERR_INVALID_ARGUMENT;
@@ -125,6 +129,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* beta
     a.in_dtype = in_dtype; a.g_dtype = g_dtype; a.o_dtype = o_dtype;
     a.B = B; a.T = T; a.n_seqs = n_seqs; a.H = H; a.dk = dk; a.dv = dv;
     a.scale = scale; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.ckpt = ckpt; a.ckpt_every = ckpt_every; a.ckpt_slots = ckpt_slots;
     return from_hip(kda::launch_chunk(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -151,6 +156,26 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void*
     return chunk_fwd_impl(q, k, v, beta, in_dtype, z, z_dtype, A, g_min, initial_state,
                           final_state, cu_seqlens, o, o_dtype, B, T, n_seqs, H, dk, dv, chunk,
                           scale, workspace, workspace_bytes, stream, true);
+}
+
+int kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* v, const void* beta,
+                               int in_dtype, const float* A, const void* g_or_z, int gz_dtype,
+                               float g_min, const float* initial_state, float* final_state,
+                               const int32_t* cu_seqlens, void* o, int o_dtype, int32_t B,
+                               int64_t T, int32_t n_seqs, int32_t H, int32_t dk, int32_t dv,
+                               int32_t chunk, float scale, float* checkpoints,
+                               int32_t checkpoint_every, int64_t max_checkpoints, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (!checkpoints || checkpoint_every < 64 || checkpoint_every % 64 != 0 || max_checkpoints < 0)
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (B < 1 || T < 0 || n_seqs < 1) return KDA_ERR_INVALID_ARGUMENT;
+    // slots the layout can reach: B * floor(T / every), or floor(T / every) + n_seqs when packed
+    const int64_t need = cu_seqlens ? T / checkpoint_every + n_seqs : int64_t(B) * (T / checkpoint_every);
+    if (max_checkpoints < need) return KDA_ERR_INVALID_ARGUMENT;
+    return chunk_fwd_impl(q, k, v, beta, in_dtype, g_or_z, gz_dtype, A, A ? g_min : 0.0f,
+                          initial_state, final_state, cu_seqlens, o, o_dtype, B, T, n_seqs, H, dk,
+                          dv, chunk, scale, workspace, workspace_bytes, stream, A != nullptr,
+                          checkpoints, checkpoint_every, max_checkpoints);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const void* beta, int in_dtype,

@@ -553,6 +553,23 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     // state tiles: lane (ln, lq) of tile i holds S[16i + 4lq + r][n0 + ln]
     f32x4 S[CT];
     const int64_t sbase = unit * DK * DV;
+
+    // Checkpoints: the state after every ckpt_every tokens of the sequence goes to slot
+    // ck_base + j - 1 (j = 1, 2, ...): ck_base = n * floor(T / every) for fixed-length batches,
+    // floor(cu[n] / every) + n for packed ones (disjoint for the same reason as the block slots).
+    const int64_t ck_every = p.ckpt ? p.ckpt_every : 1;
+    const int64_t ck_base = p.cu ? static_cast<int64_t>(p.cu[n]) / ck_every + n
+                                 : static_cast<int64_t>(n) * (p.T / ck_every);
+    auto checkpoint = [&](int64_t done) {          // `done` tokens of the sequence processed
+        if (p.ckpt == nullptr || done > len || done % ck_every != 0) return;
+        const int64_t slot = ck_base + done / ck_every - 1;
+        if (slot >= p.ckpt_slots) return;
+        float* dst = p.ckpt + (slot * H + h) * DK * DV;
+#pragma unroll
+        for (int i = 0; i < CT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(16 * i + 4 * lq + r) * DV + n0 + ln] = S[i][r];
+    };
     {
         // an absent initial state is an empty range: every load reads 0
         const __amdgpu_buffer_rsrc_t h0r =
@@ -746,17 +763,22 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     for (int sl = 0; sl < NSLICE; ++sl) prefetch_slice(bufA, 0, sl);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
+    // (A checkpoint's stores go out before the next chunk's transfers, so they are older than
+    // every load the waits above count on.)
     for (int64_t ci = 0; ci < nchunks; ci += 2) {
         __builtin_amdgcn_sched_barrier(0);
         run(bufA, ci, bufB);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAIT_LOADS);
         __syncthreads();
+        checkpoint((ci + 1) * CHT);
         if (ci + 1 >= nchunks) break;
+        __builtin_amdgcn_sched_barrier(0);
         run(bufB, ci + 1, bufA);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAIT_LOADS);
         __syncthreads();
+        checkpoint((ci + 2) * CHT);
     }
 
     if (p.hT) {

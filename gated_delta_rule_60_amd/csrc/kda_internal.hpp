@@ -34,6 +34,9 @@ struct ChunkArgs {
     float scale;
     void* workspace;
     size_t workspace_bytes;
+    float* ckpt;           // state checkpoints or nullptr
+    int32_t ckpt_every;    // tokens between checkpoints (a multiple of 64)
+    int64_t ckpt_slots;    // capacity of ckpt in [H, dk, dv] states
 };
 
 // Workspace bytes of a chunked prefill: one record per (head, 16-token block).

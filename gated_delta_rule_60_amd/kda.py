@@ -55,6 +55,10 @@ def load_library(path: Optional[str] = None):
                                         vp, vp, vp, vp, ctypes.c_int, i32, i64, i32, i32, i32,
                                         i32, i32, f32, vp, sz, vp]
     lib.kda_chunk_fwd_gated.restype = ctypes.c_int
+    lib.kda_chunk_fwd_checkpointed.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int,
+                                               f32, vp, vp, vp, vp, ctypes.c_int, i32, i64, i32,
+                                               i32, i32, i32, i32, f32, vp, i32, i64, vp, sz, vp]
+    lib.kda_chunk_fwd_checkpointed.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
                                     ctypes.c_int, i32, i32, i32, i32, f32, vp]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -64,7 +68,7 @@ def load_library(path: Optional[str] = None):
 
 
 EXPORTED = ["kda_status_string", "kda_version", "kda_gate", "kda_chunk_fwd_workspace_size",
-            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_decode_step"]
+            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_checkpointed", "kda_decode_step"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -168,6 +172,47 @@ def kda_chunk_fwd_gated(q, k, v, beta, A, z, g_min: float = -5.0, initial_state=
         _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(o), _dt(o), B, T, N, H,
         dk, dv, 64, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
     return o, final_state
+
+
+def checkpoint_layout(every: int, T: int, B: int = 1, seqlens=None):
+    """Host-side slot layout of kda_chunk_fwd_checkpointed: ([(first slot, count) per sequence],
+    slots needed).  seqlens (host ints) describe a packed batch of total length T, else B
+    sequences of T tokens."""
+    if seqlens is None:
+        per = T // every
+        return [(n * per, per) for n in range(B)], B * per
+    out, start = [], 0
+    for n, length in enumerate(seqlens):
+        out.append((start // every + n, int(length) // every))
+        start += int(length)
+    return out, T // every + len(seqlens)
+
+
+def kda_chunk_fwd_checkpointed(q, k, v, beta, every: int, g=None, A=None, z=None,
+                               g_min: float = -5.0, initial_state=None, final_state=None,
+                               cu_seqlens=None, o=None, o_dtype=None, scale: float = 1.0,
+                               output_final_state: bool = True, checkpoints=None, workspace=None,
+                               stream=None):
+    """Chunked prefill that also stores the state after every `every` tokens (a multiple of
+    64) of each sequence.  Give g (as kda_chunk_fwd) or A and z (as kda_chunk_fwd_gated).
+    Returns (o, final_state, checkpoints [slots, H, dk, dv] fp32); slot layout as
+    checkpoint_layout; a new checkpoints buffer starts zeroed."""
+    if (g is None) == (A is None or z is None):
+        raise ValueError("give either g, or A and z")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N, o, final_state, workspace, ws_bytes = _chunk_outputs(
+        q, v, cu_seqlens, o, o_dtype, final_state, output_final_state, workspace)
+    need = (B * (T // every)) if cu_seqlens is None else (T // every + N)
+    if checkpoints is None:
+        checkpoints = torch.zeros((need, H, dk, dv), dtype=torch.float32, device=q.device)
+    gz = g if g is not None else z
+    _check("kda_chunk_fwd_checkpointed", load_library().kda_chunk_fwd_checkpointed(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(A), _ptr(gz), _dt(gz), float(g_min),
+        _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(o), _dt(o), B, T, N, H,
+        dk, dv, 64, float(scale), _ptr(checkpoints), int(every), checkpoints.shape[0],
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return o, final_state, checkpoints
 
 
 def kda_decode_step(q, k, v, beta, g, state, o=None, o_dtype=None, scale: float = 1.0,

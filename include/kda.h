@@ -138,6 +138,38 @@ int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const void 
                         size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_fwd_checkpointed -- the chunked prefill that also stores the state at fixed token
+ * boundaries, for prefix caching: a later request that shares a prefix resumes from the stored
+ * state (copy it, then continue) instead of recomputing the prefix ([habr, § Как обслуживать
+ * два разных кеша]: the recurrent state is what such a cache keeps).
+ *   A, g_or_z, gz_dtype, g_min : A non-NULL fuses the gate as kda_chunk_fwd_gated does (g_or_z
+ *                   is z, g_min as there); A NULL makes g_or_z the log-decay g of kda_chunk_fwd
+ *                   (g_min is then ignored).
+ *   checkpoints   : fp32 device buffer [max_checkpoints, H, d_k, d_v] owned by the caller.
+ *                   Checkpoint j >= 1 of sequence n is its state after its first
+ *                   j * checkpoint_every tokens, for every j with j * checkpoint_every <= len_n
+ *                   (the last one equals the final state when the length is a multiple); it goes
+ *                   to slot base(n) + j - 1 with base(n) = n * floor(T / checkpoint_every) for
+ *                   fixed-length batches and floor(cu_seqlens[n] / checkpoint_every) + n for
+ *                   packed ones.  Slots no checkpoint maps to are left untouched.
+ *   checkpoint_every : tokens between checkpoints, a positive multiple of 64 (the chunk).
+ *   max_checkpoints  : slots in `checkpoints`; at least B * floor(T / checkpoint_every) for
+ *                   fixed-length batches and floor(T / checkpoint_every) + n_seqs for packed ones.
+ * A NULL buffer, a checkpoint_every that is not a positive multiple of 64, too few slots, or a
+ * buffer that overlaps any other argument return KDA_ERR_INVALID_ARGUMENT.  Every other argument,
+ * the workspace size and the error behaviour are those of kda_chunk_fwd; o and final_state equal
+ * kda_chunk_fwd's (or kda_chunk_fwd_gated's) bit for bit.
+ */
+int kda_chunk_fwd_checkpointed(const void *q, const void *k, const void *v, const void *beta,
+                               int in_dtype, const float *A, const void *g_or_z, int gz_dtype,
+                               float g_min, const float *initial_state, float *final_state,
+                               const int32_t *cu_seqlens, void *o, int o_dtype, int32_t B,
+                               int64_t T, int32_t n_seqs, int32_t H, int32_t dk, int32_t dv,
+                               int32_t chunk, float scale, float *checkpoints,
+                               int32_t checkpoint_every, int64_t max_checkpoints, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * kda_decode_step -- one token of the recurrence for N independent sequences, updating each
  * state in place.  One pass reads S once and writes it once: reading the large recurrent
  * state is this step's cost ([habr, § Как обслуживать два разных кеша]).

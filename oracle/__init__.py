@@ -164,6 +164,47 @@ def forward_units(q, k, v, beta, g, units, S0=None, cu_seqlens=None, scale: floa
         return dict(ex.map(run, list(units)))
 
 
+def forward_checkpoints(q, k, v, beta, g, every: int, units=None, S0=None, cu_seqlens=None,
+                        scale: float = 1.0, max_workers: int | None = None,
+                        lib_path: str | None = None):
+    """States after every `every` tokens of each chosen (sequence, head) unit (all units when
+    `units` is None): {(n, h): [S after every, 2 every, ... tokens] (float64 [dk, dv] each)}.
+
+    The token loop of kda_oracle.c runs segment by segment on one fp64 state, so each value is
+    exactly the state a single pass holds at that position -- the prefix-cache checkpoints of a
+    chunked prefill (state kept at fixed boundaries so a shared prefix is not recomputed).
+    """
+    qq, idt = _host(q)
+    kk, _ = _host(k)
+    vv, _ = _host(v)
+    bb, _ = _host(beta)
+    gg, gdt = _host(g)
+    B, T, N, H, dk, dv, cu = _shapes(qq, vv, cu_seqlens)
+    s0, sdt = (None, _F32) if S0 is None else _host(S0)
+    if s0 is not None and sdt == _BF16:
+        raise TypeError("forward_checkpoints: bf16 S0 not supported")
+    lib = _load(lib_path)
+    if units is None:
+        units = [(n, h) for n in range(N) for h in range(H)]
+
+    def run(unit):
+        n, h = unit
+        tok0 = int(cu[n]) if cu is not None else n * T
+        length = int(cu[n + 1] - cu[n]) if cu is not None else T
+        S = np.zeros((dk, dv)) if s0 is None else np.array(s0[n, h], dtype=np.float64)
+        o_seg = np.empty((every, dv), dtype=np.float64)
+        states = []
+        for j in range(length // every):
+            lib.kda_oracle_unit(_p(qq), _p(kk), _p(vv), _p(bb), _p(gg), idt, gdt, tok0 + j * every,
+                                every, H, h, dk, dv, float(scale), _p(S), _p(o_seg), dv)
+            states.append(S.copy())
+        return unit, states
+
+    workers = max_workers or min(len(units), os.cpu_count() or 1) or 1
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return dict(ex.map(run, list(units)))
+
+
 def decode_step(q, k, v, beta, g, S: np.ndarray, scale: float = 1.0, nthreads: int = 0,
                 lib_path: str | None = None):
     """One token per sequence: q, k, g [N, H, dk]; v [N, H, dv]; beta [N, H];

@@ -147,3 +147,44 @@ def test_decode_rejects(lib):
     assert d(q=0) == INV
     assert d(o=FAKE + 0x10000000 + 64) == INV           # o overlaps the state
     assert d(N=0, q=0) == 0                              # nothing to do
+
+
+def ckpt(lib, q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, beta=FAKE + 0x30000000,
+         in_dt=1, A=0, gz=FAKE + 0x40000000, gz_dt=0, gmin=-5.0, h0=0, hT=0, cu=0,
+         o=FAKE + 0x50000000, o_dt=1, B=1, T=128, N=1, H=2, dk=128, dv=128, chunk=64, scale=1.0,
+         ck=FAKE + 0x90000000, every=64, slots=2, ws=FAKE + 0x80000000, ws_bytes=1 << 30):
+    return lib.kda_chunk_fwd_checkpointed(P(q), P(k), P(v), P(beta), in_dt, P(A), P(gz), gz_dt,
+                                          gmin, P(h0), P(hT), P(cu), P(o), o_dt, B, T, N, H, dk,
+                                          dv, chunk, scale, P(ck), every, slots, P(ws), ws_bytes,
+                                          None)
+
+
+def test_chunk_fwd_checkpointed_rejects(lib):
+    assert ckpt(lib, ck=0) == INV                        # buffer required
+    assert ckpt(lib, every=0) == INV
+    assert ckpt(lib, every=32) == INV                    # not a multiple of the 64-token chunk
+    assert ckpt(lib, every=96) == INV
+    assert ckpt(lib, slots=1) == INV                     # T=128, every=64: two slots needed
+    assert ckpt(lib, B=2, N=2, T=256, slots=7) == INV    # 2 * 4 needed
+    assert ckpt(lib, cu=FAKE + 0x60000000, N=3, slots=4) == INV   # packed: 128/64 + 3 needed
+    assert ckpt(lib, ck=FAKE + 0x50000000 + 64) == INV   # checkpoints overlap o
+    assert ckpt(lib, ck=FAKE + 0x80000000 + 64) == INV   # checkpoints overlap the workspace
+    assert ckpt(lib, ck=FAKE + 0x40000000 - 64) == INV   # checkpoints run into g
+    assert ckpt(lib, A=FAKE + 0x48000000, gmin=1.0) == UNS   # fused gate: g_min checked as usual
+    assert ckpt(lib, dk=96) == UNS
+    assert ckpt(lib, ws_bytes=16) == WS                  # otherwise kda_chunk_fwd's checks
+    assert ckpt(lib, cu=FAKE + 0x60000000, N=3, slots=5, ws_bytes=16) == WS
+
+
+def test_checkpoint_layout_helper():
+    # fixed-length: sequence n starts at n * floor(T / every)
+    bases, need = K.checkpoint_layout(64, 300, B=2)
+    assert bases == [(0, 4), (4, 4)] and need == 8
+    # packed: base(n) = floor(cu[n] / every) + n, count floor(len / every)
+    lens = [0, 5, 64, 130, 200, 17]
+    bases, need = K.checkpoint_layout(64, sum(lens), seqlens=lens)
+    cu = [0, 0, 5, 69, 199, 399]
+    assert bases == [(cu[n] // 64 + n, lens[n] // 64) for n in range(6)]
+    assert need == sum(lens) // 64 + 6
+    ends = [b + c for b, c in bases]
+    assert all(ends[n] <= bases[n + 1][0] for n in range(5)) and ends[-1] <= need

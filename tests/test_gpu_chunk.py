@@ -252,3 +252,88 @@ def test_fused_gate_f32_config():
     o_ref, S_ref, _ = oracle.forward(d["q"], d["k"], d["v"], d["beta"], oracle.gate(d["A"], d["z"]),
                                      S0=d["S0"])
     assert rel_err(o, o_ref) <= TOL["f32"] and rel_err(hT, S_ref) <= TOL["f32"]
+
+
+# ---- checkpoint emission (kda_chunk_fwd_checkpointed) ------------------------------------------
+def _ckpt_bases(d, every):
+    """First slot and count of each sequence's checkpoints, from the layout kda.h specifies."""
+    if d["cu_seqlens"] is None:
+        B, T = d["q"].shape[:2]
+        return [(n * (T // every), T // every) for n in range(B)]
+    cu = d["cu_seqlens"].numpy()
+    return [(int(cu[n]) // every + n, int(cu[n + 1] - cu[n]) // every) for n in range(len(cu) - 1)]
+
+
+def _check_checkpoints(d, every, tol, gated=False, units=None, label=""):
+    B, T, H, dk = d["q"].shape
+    dv = d["v"].shape[-1]
+    cu = d["cu_seqlens"].to(DEV) if d["cu_seqlens"] is not None else None
+    N = B if cu is None else cu.numel() - 1
+    h0 = d["S0"].to(DEV) if d["S0"] is not None else None
+    slots = (B * (T // every)) if cu is None else (T // every + N)
+    ck = torch.full((slots, H, dk, dv), float("nan"), dtype=torch.float32, device=DEV)
+    args = [d[x].to(DEV) for x in ("q", "k", "v", "beta")]
+    if gated:
+        gz = dict(A=d["A"].to(DEV), z=d["z"].to(DEV))
+        g = oracle_g(d)
+    else:
+        g = oracle_g(d)
+        gz = dict(g=g.to(DEV))
+    o, hT, ck = K.kda_chunk_fwd_checkpointed(*args, every, initial_state=h0, cu_seqlens=cu,
+                                             o_dtype=torch.float32, checkpoints=ck, **gz)
+    torch.cuda.synchronize()
+    # the prefill outputs are those of the plain entry points, bit for bit
+    if gated:
+        o2, h2 = K.kda_chunk_fwd_gated(*args, gz["A"], gz["z"], initial_state=h0, cu_seqlens=cu,
+                                       o_dtype=torch.float32)
+    else:
+        o2, h2 = K.kda_chunk_fwd(*args, gz["g"], initial_state=h0, cu_seqlens=cu, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(hT, h2)
+    # every mapped slot against the oracle's state at that boundary; the other slots untouched
+    bases = _ckpt_bases(d, every)
+    if units is None:
+        units = [(n, h) for n in range(N) for h in range(H)]
+    ref = oracle.forward_checkpoints(d["q"], d["k"], d["v"], d["beta"], g, every, units=units,
+                                     S0=d["S0"], cu_seqlens=d["cu_seqlens"].numpy() if cu is not None else None)
+    ck_host = ck.cpu()
+    worst = 0.0
+    for (n, h), states in ref.items():
+        base, count = bases[n]
+        assert len(states) == count
+        for j, S_j in enumerate(states):
+            worst = max(worst, rel_err(ck_host[base + j, h], S_j))
+    say(f"  {label} checkpoints: worst S err {worst:.2e}")
+    assert worst <= tol
+    mapped = set()
+    for base, count in bases:
+        mapped.update(range(base, base + count))
+    for s in range(slots):
+        if s not in mapped:
+            assert torch.isnan(ck_host[s]).all(), s
+
+
+@pytest.mark.parametrize("case", ["fixed", "varlen", "f32", "gated"])
+def test_checkpoints_parity(case):
+    """States stored every k tokens equal the oracle's states at those boundaries; o and the
+    final state equal the plain entry points' bit for bit; slots between packed sequences keep
+    their contents."""
+    if case == "fixed":
+        d, every, tol = prefill_case("prefill_bf16", B=2, H=2, T=300), 64, TOL["bf16"]
+    elif case == "varlen":
+        d, every, tol = prefill_case("prefill_varlen", seqlens=[0, 5, 64, 130, 200, 17, 256], H=3), 64, TOL["bf16"]
+    elif case == "f32":
+        d, every, tol = prefill_case("prefill_f32_small"), 64, TOL["f32"]
+    else:
+        d, every, tol = prefill_case("prefill_bf16", B=2, H=2, T=257), 128, TOL["bf16"]
+    say("checkpoints", case, every)
+    _check_checkpoints(d, every, tol, gated=(case == "gated"), label=case)
+
+
+def test_checkpoints_full_size_sampled():
+    """The bf16 prefill workload (B=4, H=16, T=4096) with a checkpoint every 512 tokens, fused
+    gate; four units checked at all eight boundaries."""
+    d = prefill_case("prefill_bf16")
+    say("checkpoints full size", d["cfg"])
+    _check_checkpoints(d, 512, TOL["bf16"], gated=True, units=[(0, 0), (1, 5), (2, 11), (3, 15)],
+                       label="full")
