@@ -142,8 +142,44 @@ def run_decode(args, dev, inputs, K, stream):
     dec_units = N * dcfg.H
     dec_gbs = dec_units * DECODE_BYTES_PER_UNIT / (dec_ms_step * 1e-3)
 
+    # speculative decoding on the same state: verify a 4-token draft (state read once, every
+    # token's output written), then commit 2 accepted tokens (state read and written once)
+    n_draft, n_acc = 4, 2
+    draft = [t[:n_draft].transpose(0, 1).contiguous() for t in (dq, dk_, dv_, db, dg)]
+    od4 = torch.empty((N, n_draft, dcfg.H, dcfg.dv), dtype=torch.bfloat16, device=dev)
+    acc = torch.full((N,), n_acc, dtype=torch.int32, device=dev)
+    K.kda_decode_verify(*draft, Sd, o=od4, stream=stream)
+    K.kda_decode_commit(*draft, Sd, acc, stream=stream)
+    torch.cuda.synchronize()
+    reps = 20
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        K.kda_decode_verify(*draft, Sd, o=od4, stream=stream)
+    ev[1].record(stream)
+    for _ in range(reps):
+        K.kda_decode_commit(*draft, Sd, acc, stream=stream)
+    ev[2].record(stream)
+    ev[2].synchronize()
+    ver_ms = ev[0].elapsed_time(ev[1]) / reps
+    com_ms = ev[1].elapsed_time(ev[2]) / reps
+    units = N * dcfg.H
+    state_b = dcfg.dk * dcfg.dv * 4
+    tok_in_b = 3 * dcfg.dk * 2 + dcfg.dv * 2 + 2            # q, k, g, v, beta (bf16)
+    ver_b = units * (state_b + n_draft * (tok_in_b + dcfg.dv * 2))
+    com_b = units * (2 * state_b + n_acc * tok_in_b)
+    spec = {"draft_tokens": n_draft, "accepted": n_acc,
+            "verify_ms": round(ver_ms, 4), "commit_ms": round(com_ms, 4),
+            "verify_gbs": round(ver_b / (ver_ms * 1e-3) / 1e9, 1),
+            "commit_gbs": round(com_b / (com_ms * 1e-3) / 1e9, 1),
+            "verify_frac_hbm": round(ver_b / (ver_ms * 1e-3) / HBM_PEAK, 4),
+            "commit_frac_hbm": round(com_b / (com_ms * 1e-3) / HBM_PEAK, 4),
+            "step_by_step_ms": round(n_draft * dec_ms_step, 4),
+            "note": "verify + commit against 4 kda_decode_step calls on state copies"}
+
     return {"seq_steps_per_s": round(N / (dec_ms_step * 1e-3), 1),
             "ms_per_step": round(dec_ms_step, 4),
+            "spec_decode": spec,
             "roofline": {"bound": "hbm", "achieved": round(dec_gbs / 1e9, 1),
                          "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                          "frac": round(dec_gbs / HBM_PEAK, 4),
@@ -180,7 +216,7 @@ def main():
 
     if args.mode == "decode":
         r = run_decode(args, dev, inputs, K, torch.cuda.current_stream())
-        log(f"decode: {r['ms_per_step']:.4f} ms/step")
+        log(f"decode: {r['ms_per_step']:.4f} ms/step; spec decode {r['spec_decode']}")
         return
 
     # ------------------------------------------------------------------ prefill workload

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 210;  // 0.2.1
+constexpr int kVersion = 220;  // 0.2.2
 
 bool valid_dtype(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
 int64_t esize(int dt) { return dt == KDA_F32 ? 4 : 2; }
@@ -198,6 +198,47 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* bet
     if (overlap(r_o, r_s)) return KDA_ERR_INVALID_ARGUMENT;
     return from_hip(kda::launch_decode(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype, N,
                                        H, dk, dv, scale, static_cast<hipStream_t>(stream)));
+}
+
+int kda_decode_verify(const void* q, const void* k, const void* v, const void* beta, int in_dtype,
+                      const void* g, int g_dtype, const float* state, void* o, int o_dtype,
+                      int32_t N, int32_t K, int32_t H, int32_t dk, int32_t dv, float scale,
+                      void* stream) {
+    if (!valid_dtype(in_dtype) || !valid_dtype(g_dtype) || !valid_dtype(o_dtype))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (N < 0 || K < 1 || H < 1 || dk < 1 || dv < 1 || !std::isfinite(scale))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_d(dk) || !supported_d(dv)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !beta || !g || !state || !o) return KDA_ERR_INVALID_ARGUMENT;
+    const int64_t rows = int64_t(N) * K * H;
+    const Range r_o = range(o, rows * dv * esize(o_dtype));
+    const Range others[] = {range(q, rows * dk * esize(in_dtype)), range(k, rows * dk * esize(in_dtype)),
+                            range(v, rows * dv * esize(in_dtype)), range(beta, rows * esize(in_dtype)),
+                            range(g, rows * dk * esize(g_dtype)), range(state, int64_t(N) * H * dk * dv * 4)};
+    for (const Range& x : others)
+        if (overlap(r_o, x)) return KDA_ERR_INVALID_ARGUMENT;
+    return from_hip(kda::launch_decode_verify(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype,
+                                              N, K, H, dk, dv, scale, static_cast<hipStream_t>(stream)));
+}
+
+int kda_decode_commit(const void* q, const void* k, const void* v, const void* beta, int in_dtype,
+                      const void* g, int g_dtype, float* state, const int32_t* accepted, int32_t N,
+                      int32_t K, int32_t H, int32_t dk, int32_t dv, void* stream) {
+    if (!valid_dtype(in_dtype) || !valid_dtype(g_dtype)) return KDA_ERR_INVALID_ARGUMENT;
+    if (N < 0 || K < 1 || H < 1 || dk < 1 || dv < 1) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_d(dk) || !supported_d(dv)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !beta || !g || !state || !accepted) return KDA_ERR_INVALID_ARGUMENT;
+    const int64_t rows = int64_t(N) * K * H;
+    const Range r_s = range(state, int64_t(N) * H * dk * dv * 4);
+    const Range others[] = {range(q, rows * dk * esize(in_dtype)), range(k, rows * dk * esize(in_dtype)),
+                            range(v, rows * dv * esize(in_dtype)), range(beta, rows * esize(in_dtype)),
+                            range(g, rows * dk * esize(g_dtype)), range(accepted, int64_t(N) * 4)};
+    for (const Range& x : others)
+        if (overlap(r_s, x)) return KDA_ERR_INVALID_ARGUMENT;
+    return from_hip(kda::launch_decode_commit(q, k, v, beta, in_dtype, g, g_dtype, state, accepted,
+                                              N, K, H, dk, dv, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

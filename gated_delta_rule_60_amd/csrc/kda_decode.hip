@@ -12,6 +12,10 @@
 //     S <- Diag(alpha) S + beta k u^T                     one write of S
 // (o follows from o = S_new^T q = S^T Diag(alpha) q + beta u (k . q).)
 //
+// Speculative decoding: decode_multi_kernel runs K draft tokens of a sequence on one read of the
+// state -- verify returns every token's output and leaves the state alone; commit replays the
+// accepted prefix (from the same token inputs) and writes the state once.
+//
 // Layout: one 256-lane workgroup per (sequence, head).  Lane t owns four consecutive state
 // columns (16-byte loads/stores) of d_k / (256 / (d_v / 4)) consecutive rows, so each row is
 // read by d_v/4 lanes as one contiguous segment.  Partial column sums meet in LDS.  The state
@@ -34,6 +38,91 @@ __device__ __forceinline__ void stream_store4(float* p, float4 x) {
     __builtin_nontemporal_store(y, reinterpret_cast<f32x4_t*>(p));
 }
 
+// Shared memory of one step.
+template <int DK, int DV>
+struct StepSmem {
+    static constexpr int CG = DV / 4, RG = 256 / CG;
+    float alpha[DK], ak[DK], aq[DK], k[DK];
+    float4 red_a[RG][CG];
+    float4 red_b[RG][CG];
+    float kq[4];
+};
+
+// One token of one (sequence, head) on the state held in registers s[] (rows rg*RPT + i, columns
+// 4cg .. 4cg+3).  tok indexes the token's [.., H, d] rows of q, k, g (times DK), v (times DV) and
+// beta; o (if not null) receives the token's output row.  With STORE each updated row also goes
+// to S as soon as it is formed (interleaving the stores with the update keeps the write stream
+// smooth).  Every lane of the workgroup calls it.
+template <int DK, int DV, int IDT, int GDT, int ODT, bool STORE>
+__device__ __forceinline__ void decode_token(float4 (&s)[DK / (256 / (DV / 4))], StepSmem<DK, DV>& sm,
+                                             const void* __restrict__ q, const void* __restrict__ k,
+                                             const void* __restrict__ v, const void* __restrict__ beta,
+                                             const void* __restrict__ g, int64_t tok,
+                                             void* __restrict__ o, float scale, float* __restrict__ S) {
+    constexpr int CG = DV / 4;    // lanes per state row
+    constexpr int RG = 256 / CG;  // row groups
+    constexpr int RPT = DK / RG;  // rows per lane
+    const int t = threadIdx.x;
+    const int cg = t % CG, rg = t / CG;
+
+    float kq = 0.0f;
+    if (t < DK) {
+        const float a = expf(load_as_f32<GDT>(g, tok * DK + t));
+        const float kk = load_as_f32<IDT>(k, tok * DK + t);
+        const float qq = load_as_f32<IDT>(q, tok * DK + t);
+        sm.alpha[t] = a;
+        sm.ak[t] = a * kk;
+        sm.aq[t] = a * qq;
+        sm.k[t] = kk;
+        kq = kk * qq;
+    }
+    // k . q over the first DK lanes (wavefront reduction, then one value per wave)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) kq += __shfl_xor(kq, off, 64);
+    if ((t & 63) == 0) sm.kq[t >> 6] = kq;
+    __syncthreads();
+
+    float4 pa = make_float4(0.f, 0.f, 0.f, 0.f), pb = pa;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg * RPT + i;
+        const float ak = sm.ak[r], aq = sm.aq[r];
+        pa.x += ak * s[i].x; pa.y += ak * s[i].y; pa.z += ak * s[i].z; pa.w += ak * s[i].w;
+        pb.x += aq * s[i].x; pb.y += aq * s[i].y; pb.z += aq * s[i].z; pb.w += aq * s[i].w;
+    }
+    sm.red_a[rg][cg] = pa;
+    sm.red_b[rg][cg] = pb;
+    __syncthreads();
+
+    float4 A4 = make_float4(0.f, 0.f, 0.f, 0.f), B4 = A4;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+        const float4 x = sm.red_a[r][cg], y = sm.red_b[r][cg];
+        A4.x += x.x; A4.y += x.y; A4.z += x.z; A4.w += x.w;
+        B4.x += y.x; B4.y += y.y; B4.z += y.z; B4.w += y.w;
+    }
+    const float kqs = sm.kq[0] + sm.kq[1] + sm.kq[2] + sm.kq[3];
+    const float bt = load_as_f32<IDT>(beta, tok);
+    const float4 vv = load4_as_f32<IDT>(v, tok * DV + 4 * cg);
+    const float4 u = make_float4(vv.x - A4.x, vv.y - A4.y, vv.z - A4.z, vv.w - A4.w);
+    if (o != nullptr && rg == 0) {
+        const float c = bt * kqs;
+        const float4 oo = make_float4(scale * (B4.x + c * u.x), scale * (B4.y + c * u.y),
+                                      scale * (B4.z + c * u.z), scale * (B4.w + c * u.w));
+        store4_from_f32<ODT>(o, tok * DV + 4 * cg, oo);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg * RPT + i;
+        const float al = sm.alpha[r], bk = bt * sm.k[r];
+        s[i].x = al * s[i].x + bk * u.x;
+        s[i].y = al * s[i].y + bk * u.y;
+        s[i].z = al * s[i].z + bk * u.z;
+        s[i].w = al * s[i].w + bk * u.w;
+        if constexpr (STORE) stream_store4(S + r * DV + 4 * cg, s[i]);
+    }
+}
+
 template <int DK, int DV, int IDT, int GDT, int ODT>
 __global__ void __launch_bounds__(256) decode_kernel(const void* __restrict__ q,
                                                      const void* __restrict__ k,
@@ -46,11 +135,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const void* __restrict__ q,
     constexpr int RG = 256 / CG;  // row groups
     constexpr int RPT = DK / RG;  // rows per lane
     static_assert(RPT >= 1 && RG * RPT == DK, "shape");
-
-    __shared__ float s_alpha[DK], s_ak[DK], s_aq[DK], s_k[DK];
-    __shared__ float4 s_red_a[RG][CG];
-    __shared__ float4 s_red_b[RG][CG];
-    __shared__ float s_kq[4];
+    __shared__ StepSmem<DK, DV> sm;
 
     const int64_t unit = blockIdx.x;  // sequence * H + head
     const int t = threadIdx.x;
@@ -62,63 +147,56 @@ __global__ void __launch_bounds__(256) decode_kernel(const void* __restrict__ q,
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         s[i] = stream_load4(S + (rg * RPT + i) * DV + 4 * cg);
+    decode_token<DK, DV, IDT, GDT, ODT, true>(s, sm, q, k, v, beta, g, unit, o, scale, S);
+}
 
-    float kq = 0.0f;
-    if (t < DK) {
-        const float a = expf(load_as_f32<GDT>(g, unit * DK + t));
-        const float kk = load_as_f32<IDT>(k, unit * DK + t);
-        const float qq = load_as_f32<IDT>(q, unit * DK + t);
-        s_alpha[t] = a;
-        s_ak[t] = a * kk;
-        s_aq[t] = a * qq;
-        s_k[t] = kk;
-        kq = kk * qq;
-    }
-    // k . q over the first DK lanes (wavefront reduction, then one value per wave)
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) kq += __shfl_xor(kq, off, 64);
-    if ((t & 63) == 0) s_kq[t >> 6] = kq;
-    __syncthreads();
+// Several tokens per sequence on one read of the state ([habr, § Как обслуживать два разных
+// кеша]: reading the recurrent state is the cost of a decode step).  Tokens are [N, K, H, d]:
+// token j of sequence n is row (n*K + j)*H + h.
+//   COMMIT = false (verify): all K tokens, o for each, the state is not written.
+//   COMMIT = true: the first accepted[n] tokens (clamped to [0, K]), no o, the state written once.
+template <int DK, int DV, int IDT, int GDT, int ODT, bool COMMIT>
+__global__ void __launch_bounds__(256) decode_multi_kernel(const void* __restrict__ q,
+                                                           const void* __restrict__ k,
+                                                           const void* __restrict__ v,
+                                                           const void* __restrict__ beta,
+                                                           const void* __restrict__ g,
+                                                           float* __restrict__ state,
+                                                           void* __restrict__ o, float scale,
+                                                           int32_t K, int32_t H,
+                                                           const int32_t* __restrict__ accepted) {
+    constexpr int CG = DV / 4;
+    constexpr int RG = 256 / CG;
+    constexpr int RPT = DK / RG;
+    static_assert(RPT >= 1 && RG * RPT == DK, "shape");
+    __shared__ StepSmem<DK, DV> sm;
 
-    float4 pa = make_float4(0.f, 0.f, 0.f, 0.f), pb = pa;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg * RPT + i;
-        const float ak = s_ak[r], aq = s_aq[r];
-        pa.x += ak * s[i].x; pa.y += ak * s[i].y; pa.z += ak * s[i].z; pa.w += ak * s[i].w;
-        pb.x += aq * s[i].x; pb.y += aq * s[i].y; pb.z += aq * s[i].z; pb.w += aq * s[i].w;
-    }
-    s_red_a[rg][cg] = pa;
-    s_red_b[rg][cg] = pb;
-    __syncthreads();
+    const int64_t unit = blockIdx.x;  // sequence * H + head
+    const int64_t n = unit / H, h = unit % H;
+    const int t = threadIdx.x;
+    const int cg = t % CG, rg = t / CG;
+    float* S = state + unit * (DK * DV);
 
-    float4 A4 = make_float4(0.f, 0.f, 0.f, 0.f), B4 = A4;
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-        const float4 x = s_red_a[r][cg], y = s_red_b[r][cg];
-        A4.x += x.x; A4.y += x.y; A4.z += x.z; A4.w += x.w;
-        B4.x += y.x; B4.y += y.y; B4.z += y.z; B4.w += y.w;
+    int32_t steps = K;
+    if constexpr (COMMIT) {
+        const int32_t a = accepted[n];
+        steps = a < 0 ? 0 : (a > K ? K : a);
+        if (steps == 0) return;                  // nothing accepted: the state stays as it is
     }
-    const float kqs = s_kq[0] + s_kq[1] + s_kq[2] + s_kq[3];
-    const float bt = load_as_f32<IDT>(beta, unit);
-    const float4 vv = load4_as_f32<IDT>(v, unit * DV + 4 * cg);
-    const float4 u = make_float4(vv.x - A4.x, vv.y - A4.y, vv.z - A4.z, vv.w - A4.w);
-    if (rg == 0) {
-        const float c = bt * kqs;
-        const float4 oo = make_float4(scale * (B4.x + c * u.x), scale * (B4.y + c * u.y),
-                                      scale * (B4.z + c * u.z), scale * (B4.w + c * u.w));
-        store4_from_f32<ODT>(o, unit * DV + 4 * cg, oo);
-    }
+    float4 s[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg * RPT + i;
-        const float al = s_alpha[r], bk = bt * s_k[r];
-        float4 x = s[i];
-        x.x = al * x.x + bk * u.x;
-        x.y = al * x.y + bk * u.y;
-        x.z = al * x.z + bk * u.z;
-        x.w = al * x.w + bk * u.w;
-        stream_store4(S + r * DV + 4 * cg, x);
+    for (int i = 0; i < RPT; ++i)
+        s[i] = stream_load4(S + (rg * RPT + i) * DV + 4 * cg);
+    const int32_t last = COMMIT ? steps - 1 : steps;   // commit: the last token also stores S
+    for (int32_t j = 0; j < last; ++j) {
+        if (j > 0) __syncthreads();              // the previous token's shared values are read
+        decode_token<DK, DV, IDT, GDT, ODT, false>(s, sm, q, k, v, beta, g, (n * K + j) * H + h,
+                                                   COMMIT ? nullptr : o, scale, S);
+    }
+    if constexpr (COMMIT) {
+        if (last > 0) __syncthreads();
+        decode_token<DK, DV, IDT, GDT, ODT, true>(s, sm, q, k, v, beta, g, (n * K + last) * H + h,
+                                                  nullptr, scale, S);
     }
 }
 
@@ -149,6 +227,61 @@ static hipError_t dispatch_dtypes(const void* q, const void* k, const void* v, c
     KDA_DEC(KDA_F32, KDA_F32, KDA_F32)
 #undef KDA_DEC
     return hipErrorInvalidValue;
+}
+
+template <int DK, int DV, bool COMMIT>
+static hipError_t dispatch_multi(const void* q, const void* k, const void* v, const void* beta,
+                                 int idt, const void* g, int gdt, float* state, void* o, int odt,
+                                 int32_t N, int32_t K, int32_t H, float scale,
+                                 const int32_t* accepted, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(N) * H));
+#define KDA_DM(I, G, O)                                                                        \
+    if (idt == I && gdt == G && odt == O) {                                                    \
+        hipLaunchKernelGGL((decode_multi_kernel<DK, DV, I, G, O, COMMIT>), grid, dim3(256), 0,  \
+                           st, q, k, v, beta, g, state, o, scale, K, H, accepted);             \
+        return hipGetLastError();                                                              \
+    }
+    KDA_DM(KDA_BF16, KDA_BF16, KDA_BF16)
+    KDA_DM(KDA_BF16, KDA_BF16, KDA_F32)
+    KDA_DM(KDA_BF16, KDA_F32, KDA_BF16)
+    KDA_DM(KDA_BF16, KDA_F32, KDA_F32)
+    KDA_DM(KDA_F32, KDA_BF16, KDA_BF16)
+    KDA_DM(KDA_F32, KDA_BF16, KDA_F32)
+    KDA_DM(KDA_F32, KDA_F32, KDA_BF16)
+    KDA_DM(KDA_F32, KDA_F32, KDA_F32)
+#undef KDA_DM
+    return hipErrorInvalidValue;
+}
+
+template <bool COMMIT>
+static hipError_t launch_multi(const void* q, const void* k, const void* v, const void* beta,
+                               int in_dtype, const void* g, int g_dtype, float* state, void* o,
+                               int o_dtype, int32_t N, int32_t K, int32_t H, int32_t dk, int32_t dv,
+                               float scale, const int32_t* accepted, hipStream_t s) {
+    if (dk == 128 && dv == 128)
+        return dispatch_multi<128, 128, COMMIT>(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype, N, K, H, scale, accepted, s);
+    if (dk == 128 && dv == 64)
+        return dispatch_multi<128, 64, COMMIT>(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype, N, K, H, scale, accepted, s);
+    if (dk == 64 && dv == 128)
+        return dispatch_multi<64, 128, COMMIT>(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype, N, K, H, scale, accepted, s);
+    return dispatch_multi<64, 64, COMMIT>(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype, N, K, H, scale, accepted, s);
+}
+
+hipError_t launch_decode_verify(const void* q, const void* k, const void* v, const void* beta,
+                                int in_dtype, const void* g, int g_dtype, const float* state,
+                                void* o, int o_dtype, int32_t N, int32_t K, int32_t H, int32_t dk,
+                                int32_t dv, float scale, hipStream_t stream) {
+    return launch_multi<false>(q, k, v, beta, in_dtype, g, g_dtype, const_cast<float*>(state), o,
+                               o_dtype, N, K, H, dk, dv, scale, nullptr, stream);
+}
+
+hipError_t launch_decode_commit(const void* q, const void* k, const void* v, const void* beta,
+                                int in_dtype, const void* g, int g_dtype, float* state,
+                                const int32_t* accepted, int32_t N, int32_t K, int32_t H,
+                                int32_t dk, int32_t dv, hipStream_t stream) {
+    // o is not written in commit mode; its dtype only selects an instantiation
+    return launch_multi<true>(q, k, v, beta, in_dtype, g, g_dtype, state, nullptr, KDA_F32, N, K,
+                              H, dk, dv, 1.0f, accepted, stream);
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* beta,

@@ -15,6 +15,17 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
                          int o_dtype, int32_t N, int32_t H, int32_t dk, int32_t dv, float scale,
                          hipStream_t stream);
 
+// Several tokens per sequence ([N, K, H, d] inputs) on one read of the state: verify writes
+// o [N, K, H, dv] and leaves the state; commit applies the first accepted[n] tokens in place.
+hipError_t launch_decode_verify(const void* q, const void* k, const void* v, const void* beta,
+                                int in_dtype, const void* g, int g_dtype, const float* state,
+                                void* o, int o_dtype, int32_t N, int32_t K, int32_t H, int32_t dk,
+                                int32_t dv, float scale, hipStream_t stream);
+hipError_t launch_decode_commit(const void* q, const void* k, const void* v, const void* beta,
+                                int in_dtype, const void* g, int g_dtype, float* state,
+                                const int32_t* accepted, int32_t N, int32_t K, int32_t H,
+                                int32_t dk, int32_t dv, hipStream_t stream);
+
 struct ChunkArgs {
     const void* q;
     const void* k;

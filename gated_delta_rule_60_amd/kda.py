@@ -62,13 +62,20 @@ def load_library(path: Optional[str] = None):
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
                                     ctypes.c_int, i32, i32, i32, i32, f32, vp]
     lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_verify.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
+                                      ctypes.c_int, i32, i32, i32, i32, i32, f32, vp]
+    lib.kda_decode_verify.restype = ctypes.c_int
+    lib.kda_decode_commit.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
+                                      i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_commit.restype = ctypes.c_int
     if path == lib_path():
         _lib = lib
     return lib
 
 
 EXPORTED = ["kda_status_string", "kda_version", "kda_gate", "kda_chunk_fwd_workspace_size",
-            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_checkpointed", "kda_decode_step"]
+            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_checkpointed", "kda_decode_step",
+            "kda_decode_verify", "kda_decode_commit"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -227,3 +234,30 @@ def kda_decode_step(q, k, v, beta, g, state, o=None, o_dtype=None, scale: float 
         _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(g), _dt(g), _ptr(state), _ptr(o),
         _dt(o), N, H, dk, dv, float(scale), _stream(stream)))
     return o
+
+
+def kda_decode_verify(q, k, v, beta, g, state, o=None, o_dtype=None, scale: float = 1.0,
+                      stream=None):
+    """K draft tokens per sequence from a read-only state: q, k, g [N, K, H, dk]; v [N, K, H, dv];
+    beta [N, K, H]; state [N, H, dk, dv] fp32 (not modified).  Returns o [N, K, H, dv]."""
+    N, Kd, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, Kd, H, dv), dtype=o_dtype or q.dtype, device=q.device)
+    _check("kda_decode_verify", load_library().kda_decode_verify(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(g), _dt(g), _ptr(state), _ptr(o),
+        _dt(o), N, Kd, H, dk, dv, float(scale), _stream(stream)))
+    return o
+
+
+def kda_decode_commit(q, k, v, beta, g, state, accepted, stream=None):
+    """Advance each state in place by its first accepted[n] draft tokens (device int32 [N]);
+    inputs as kda_decode_verify.  Returns state."""
+    N, Kd, H, dk = q.shape
+    dv = v.shape[-1]
+    if accepted.dtype != torch.int32:
+        raise TypeError("accepted must be int32")
+    _check("kda_decode_commit", load_library().kda_decode_commit(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(g), _dt(g), _ptr(state),
+        _ptr(accepted), N, Kd, H, dk, dv, _stream(stream)))
+    return state

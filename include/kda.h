@@ -183,6 +183,37 @@ int kda_decode_step(const void *q, const void *k, const void *v, const void *bet
                     const void *g, int g_dtype, float *state, void *o, int o_dtype, int32_t N,
                     int32_t H, int32_t dk, int32_t dv, float scale, void *stream);
 
+/*
+ * Speculative decoding ([habr, § Как обслуживать два разных кеша]: no copy of the state is kept
+ * per draft token; the accepted stretch is recomputed on chip from the token inputs, which is
+ * cheaper than reading the large state again and again).  A draft of K tokens per sequence is
+ * laid out like a prefill batch: q, k, g [N, K, H, d_k]; v [N, K, H, d_v]; beta [N, K, H]
+ * (token j of sequence n is row (n*K + j)*H + h).
+ *
+ * kda_decode_verify -- runs all K draft tokens of every sequence from `state` (read only, never
+ * written) and writes each token's output o [N, K, H, d_v] (o_dtype): the outputs K calls of
+ * kda_decode_step would give, with one read of the state instead of K reads and writes.
+ * o must not overlap any other argument.
+ *
+ * kda_decode_commit -- once the draft is judged, advances each state in place by its accepted
+ * tokens: accepted is a device int32 [N] array of counts (values outside [0, K] are clamped;
+ * 0 leaves the state untouched).  The same inputs are passed again; no o is produced.  The new
+ * state equals accepted[n] successive kda_decode_step calls bit for bit.  The state must not
+ * overlap any input or `accepted`.
+ *
+ * Both: dtypes, dimensions (d_k, d_v in {64, 128}), N >= 0 (0 is a no-op), K >= 1, H >= 1 and the
+ * error behaviour as in kda_decode_step; the caller owns every buffer; work is enqueued on
+ * `stream`.
+ */
+int kda_decode_verify(const void *q, const void *k, const void *v, const void *beta, int in_dtype,
+                      const void *g, int g_dtype, const float *state, void *o, int o_dtype,
+                      int32_t N, int32_t K, int32_t H, int32_t dk, int32_t dv, float scale,
+                      void *stream);
+
+int kda_decode_commit(const void *q, const void *k, const void *v, const void *beta, int in_dtype,
+                      const void *g, int g_dtype, float *state, const int32_t *accepted, int32_t N,
+                      int32_t K, int32_t H, int32_t dk, int32_t dv, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

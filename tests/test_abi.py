@@ -188,3 +188,38 @@ def test_checkpoint_layout_helper():
     assert need == sum(lens) // 64 + 6
     ends = [b + c for b, c in bases]
     assert all(ends[n] <= bases[n + 1][0] for n in range(5)) and ends[-1] <= need
+
+
+def verify(lib, q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, beta=FAKE + 0x30000000,
+           in_dt=1, g=FAKE + 0x40000000, g_dt=1, S=FAKE + 0x70000000, o=FAKE + 0x50000000,
+           o_dt=1, N=4, Kd=3, H=2, dk=128, dv=128, scale=1.0):
+    return lib.kda_decode_verify(P(q), P(k), P(v), P(beta), in_dt, P(g), g_dt, P(S), P(o), o_dt,
+                                 N, Kd, H, dk, dv, scale, None)
+
+
+def commit(lib, q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, beta=FAKE + 0x30000000,
+           in_dt=1, g=FAKE + 0x40000000, g_dt=1, S=FAKE + 0x70000000, acc=FAKE + 0x60000000,
+           N=4, Kd=3, H=2, dk=128, dv=128):
+    return lib.kda_decode_commit(P(q), P(k), P(v), P(beta), in_dt, P(g), g_dt, P(S), P(acc), N, Kd,
+                                 H, dk, dv, None)
+
+
+def test_decode_verify_commit_reject(lib):
+    assert verify(lib, Kd=0) == INV
+    assert verify(lib, N=-1) == INV
+    assert verify(lib, H=0) == INV
+    assert verify(lib, in_dt=5) == INV
+    assert verify(lib, o_dt=3) == INV
+    assert verify(lib, scale=float("inf")) == INV
+    assert verify(lib, dk=96) == UNS
+    assert verify(lib, S=0) == INV
+    assert verify(lib, o=0) == INV
+    assert verify(lib, o=FAKE + 0x100) == INV              # o overlaps q
+    assert verify(lib, o=FAKE + 0x70000000 + 64) == INV    # o overlaps the state
+    assert verify(lib, N=0, q=0, o=0) == 0                 # nothing to do
+    assert commit(lib, Kd=0) == INV
+    assert commit(lib, acc=0) == INV
+    assert commit(lib, dv=32) == UNS
+    assert commit(lib, S=FAKE + 0x40000000 + 64) == INV    # state overlaps g
+    assert commit(lib, acc=FAKE + 0x70000000 + 128) == INV  # accepted inside the state
+    assert commit(lib, N=0, q=0, S=0) == 0
