@@ -494,7 +494,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
 // s_waitcnt immediate for "vmcnt <= n", other counters unconstrained.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
-template <int DK, int IDT, int ODT, bool PRECISE, int NW>
+template <int DK, int IDT, int ODT, bool PRECISE, int NW, bool CKPT>
 __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, int32_t n_vblk,
                                                                  int64_t nslots, const uint8_t* ws) {
     using R = Rec<DK, PRECISE>;
@@ -554,14 +554,16 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     f32x4 S[CT];
     const int64_t sbase = unit * DK * DV;
 
-    // Checkpoints: the state after every ckpt_every tokens of the sequence goes to slot
+    // Checkpoints (CKPT): the state after every ckpt_every tokens of the sequence goes to slot
     // ck_base + j - 1 (j = 1, 2, ...): ck_base = n * floor(T / every) for fixed-length batches,
     // floor(cu[n] / every) + n for packed ones (disjoint for the same reason as the block slots).
-    const int64_t ck_every = p.ckpt ? p.ckpt_every : 1;
-    const int64_t ck_base = p.cu ? static_cast<int64_t>(p.cu[n]) / ck_every + n
-                                 : static_cast<int64_t>(n) * (p.T / ck_every);
+    const int64_t ck_every = CKPT ? p.ckpt_every : 1;
+    const int64_t ck_base = !CKPT ? 0
+                            : p.cu ? static_cast<int64_t>(p.cu[n]) / ck_every + n
+                                   : static_cast<int64_t>(n) * (p.T / ck_every);
     auto checkpoint = [&](int64_t done) {          // `done` tokens of the sequence processed
-        if (p.ckpt == nullptr || done > len || done % ck_every != 0) return;
+        if constexpr (!CKPT) return;
+        if (done > len || done % ck_every != 0) return;
         const int64_t slot = ck_base + done / ck_every - 1;
         if (slot >= p.ckpt_slots) return;
         float* dst = p.ckpt + (slot * H + h) * DK * DV;
@@ -821,9 +823,13 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     const int32_t n_vblk = a.dv / (16 * NW);
     const int64_t units = static_cast<int64_t>(a.n_seqs) * a.H;
     const int64_t groups = (units + 7) / 8;
-    hipLaunchKernelGGL((chunk_state_kernel<DK, IDT, ODT, PRECISE, NW>),
-                       dim3(static_cast<unsigned>(groups * 8 * n_vblk)), dim3(64 * NW), 0, stream, a, n_vblk,
-                       nslots, static_cast<const uint8_t*>(ws));
+    const dim3 grid(static_cast<unsigned>(groups * 8 * n_vblk));
+    if (a.ckpt)
+        hipLaunchKernelGGL((chunk_state_kernel<DK, IDT, ODT, PRECISE, NW, true>), grid, dim3(64 * NW), 0,
+                           stream, a, n_vblk, nslots, static_cast<const uint8_t*>(ws));
+    else
+        hipLaunchKernelGGL((chunk_state_kernel<DK, IDT, ODT, PRECISE, NW, false>), grid, dim3(64 * NW), 0,
+                           stream, a, n_vblk, nslots, static_cast<const uint8_t*>(ws));
     return hipGetLastError();
 }
 
