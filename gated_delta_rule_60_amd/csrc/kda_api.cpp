@@ -67,7 +67,7 @@ size_t kda_chunk_fwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_
     if (n_seqs < 1 || total_tokens < 0 || H < 1 || !supported_d(dk) || !supported_d(dv) ||
         chunk != 64 || !valid_dtype(in_dtype))
         return 0;
-    return kda::chunk_workspace_bytes(n_seqs, total_tokens, H, dk, in_dtype);
+    return kda::chunk_workspace_bytes(n_seqs, total_tokens, H, dk, dv, in_dtype);
 }
 
 }  // extern "C"
@@ -94,7 +94,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* beta
     const int64_t ntok = int64_t(B) * T;
     if (ntok > 0 && (!q || !k || !v || !beta || !g || !o || (gated && !gate_A)))
         return KDA_ERR_INVALID_ARGUMENT;
-    const size_t need = kda::chunk_workspace_bytes(n_seqs, ntok, H, dk, in_dtype);
+    const size_t need = kda::chunk_workspace_bytes(n_seqs, ntok, H, dk, dv, in_dtype);
     if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE;
 
     const int64_t state_bytes = int64_t(n_seqs) * H * dk * dv * 4;

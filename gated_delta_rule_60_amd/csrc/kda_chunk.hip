@@ -494,9 +494,55 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
 // s_waitcnt immediate for "vmcnt <= n", other counters unconstrained.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
-template <int DK, int IDT, int ODT, bool PRECISE, int NW, bool CKPT>
+// ---- segments of long sequences ---------------------------------------------------------------
+// A sequence longer than SEG_TOK tokens is cut into segments of SEG_TOK tokens [bagrov § Уровень
+// графического ускорителя: the long-context scheduler].  The state after a segment is an affine
+// map of the state before it, S_out = M S_in + B (M: d_k x d_k, B: d_k x d_v), so:
+//   pass 1: segment 0 runs from the initial state (output included) and every middle segment
+//           computes its pair (M, B) -- the same state recurrence on columns started at the
+//           identity with V = 0, and on columns started at zero -- all segments in parallel;
+//   scan  : S_start(s + 1) = M_s S_start(s) + B_s along each sequence (column blocks apart);
+//   pass 2: every later segment runs from its start state, output included.
+// Segment slots: n * max(1, ceil(T / SEG_TOK)) for fixed-length batches, floor(cu[n] / SEG_TOK) + n
+// for packed ones; per (slot, head) the workspace holds S_start, M and B in fp32.
+constexpr int64_t SEG_TOK = 8192;
+
+struct SegArgs {
+    float* S;            // [slots, H, d_k, d_v] segment start states
+    float* M;            // [slots, H, d_k, d_k]
+    float* B;            // [slots, H, d_k, d_v]
+    int64_t slots;
+    int32_t n_vblk_m;    // column blocks of M (d_k columns)
+};
+
+__device__ __forceinline__ int64_t seg_count(int64_t len) {
+    return len <= 0 ? 1 : (len + SEG_TOK - 1) / SEG_TOK;   // an empty sequence still has one
+}
+
+// Segment slot -> sequence n and segment s within it; false for slots no segment maps to.
+__device__ __forceinline__ bool locate_seg(const ChunkArgs& p, int64_t slot, int& n, int64_t& s) {
+    if (p.cu) {
+        int lo = 0, hi = p.n_seqs - 1;
+        while (lo < hi) {                 // largest n with base(n) <= slot
+            const int mid = (lo + hi + 1) >> 1;
+            const int64_t base = static_cast<int64_t>(p.cu[mid]) / SEG_TOK + mid;
+            if (base <= slot) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
+        s = slot - (static_cast<int64_t>(p.cu[n]) / SEG_TOK + n);
+        return s >= 0 && s < seg_count(static_cast<int64_t>(p.cu[n + 1]) - p.cu[n]);
+    }
+    const int64_t per = seg_count(p.T);
+    n = static_cast<int>(slot / per);
+    s = slot % per;
+    return n < p.n_seqs;
+}
+
+// MODE 0: whole sequences.  MODE 1: segment pass 1.  MODE 2: segment pass 2.
+template <int DK, int IDT, int ODT, bool PRECISE, int NW, bool CKPT, int MODE>
 __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, int32_t n_vblk,
-                                                                 int64_t nslots, const uint8_t* ws) {
+                                                                 int64_t nslots, const uint8_t* ws,
+                                                                 SegArgs sg) {
     using R = Rec<DK, PRECISE>;
     constexpr int KS = DK / 32;
     constexpr int CT = DK / 16;
@@ -525,17 +571,24 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     const int ln = lane & 15, lq = lane >> 4;
 
     // Workgroup -> (unit, column block).  The column blocks of one unit sit 8 workgroup ids
-    // apart so they land on the same XCD and share its L2 for the unit's records.
-    const int64_t units = static_cast<int64_t>(p.n_seqs) * p.H;
+    // apart so they land on the same XCD and share its L2 for the unit's records.  A unit is a
+    // (sequence, head), or a (segment slot, head) in the segment passes; pass 1 puts the M column
+    // blocks first.
+    const int64_t H = p.H;
+    const int64_t units = (MODE == 0 ? static_cast<int64_t>(p.n_seqs) : sg.slots) * H;
+    const int nvx = MODE == 1 ? sg.n_vblk_m + n_vblk : n_vblk;
     const int64_t bid = blockIdx.x;
-    const int64_t grp = bid / (8 * n_vblk), remv = bid % (8 * n_vblk);
-    const int vb = static_cast<int>(remv / 8);
+    const int64_t grp = bid / (8 * nvx), remv = bid % (8 * nvx);
+    int vb = static_cast<int>(remv / 8);
     const int64_t unit = grp * 8 + remv % 8;
     if (unit >= units) return;
-    const int n = static_cast<int>(unit / p.H), h = static_cast<int>(unit % p.H);
+    const int h = static_cast<int>(unit % H);
+    int n = static_cast<int>(unit / H);
+    int64_t seg = 0;
+    if constexpr (MODE != 0) {
+        if (!locate_seg(p, unit / H, n, seg)) return;
+    }
     const int DV = p.dv;
-    const int n0 = vb * BVW + wave * 16;               // this wave's first state column
-    const int64_t H = p.H;
     const int32_t vstride = static_cast<int32_t>(H) * DV;
 
     int64_t bos, len, base;
@@ -550,9 +603,50 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     }
     const uint8_t* recs = ws + (static_cast<int64_t>(h) * nslots + base) * R::BYTES;
 
+    // What this workgroup does: the chunks it runs, where its state starts and ends, and whether
+    // it reads V and writes o.  A pair column block (role M) starts from the identity with V = 0.
+    const int64_t nchunks_all = (len + CHT - 1) / CHT;
+    int64_t c_begin = 0, c_end = nchunks_all;
+    const int64_t useq = static_cast<int64_t>(n) * H + h;           // (sequence, head)
+    const float* init = p.h0 ? p.h0 + useq * DK * DV : nullptr;       // nullptr: zeros
+    float* fin = p.hT ? p.hT + useq * DK * DV : nullptr;              // nullptr: not stored
+    int ldst = DV;                                                     // row stride of init / fin
+    bool ident = false, use_v = true, emit_o = true;
+    if constexpr (MODE != 0) {
+        constexpr int64_t SEGC = SEG_TOK / CHT;
+        const int64_t nseg = seg_count(len), slot = unit / H;
+        const int64_t us = slot * H + h;                                // (segment slot, head)
+        c_begin = seg * SEGC;
+        c_end = c_begin + SEGC < nchunks_all ? c_begin + SEGC : nchunks_all;
+        if (MODE == 1) {
+            if (seg == 0) {
+                if (vb >= n_vblk) return;
+                if (nseg > 1) fin = sg.S + (us + H) * DK * DV;         // start of segment 1
+            } else if (seg + 1 < nseg) {
+                init = nullptr;
+                emit_o = false;
+                if (vb < sg.n_vblk_m) {
+                    ident = true;
+                    use_v = false;
+                    fin = sg.M + us * DK * DK;
+                    ldst = DK;
+                } else {
+                    vb -= sg.n_vblk_m;
+                    fin = sg.B + us * DK * DV;
+                }
+            } else {
+                return;                                                // the last segment: pass 2
+            }
+        } else {
+            if (seg == 0) return;                                      // ran in pass 1
+            init = sg.S + us * DK * DV;
+            if (seg + 1 < nseg) fin = nullptr;                         // its end state is known
+        }
+    }
+    const int n0 = vb * BVW + wave * 16;               // this wave's first state column
+
     // state tiles: lane (ln, lq) of tile i holds S[16i + 4lq + r][n0 + ln]
     f32x4 S[CT];
-    const int64_t sbase = unit * DK * DV;
 
     // Checkpoints (CKPT): the state after every ckpt_every tokens of the sequence goes to slot
     // ck_base + j - 1 (j = 1, 2, ...): ck_base = n * floor(T / every) for fixed-length batches,
@@ -563,7 +657,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                                    : static_cast<int64_t>(n) * (p.T / ck_every);
     auto checkpoint = [&](int64_t done) {          // `done` tokens of the sequence processed
         if constexpr (!CKPT) return;
-        if (done > len || done % ck_every != 0) return;
+        if (!emit_o || done > len || done % ck_every != 0) return;
         const int64_t slot = ck_base + done / ck_every - 1;
         if (slot >= p.ckpt_slots) return;
         float* dst = p.ckpt + (slot * H + h) * DK * DV;
@@ -575,13 +669,15 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     {
         // an absent initial state is an empty range: every load reads 0
         const __amdgpu_buffer_rsrc_t h0r =
-            make_rsrc(p.h0 ? p.h0 + sbase : nullptr, p.h0 ? static_cast<uint32_t>(DK * DV * 4) : 0u);
+            make_rsrc(init, init ? static_cast<uint32_t>(DK * ldst * 4) : 0u);
 #pragma unroll
         for (int i = 0; i < CT; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 4; ++r) {
                 S[i][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    h0r, ((16 * i + 4 * lq + r) * DV + n0 + ln) * 4, 0, 0));
+                    h0r, ((16 * i + 4 * lq + r) * ldst + n0 + ln) * 4, 0, 0));
+                if (ident) S[i][r] = (16 * i + 4 * lq + r == n0 + ln) ? 1.f : 0.f;
+            }
     }
 
     auto tokens_in = [&](int64_t c) -> int {            // tokens of chunk c (0 past the end)
@@ -601,7 +697,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
             make_rsrc(nt > 0 ? recs + c * NB * R::BYTES : ws, static_cast<uint32_t>(nbk * R::BYTES));
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(
             nt > 0 ? static_cast<const uint8_t*>(p.v) + ((bos + c * CHT) * H + h) * DV * ESZ : p.v,
-            static_cast<uint32_t>(nt * vstride * ESZ));
+            use_v ? static_cast<uint32_t>(nt * vstride * ESZ) : 0u);
         const int i0 = slice * NITEM / NSLICE, i1 = (slice + 1) * NITEM / NSLICE;
 #pragma unroll
         for (int it = 0; it < NITEM; ++it) {
@@ -628,7 +724,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
         // o rows of this chunk and head; rows past the chunk's tokens fall outside the range
         const __amdgpu_buffer_rsrc_t orr =
             make_rsrc(static_cast<char*>(p.o) + ((bos + c * CHT) * H + h) * DV * OSZ,
-                      static_cast<uint32_t>(nt * vstride * OSZ));
+                      emit_o ? static_cast<uint32_t>(nt * vstride * OSZ) : 0u);
         // The Kt / Qt fragments of block b + 1 are read from LDS while block b computes (they
         // are needed first thing in a block); the rest of a block's operands are read at its
         // start and consumed later in it.
@@ -760,21 +856,20 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     // waits for those transfers -- the o stores of the chunk's last two blocks (4 each) may stay
     // in flight, every load is older -- and meets the other waves at the barrier.
     constexpr int WAIT_LOADS = vmcnt_imm(8);
-    const int64_t nchunks = (len + CHT - 1) / CHT;
 #pragma unroll
-    for (int sl = 0; sl < NSLICE; ++sl) prefetch_slice(bufA, 0, sl);
+    for (int sl = 0; sl < NSLICE; ++sl) prefetch_slice(bufA, c_begin, sl);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     // (A checkpoint's stores go out before the next chunk's transfers, so they are older than
     // every load the waits above count on.)
-    for (int64_t ci = 0; ci < nchunks; ci += 2) {
+    for (int64_t ci = c_begin; ci < c_end; ci += 2) {
         __builtin_amdgcn_sched_barrier(0);
         run(bufA, ci, bufB);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WAIT_LOADS);
         __syncthreads();
         checkpoint((ci + 1) * CHT);
-        if (ci + 1 >= nchunks) break;
+        if (ci + 1 >= c_end) break;
         __builtin_amdgcn_sched_barrier(0);
         run(bufB, ci + 1, bufA);
         __builtin_amdgcn_sched_barrier(0);
@@ -783,12 +878,67 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
         checkpoint((ci + 2) * CHT);
     }
 
-    if (p.hT) {
+    if (fin) {
 #pragma unroll
         for (int i = 0; i < CT; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                p.hT[sbase + static_cast<int64_t>(16 * i + 4 * lq + r) * DV + n0 + ln] = S[i][r];
+                fin[static_cast<int64_t>(16 * i + 4 * lq + r) * ldst + n0 + ln] = S[i][r];
+    }
+}
+
+// Segment scan: one workgroup per (sequence, head, 16 state columns) walks the sequence's
+// segments, S_start(s + 1) = M_s S_start(s) + B_s for s = 1 .. nseg - 2, in fp32.  The column
+// blocks are independent (M acts on the rows), so they run apart.
+template <int DK>
+__global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) {
+    __shared__ float sM[DK][DK + 1];
+    __shared__ float sS[DK][16];
+    const int DV = p.dv, ncb = DV / 16;
+    const int64_t H = p.H;
+    const int cb = static_cast<int>(blockIdx.x % ncb);
+    const int64_t useq = blockIdx.x / ncb;
+    const int n = static_cast<int>(useq / H), h = static_cast<int>(useq % H);
+    int64_t len, slot0;
+    if (p.cu) {
+        len = static_cast<int64_t>(p.cu[n + 1]) - p.cu[n];
+        slot0 = static_cast<int64_t>(p.cu[n]) / SEG_TOK + n;
+    } else {
+        len = p.T;
+        slot0 = static_cast<int64_t>(n) * seg_count(p.T);
+    }
+    const int64_t nseg = seg_count(len);
+    if (nseg < 3) return;                             // no middle segment: nothing to combine
+    const int t = threadIdx.x;
+    const int i = t >> 1, j0 = (t & 1) * 8;         // this thread: row i, columns j0 .. j0+7
+    const float* S1 = sg.S + ((slot0 + 1) * H + h) * DK * DV + cb * 16;
+    for (int e = t; e < DK * 16; e += 256) sS[e >> 4][e & 15] = S1[(e >> 4) * DV + (e & 15)];
+    for (int64_t s = 1; s + 1 < nseg; ++s) {
+        const int64_t us = (slot0 + s) * H + h;
+        const float* M = sg.M + us * DK * DK;
+        const float* Bm = sg.B + us * DK * DV + cb * 16;
+        __syncthreads();                             // sS written, the previous sM reads done
+        for (int e = t; e < DK * DK; e += 256) sM[e / DK][e % DK] = M[e];
+        __syncthreads();
+        float acc[8];
+        if (i < DK) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) acc[jj] = Bm[static_cast<int64_t>(i) * DV + j0 + jj];
+            for (int k = 0; k < DK; ++k) {
+                const float m = sM[i][k];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) acc[jj] = fmaf(m, sS[k][j0 + jj], acc[jj]);
+            }
+        }
+        __syncthreads();                             // every read of sS done
+        if (i < DK) {
+            float* dst = sg.S + ((slot0 + s + 1) * H + h) * DK * DV + cb * 16 + static_cast<int64_t>(i) * DV;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                sS[i][j0 + jj] = acc[jj];
+                dst[j0 + jj] = acc[jj];
+            }
+        }
     }
 }
 
@@ -803,10 +953,44 @@ size_t record_bytes(int32_t dk, bool precise) {
     return precise ? Rec<64, true>::BYTES : Rec<64, false>::BYTES;
 }
 
+// Segments pay when the state pass would leave most of the chip idle -- few (sequence, head)
+// column blocks -- and sequences are long on average.  A pure function of the sizes, so that
+// the workspace query and the launch agree.
+bool use_segments(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dv) {
+    const int64_t wgs = static_cast<int64_t>(n_seqs) * H * (dv / (16 * STATE_WAVES));
+    return wgs <= 128 && total_tokens >= 2 * SEG_TOK * static_cast<int64_t>(n_seqs);
+}
+int64_t seg_slot_bound(int32_t n_seqs, int64_t total_tokens) {   // packed and fixed batches
+    return total_tokens / SEG_TOK + n_seqs + 1;
+}
+size_t record_area(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk, bool precise) {
+    const int64_t slots = total_tokens / BLK + n_seqs + 1;   // bound for packed and fixed batches
+    const size_t b = static_cast<size_t>(slots) * static_cast<size_t>(H) * record_bytes(dk, precise);
+    return (b + 255) & ~static_cast<size_t>(255);
+}
+
+template <int DK, int IDT, int ODT, bool PRECISE, int NW, bool CKPT, int MODE>
+void launch_state(const ChunkArgs& a, int64_t nslots, const uint8_t* ws, const SegArgs& sg,
+                  int64_t units, int nvx, hipStream_t stream) {
+    const int64_t groups = (units + 7) / 8;
+    const int32_t n_vblk = a.dv / (16 * NW);
+    hipLaunchKernelGGL((chunk_state_kernel<DK, IDT, ODT, PRECISE, NW, CKPT, MODE>),
+                       dim3(static_cast<unsigned>(groups * 8 * nvx)), dim3(64 * NW), 0, stream, a,
+                       n_vblk, nslots, ws, sg);
+}
+
+template <int DK, int IDT, int ODT, bool PRECISE, int MODE, int NW = STATE_WAVES>
+void launch_state_ck(const ChunkArgs& a, int64_t nslots, const uint8_t* ws, const SegArgs& sg,
+                     int64_t units, int nvx, hipStream_t stream) {
+    if (a.ckpt) launch_state<DK, IDT, ODT, PRECISE, NW, true, MODE>(a, nslots, ws, sg, units, nvx, stream);
+    else launch_state<DK, IDT, ODT, PRECISE, NW, false, MODE>(a, nslots, ws, sg, units, nvx, stream);
+}
+
 template <int DK, int IDT, int GDT, int ODT>
 hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     constexpr bool PRECISE = (IDT == KDA_F32);
-    const int64_t nslots = slot_count(a.n_seqs, static_cast<int64_t>(a.B) * a.T, a.cu != nullptr, a.B, a.T);
+    const int64_t total = static_cast<int64_t>(a.B) * a.T;
+    const int64_t nslots = slot_count(a.n_seqs, total, a.cu != nullptr, a.B, a.T);
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
     const int64_t intra_wgs = nslots * a.H;
     if (intra_wgs > 0) {
@@ -821,15 +1005,40 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     }
     constexpr int NW = STATE_WAVES;
     const int32_t n_vblk = a.dv / (16 * NW);
-    const int64_t units = static_cast<int64_t>(a.n_seqs) * a.H;
-    const int64_t groups = (units + 7) / 8;
-    const dim3 grid(static_cast<unsigned>(groups * 8 * n_vblk));
-    if (a.ckpt)
-        hipLaunchKernelGGL((chunk_state_kernel<DK, IDT, ODT, PRECISE, NW, true>), grid, dim3(64 * NW), 0,
-                           stream, a, n_vblk, nslots, static_cast<const uint8_t*>(ws));
+    SegArgs sg{};
+    if (!use_segments(a.n_seqs, total, a.H, a.dv)) {
+        launch_state_ck<DK, IDT, ODT, PRECISE, 0>(a, nslots, ws, sg, static_cast<int64_t>(a.n_seqs) * a.H,
+                                                  n_vblk, stream);
+        return hipGetLastError();
+    }
+    // Long sequences: pass 1, the scan of segment pairs, pass 2.  With d_k = d_v = 128 the
+    // segment passes use 8-wave workgroups: one covers all 128 columns of a state, M or B, so a
+    // (segment, head) streams its records into two CUs instead of four.
+    const size_t st = static_cast<size_t>(seg_slot_bound(a.n_seqs, total)) * a.H * DK;
+    sg.S = reinterpret_cast<float*>(ws + record_area(a.n_seqs, total, a.H, DK, PRECISE));
+    sg.B = sg.S + st * a.dv;
+    sg.M = sg.B + st * a.dv;
+    sg.slots = a.cu ? seg_slot_bound(a.n_seqs, total)
+                    : static_cast<int64_t>(a.B) * (a.T <= 0 ? 1 : (a.T + SEG_TOK - 1) / SEG_TOK);
+    const int64_t seg_units = sg.slots * a.H;
+    const bool wide = (DK == 128 && a.dv == 128);
+    const int nw = wide ? 2 * NW : NW;
+    sg.n_vblk_m = DK / (16 * nw);
+    const int nvb = a.dv / (16 * nw);
+    if (wide)
+        launch_state_ck<DK, IDT, ODT, PRECISE, 1, 2 * NW>(a, nslots, ws, sg, seg_units, sg.n_vblk_m + nvb, stream);
     else
-        hipLaunchKernelGGL((chunk_state_kernel<DK, IDT, ODT, PRECISE, NW, false>), grid, dim3(64 * NW), 0,
-                           stream, a, n_vblk, nslots, static_cast<const uint8_t*>(ws));
+        launch_state_ck<DK, IDT, ODT, PRECISE, 1>(a, nslots, ws, sg, seg_units, sg.n_vblk_m + nvb, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((seg_scan_kernel<DK>), dim3(static_cast<unsigned>(static_cast<int64_t>(a.n_seqs) * a.H * (a.dv / 16))),
+                       dim3(256), 0, stream, a, sg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (wide)
+        launch_state_ck<DK, IDT, ODT, PRECISE, 2, 2 * NW>(a, nslots, ws, sg, seg_units, nvb, stream);
+    else
+        launch_state_ck<DK, IDT, ODT, PRECISE, 2>(a, nslots, ws, sg, seg_units, nvb, stream);
     return hipGetLastError();
 }
 
@@ -851,11 +1060,15 @@ hipError_t dispatch(const ChunkArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Workspace: one record per (head, 16-token block slot).
+// Workspace: one record per (head, 16-token block slot); for segmented launches, then the
+// segment start states, B and M per (segment slot, head).
 size_t chunk_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
-                             int32_t in_dtype) {
-    const int64_t slots = total_tokens / BLK + n_seqs + 1;   // bound for packed and fixed batches
-    return static_cast<size_t>(slots) * static_cast<size_t>(H) * record_bytes(dk, in_dtype == KDA_F32);
+                             int32_t dv, int32_t in_dtype) {
+    size_t b = record_area(n_seqs, total_tokens, H, dk, in_dtype == KDA_F32);
+    if (use_segments(n_seqs, total_tokens, H, dv))
+        b += static_cast<size_t>(seg_slot_bound(n_seqs, total_tokens)) * H * dk *
+             (2 * static_cast<size_t>(dv) + dk) * 4;
+    return b;
 }
 
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream) {

@@ -52,7 +52,7 @@ struct ChunkArgs {
 
 // Workspace bytes of a chunked prefill: one record per (head, 16-token block).
 size_t chunk_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
-                             int32_t in_dtype);
+                             int32_t dv, int32_t in_dtype);
 
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream);
 

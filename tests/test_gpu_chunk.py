@@ -337,3 +337,51 @@ def test_checkpoints_full_size_sampled():
     say("checkpoints full size", d["cfg"])
     _check_checkpoints(d, 512, TOL["bf16"], gated=True, units=[(0, 0), (1, 5), (2, 11), (3, 15)],
                        label="full")
+
+
+# ---- long sequences split into 8192-token segments ----------------------------------------------
+# A launch is segmented when its state pass would use at most 128 column blocks of 64 state
+# columns and sequences average 16384 tokens or more: pass 1 (segment 0 and the middle segments'
+# (M, B) pairs), the scan of the pairs, pass 2.  These shapes are segmented; every unit is checked.
+@pytest.mark.parametrize("T", [2 * 8192, 2 * 8192 + 64, 3 * 8192 + 100, 4 * 8192 - 17])
+def test_segmented_prefill_lengths(T):
+    """Two segments (no middle one), a one-chunk last segment, a ragged last segment, four
+    segments; random initial state."""
+    d = prefill_case("prefill_bf16", B=1, H=2, T=T)
+    say("segmented prefill", T)
+    check_full(d, oracle_g(d), TOL["bf16"], label=f"seg T={T}")
+
+
+def test_segmented_prefill_batch_and_packed():
+    """Two fixed-length sequences, then a packed batch mixing long, short and empty sequences."""
+    d = prefill_case("prefill_bf16", B=2, H=2, T=3 * 8192 + 5)
+    say("segmented prefill, B=2")
+    check_full(d, oracle_g(d), TOL["bf16"], label="seg B=2")
+    lens = [40000, 200, 0, 25000, 18000]
+    d = prefill_case("prefill_varlen", seqlens=lens, H=2)
+    say("segmented prefill, packed", lens)
+    check_full(d, oracle_g(d), TOL["bf16"], label="seg packed")
+
+
+def test_segmented_prefill_f32_and_fused_gate():
+    """fp32 inputs (32-token chunks, tolerance 1e-4) and the fused gate on segmented launches."""
+    d = prefill_case("prefill_f32_small", T=20000)
+    say("segmented prefill f32")
+    check_full(d, oracle_g(d), TOL["f32"], label="seg f32")
+    d = prefill_case("prefill_bf16", B=1, H=2, T=3 * 8192 + 33)
+    o, hT = _gated(d)
+    o_ref, S_ref, _ = oracle.forward(d["q"], d["k"], d["v"], d["beta"], oracle.gate(d["A"], d["z"]),
+                                     S0=d["S0"])
+    eo, es = rel_err(o, o_ref), rel_err(hT, S_ref)
+    say(f"  seg fused gate: o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_segmented_checkpoints():
+    """Checkpoints every 4096 tokens on a segmented launch (boundaries inside and at the ends of
+    segments), fixed-length and packed."""
+    d = prefill_case("prefill_bf16", B=1, H=2, T=3 * 8192 + 300)
+    say("segmented checkpoints")
+    _check_checkpoints(d, 4096, TOL["bf16"], label="seg")
+    d = prefill_case("prefill_varlen", seqlens=[40000, 200, 0, 25000, 18000], H=2)
+    _check_checkpoints(d, 4096, TOL["bf16"], gated=True, label="seg packed")
