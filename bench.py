@@ -6,8 +6,9 @@ the intra-block work and the state pass, from A and z (bf16) to o (bf16) and the
 (fp32).  The same step through the separate kda_gate + kda_chunk_fwd entry points is timed too
 and reported under "unfused".  Inputs are synthetic (seeded generators, the workload's shapes
 and distributions) and resident in HBM before the timed region starts.  The decode workload
-(256 sequences x 32 heads, 64 in-place steps) is timed in the same run and reported under
-"decode".
+(256 sequences x 32 heads, 64 in-place steps, plus speculative-decode verify and commit) is
+timed in the same run and reported under "decode", and the long workload (1 x 65536 tokens, 32
+heads, run in 8192-token segments) under "long_prefill".
 
 Prints ONE JSON line.  ``value`` is prefill tokens/s (B*T tokens per step / step time).
 ``roofline`` describes the step's one operation, kda_chunk_fwd_gated (its two kernels: the
@@ -56,6 +57,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-sequence prefill leg")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--mode", choices=("all", "prefill", "decode"), default="all",
                     help="prefill / decode: run only that workload and print no JSON line "
@@ -191,6 +193,45 @@ def run_decode(args, dev, inputs, K, stream):
                       "bf16 q/k/v/beta/g, 64 steps"}
 
 
+def run_long(args, dev, inputs, K, stream):
+    """The long workload: 1 sequence x 65536 tokens, 32 heads, z ~ N(0, 2^2).  With few
+    (sequence, head) units the library cuts the sequence into 8192-token segments (pass 1, the
+    scan of segment pairs, pass 2).  kda_chunk_fwd_gated, timed with HIP events over 5 calls."""
+    cfg = inputs.config("prefill_long")
+    log("generating", cfg)
+    d = inputs.make_prefill(cfg)
+    q, k, v, beta, z = (d[x].to(dev) for x in ("q", "k", "v", "beta", "z"))
+    A, S0 = d["A"].to(dev), d["S0"].to(dev)
+    del d
+    B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty_like(S0)
+    ws = torch.empty(K.kda_chunk_fwd_workspace_size(B, B * T, H, dk, dv), dtype=torch.uint8,
+                     device=dev)
+
+    def call():
+        K.kda_chunk_fwd_gated(q, k, v, beta, A, z, initial_state=S0, final_state=hT, o=o,
+                              workspace=ws, stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    alg = B * T * H * FUSED_BYTES_PER_TH + H * dk * 4 + 2 * B * H * dk * dv * 4
+    return {"config": "1 x 65536 tokens, 32 heads, d_k=d_v=128, bf16, gate fused; "
+                      "split into 8192-token segments",
+            "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "algorithmic_gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(alg / (ms * 1e-3) / HBM_PEAK, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -290,6 +331,7 @@ def main():
     value = tokens / (ms_per_step * 1e-3)
 
     dec = run_decode(args, dev, inputs, K, stream)
+    long_ = None if args.no_long else run_long(args, dev, inputs, K, stream)
     copy_bps = copy_ceiling(dev, stream)
     dec["roofline"]["frac_of_copy"] = round(dec["roofline"]["achieved"] * 1e9 / copy_bps, 4)
 
@@ -341,6 +383,7 @@ def main():
                     "kda_chunk_fwd_frac_hbm": round(chunk_bytes / (chunk_avg * 1e-3) / HBM_PEAK, 4),
                     "tokens_per_s": round(tokens / ((gate_avg + chunk_avg) * 1e-3), 1)},
         "decode": dec,
+        "long_prefill": long_,
         "copy_ceiling_gbs": round(copy_bps / 1e9, 1),
         "cpu_baseline": cpu,
     }
