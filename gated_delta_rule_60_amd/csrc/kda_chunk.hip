@@ -258,10 +258,18 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
     constexpr int LE = BLK * 64;          // elements of one [16][64] LDS operand array
     constexpr float LOG2E = 1.4426950408889634f;
 
-    // split operands of one phase (reused by the next): 12 KB, so that 12 waves fit a CU
-    __shared__ __attribute__((aligned(16))) uint16_t sKh[LE], sKl[LE];   // Kt  hi/lo
-    __shared__ __attribute__((aligned(16))) uint16_t sQh[LE], sQl[LE];   // Qt  hi/lo
-    __shared__ __attribute__((aligned(16))) uint16_t sDh[LE], sDl[LE];   // Kd  hi/lo
+    // split operands of one phase (reused by the next): 12 KB, so that 12 waves fit a CU.  Once
+    // a phase's products are formed the same 12 KB stage its share of the record, which then
+    // goes out in whole 1 KB wave stores (the record's fragment order scatters a lane's values).
+    __shared__ __attribute__((aligned(16))) uint16_t sOps[6 * LE];
+    uint16_t* const sKh = sOps;              // Kt hi / lo
+    uint16_t* const sKl = sOps + LE;
+    uint16_t* const sQh = sOps + 2 * LE;     // Qt hi / lo
+    uint16_t* const sQl = sOps + 3 * LE;
+    uint16_t* const sDh = sOps + 4 * LE;     // Kd hi / lo
+    uint16_t* const sDl = sOps + 5 * LE;
+    uint8_t* const stg = reinterpret_cast<uint8_t*>(sOps);
+    constexpr int WIN = 2 * BLK * 64;        // bytes of one record array's share of a phase
     __shared__ __attribute__((aligned(16))) float sA[16][16];
     __shared__ float sBeta[16];
 
@@ -354,6 +362,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
 #pragma unroll
         for (int c = 0; c < 4; ++c) gam[c] = fexp2(G15[c]);
         float kb[16];
+        uint2 rw[R::NA][4];                               // this lane's record words, by array
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * sub + i;
@@ -379,31 +388,28 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
             store_words<2>(sKh + off, wKh); store_words<2>(sKl + off, wKl);
             store_words<2>(sQh + off, wQh); store_words<2>(sQl + off, wQl);
             store_words<2>(sDh + off, wDh); store_words<2>(sDl + off, wDl);
-            // record: the state pass's Kt, Qt operands (frag32: four channels = 8 contiguous bytes)
-            const int fo = 2 * frag32(r, c0);
+            // record words: the state pass's Kt, Qt operands (frag32: four channels = 8 bytes)
             if constexpr (!PRECISE) {
-                *reinterpret_cast<uint2*>(rec + fo) = make_uint2(f16_pair(kt[0], kt[1]), f16_pair(kt[2], kt[3]));
-                *reinterpret_cast<uint2*>(rec + 2 * R::E + fo) = make_uint2(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]));
+                rw[0][i] = make_uint2(f16_pair(kt[0], kt[1]), f16_pair(kt[2], kt[3]));
+                rw[1][i] = make_uint2(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]));
             } else {
-                *reinterpret_cast<uint2*>(rec + fo) = make_uint2(wKh[0], wKh[1]);
-                *reinterpret_cast<uint2*>(rec + 2 * R::E + fo) = make_uint2(wKl[0], wKl[1]);
-                *reinterpret_cast<uint2*>(rec + 4 * R::E + fo) = make_uint2(wQh[0], wQh[1]);
-                *reinterpret_cast<uint2*>(rec + 6 * R::E + fo) = make_uint2(wQl[0], wQl[1]);
+                rw[0][i] = make_uint2(wKh[0], wKh[1]);
+                rw[1][i] = make_uint2(wKl[0], wKl[1]);
+                rw[2][i] = make_uint2(wQh[0], wQh[1]);
+                rw[3][i] = make_uint2(wQl[0], wQl[1]);
             }
         }
-        // record: Kb^T (frag16: the lane's 4 tokens of each channel are contiguous)
+        // record words: Kb^T (frag16: the lane's 4 tokens of each channel are contiguous)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const int off = frag16(c0 + c, 4 * sub);
             if constexpr (!PRECISE) {
-                *reinterpret_cast<uint2*>(rec + 2 * (2 * R::E + off)) =
-                    make_uint2(f16_pair(kb[0 + c], kb[4 + c]), f16_pair(kb[8 + c], kb[12 + c]));
+                rw[2][c] = make_uint2(f16_pair(kb[0 + c], kb[4 + c]), f16_pair(kb[8 + c], kb[12 + c]));
             } else {
                 uint32_t h0, l0, h1, l1;
                 split_pair(kb[0 + c], kb[4 + c], h0, l0);
                 split_pair(kb[8 + c], kb[12 + c], h1, l1);
-                *reinterpret_cast<uint2*>(rec + 2 * (4 * R::E + off)) = make_uint2(h0, h1);
-                *reinterpret_cast<uint2*>(rec + 2 * (5 * R::E + off)) = make_uint2(l0, l1);
+                rw[4][c] = make_uint2(h0, h1);
+                rw[5][c] = make_uint2(l0, l1);
             }
         }
         // record: e^{G_15} - 1 (same absolute precision as e^{G_15} in fp32)
@@ -428,11 +434,41 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
             accA = mfma32_bf16_x3(kh, kl, dh, dl, accA);
             accP = mfma32_bf16_x3(qh, ql, dh, dl, accP);
         }
+
+        // ---- this phase's share of the record: array a holds bytes [a * 2E + WIN * ph, + WIN)
+        __syncthreads();   // the operand arrays have been read
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int so = 2 * frag32(4 * sub + i, c0) - WIN * ph;
+#pragma unroll
+            for (int a = 0; a < (PRECISE ? 4 : 2); ++a)
+                *reinterpret_cast<uint2*>(stg + a * WIN + so) = rw[a][i];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int so = 2 * frag16(c0 + c, 4 * sub) - WIN * ph;
+#pragma unroll
+            for (int a = (PRECISE ? 4 : 2); a < R::NA; ++a)
+                *reinterpret_cast<uint2*>(stg + a * WIN + so) = rw[a][c];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < R::NA; ++a)
+#pragma unroll
+            for (int u = 0; u < WIN / 1024; ++u)
+                *reinterpret_cast<uint4*>(rec + a * 2 * R::E + WIN * ph + (64 * u + lane) * 16) =
+                    *reinterpret_cast<const uint4*>(stg + a * WIN + (64 * u + lane) * 16);
     }
+    // T' and P are staged too, then written with e^{G_15} - 1 already in place: bytes
+    // [OFF_T, OFF_G) of the record
+    constexpr int TAIL = R::OFF_G - R::OFF_T;
+    uint16_t* const tT = reinterpret_cast<uint16_t*>(stg);
+    uint16_t* const tP = reinterpret_cast<uint16_t*>(stg + (R::OFF_P - R::OFF_T));
+    __syncthreads();   // the last phase's record share has been copied out
     {
         // lane (ln, lq) holds rows 4lq + i of column ln
-        uint16_t* Ph = reinterpret_cast<uint16_t*>(rec + R::OFF_P);
-        uint16_t* Pl = reinterpret_cast<uint16_t*>(rec + R::OFF_P + 512);
+        uint16_t* Ph = tP;
+        uint16_t* Pl = tP + 256;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * lq + i, s = ln;
@@ -473,7 +509,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
             t[r] = ((r == jc) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
         }
         const float bj = sBeta[jc];
-        uint16_t* Th = reinterpret_cast<uint16_t*>(rec + R::OFF_T);
+        uint16_t* Th = tT;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float x = t[r] * bj;
@@ -486,6 +522,9 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
             }
         }
     }
+    __syncthreads();   // T' and P staged
+    for (int j = lane; j < TAIL / 16; j += 64)
+        *reinterpret_cast<uint4*>(rec + R::OFF_T + 16 * j) = *reinterpret_cast<const uint4*>(stg + 16 * j);
 }
 
 // ============================================================================================
