@@ -928,9 +928,11 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
 
 // Segment scan: one workgroup per (sequence, head, 16 state columns) walks the sequence's
 // segments, S_start(s + 1) = M_s S_start(s) + B_s for s = 1 .. nseg - 2, in fp32.  The column
-// blocks are independent (M acts on the rows), so they run apart.
+// blocks are independent (M acts on the rows), so they run apart.  The next step's M is loaded
+// into registers (16-byte loads) while the current step computes.
 template <int DK>
 __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) {
+    constexpr int NM = DK * DK / 4 / 256;            // float4s of M per thread
     __shared__ float sM[DK][DK + 1];
     __shared__ float sS[DK][16];
     const int DV = p.dv, ncb = DV / 16;
@@ -950,15 +952,26 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
     if (nseg < 3) return;                             // no middle segment: nothing to combine
     const int t = threadIdx.x;
     const int i = t >> 1, j0 = (t & 1) * 8;         // this thread: row i, columns j0 .. j0+7
+    auto m_of = [&](int64_t s) { return sg.M + ((slot0 + s) * H + h) * DK * DK; };
+    float4 mr[NM];
+    auto load_m = [&](int64_t s) {
+        const float4* src = reinterpret_cast<const float4*>(m_of(s));
+#pragma unroll
+        for (int u = 0; u < NM; ++u) mr[u] = src[u * 256 + t];
+    };
     const float* S1 = sg.S + ((slot0 + 1) * H + h) * DK * DV + cb * 16;
     for (int e = t; e < DK * 16; e += 256) sS[e >> 4][e & 15] = S1[(e >> 4) * DV + (e & 15)];
+    load_m(1);
     for (int64_t s = 1; s + 1 < nseg; ++s) {
-        const int64_t us = (slot0 + s) * H + h;
-        const float* M = sg.M + us * DK * DK;
-        const float* Bm = sg.B + us * DK * DV + cb * 16;
+        const float* Bm = sg.B + ((slot0 + s) * H + h) * DK * DV + cb * 16;
         __syncthreads();                             // sS written, the previous sM reads done
-        for (int e = t; e < DK * DK; e += 256) sM[e / DK][e % DK] = M[e];
+#pragma unroll
+        for (int u = 0; u < NM; ++u) {
+            const int e = 4 * (u * 256 + t), r = e / DK, c = e % DK;
+            sM[r][c] = mr[u].x; sM[r][c + 1] = mr[u].y; sM[r][c + 2] = mr[u].z; sM[r][c + 3] = mr[u].w;
+        }
         __syncthreads();
+        if (s + 2 < nseg) load_m(s + 1);             // in flight during this step
         float acc[8];
         if (i < DK) {
 #pragma unroll
