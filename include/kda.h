@@ -195,9 +195,9 @@ int kda_decode_step(const void *q, const void *k, const void *v, const void *bet
  * kda_decode_step would give, with one read of the state instead of K reads and writes.
  * o must not overlap any other argument.
  *
- * kda_decode_commit -- once the draft has been checked, advances each state in place by its accepted
- * tokens: accepted is a device int32 [N] array of counts (values outside [0, K] are clamped;
- * 0 leaves the state untouched).  The same inputs are passed again; no o is produced.  The new
+ * kda_decode_commit -- once the draft has been checked, advances each state in place by its
+ * accepted tokens: accepted is a device int32 [N] array of counts (values outside [0, K] are
+ * clamped; 0 leaves the state untouched).  The same inputs are passed again; no o is produced.  The new
  * state equals accepted[n] successive kda_decode_step calls bit for bit.  The state must not
  * overlap any input or `accepted`.
  *
