@@ -385,3 +385,12 @@ def test_segmented_checkpoints():
     _check_checkpoints(d, 4096, TOL["bf16"], label="seg")
     d = prefill_case("prefill_varlen", seqlens=[40000, 200, 0, 25000, 18000], H=2)
     _check_checkpoints(d, 4096, TOL["bf16"], gated=True, label="seg packed")
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
+def test_segmented_prefill_head_dims(dk, dv):
+    """Segmented launches whose segment passes run 4-wave workgroups (d_k != d_v): the M column
+    blocks (d_k) and B column blocks (d_v) differ in number."""
+    d = prefill_case("prefill_bf16", B=1, H=2, T=3 * 8192 + 77, dk=dk, dv=dv)
+    say("segmented prefill dims", dk, dv)
+    check_full(d, oracle_g(d), TOL["bf16"], label=f"seg dk={dk} dv={dv}")
