@@ -26,14 +26,17 @@
 // 1. Intra-block kernel (everything that does not depend on S; fully parallel): one wave per
 //    (16-token block, head).  Block cumsum by quad-lane DPP moves, decay factors, A and P on
 //    MFMA from split-bf16 operands staged in LDS, T' by substitution; writes one record per
-//    (head, block) to the workspace: Kt, Qt, Kb^T in their MFMA formats, T', P, e^{G_15}.
+//    (head, block) to the workspace -- Kt, Qt, Kb^T in their MFMA formats, T', P, e^{G_15} - 1 --
+//    staged through LDS so that it leaves in whole 1 KB wave stores.
 // 2. State-passing kernel (the sequential part): one 256-lane workgroup per (sequence, head,
 //    64 state columns); each wave owns 16 state columns in fp32 accumulators for the whole
 //    sequence.  A chunk's four records and its V rows stream into double-buffered LDS while the
-//    previous chunk is processed.
-// Precision: operands that are range-bounded use fp16 (11-bit significand) in one pass; the
-// diagonal products (factors up to e^80), T' X and P W use split bf16 (hi*hi + hi*lo + lo*hi).
-// For fp32 inputs every product is split bf16.
+//    previous chunk is processed.  Optionally it stores the state every k tokens (checkpoints).
+//    Long sequences with few (sequence, head) units run it as segment passes around a scan of
+//    the segments' affine pairs (see the segment section below).
+// Precision: operands that are range-bounded use fp16 (11-bit significand) in one pass (Kt S,
+// Qt S, T' X, Kb^T W for bf16 inputs); the diagonal products (factors up to e^80) and P W use
+// split bf16 (hi*hi + hi*lo + lo*hi).  For fp32 inputs every product is split bf16.
 #include <type_traits>
 
 #include "kda_common.hpp"
