@@ -122,6 +122,14 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* beta
     for (const Range& x : {r_q, r_k, r_v, r_b, r_g, r_a, r_h0, r_cu})
         if (overlap(r_ws, x)) return KDA_ERR_INVALID_ARGUMENT;
 
+    if (kda::debug_validation_enabled() && ntok > 0) {
+        bool ok = true;
+        const hipError_t e = kda::debug_validate(gated ? nullptr : g, g_dtype, ntok * H * dk, cu_seqlens,
+                                                 n_seqs, ntok, static_cast<hipStream_t>(stream), &ok);
+        if (e != hipSuccess) return KDA_ERR_HIP;
+        if (!ok) return KDA_ERR_INVALID_ARGUMENT;
+    }
+
     kda::ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
     a.gate_A = gated ? gate_A : nullptr; a.g_min = g_min;
@@ -196,6 +204,13 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* bet
     for (const Range& x : ins)
         if (overlap(r_o, x) || overlap(r_s, x)) return KDA_ERR_INVALID_ARGUMENT;
     if (overlap(r_o, r_s)) return KDA_ERR_INVALID_ARGUMENT;
+    if (kda::debug_validation_enabled()) {
+        bool ok = true;
+        if (kda::debug_validate(g, g_dtype, int64_t(N) * H * dk, nullptr, 0, 0, static_cast<hipStream_t>(stream), &ok) !=
+            hipSuccess)
+            return KDA_ERR_HIP;
+        if (!ok) return KDA_ERR_INVALID_ARGUMENT;
+    }
     return from_hip(kda::launch_decode(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype, N,
                                        H, dk, dv, scale, static_cast<hipStream_t>(stream)));
 }
@@ -218,6 +233,13 @@ int kda_decode_verify(const void* q, const void* k, const void* v, const void* b
                             range(g, rows * dk * esize(g_dtype)), range(state, int64_t(N) * H * dk * dv * 4)};
     for (const Range& x : others)
         if (overlap(r_o, x)) return KDA_ERR_INVALID_ARGUMENT;
+    if (kda::debug_validation_enabled()) {
+        bool ok = true;
+        if (kda::debug_validate(g, g_dtype, int64_t(N) * K * H * dk, nullptr, 0, 0, static_cast<hipStream_t>(stream), &ok) !=
+            hipSuccess)
+            return KDA_ERR_HIP;
+        if (!ok) return KDA_ERR_INVALID_ARGUMENT;
+    }
     return from_hip(kda::launch_decode_verify(q, k, v, beta, in_dtype, g, g_dtype, state, o, o_dtype,
                                               N, K, H, dk, dv, scale, static_cast<hipStream_t>(stream)));
 }
@@ -237,6 +259,13 @@ int kda_decode_commit(const void* q, const void* k, const void* v, const void* b
                             range(g, rows * dk * esize(g_dtype)), range(accepted, int64_t(N) * 4)};
     for (const Range& x : others)
         if (overlap(r_s, x)) return KDA_ERR_INVALID_ARGUMENT;
+    if (kda::debug_validation_enabled()) {
+        bool ok = true;
+        if (kda::debug_validate(g, g_dtype, int64_t(N) * K * H * dk, nullptr, 0, 0, static_cast<hipStream_t>(stream), &ok) !=
+            hipSuccess)
+            return KDA_ERR_HIP;
+        if (!ok) return KDA_ERR_INVALID_ARGUMENT;
+    }
     return from_hip(kda::launch_decode_commit(q, k, v, beta, in_dtype, g, g_dtype, state, accepted,
                                               N, K, H, dk, dv, static_cast<hipStream_t>(stream)));
 }

@@ -26,6 +26,12 @@ hipError_t launch_decode_commit(const void* q, const void* k, const void* v, con
                                 const int32_t* accepted, int32_t N, int32_t K, int32_t H,
                                 int32_t dk, int32_t dv, hipStream_t stream);
 
+// Optional debug check (KDA_DEBUG_VALIDATE): g (g_elems values, or none) within [-5, 0] and, for
+// packed batches, cu_seqlens well formed.  Synchronises the stream; *ok = false on a violation.
+bool debug_validation_enabled();
+hipError_t debug_validate(const void* g, int g_dtype, int64_t g_elems, const int32_t* cu,
+                          int32_t n_seqs, int64_t total, hipStream_t stream, bool* ok);
+
 struct ChunkArgs {
     const void* q;
     const void* k;

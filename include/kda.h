@@ -31,7 +31,14 @@
  *     argument errors are reported before any device work is enqueued.  Device-resident
  *     preconditions (g in [-5, 0], well-formed cu_seqlens) are the caller's contract and are not
  *     checked; violating them gives undefined (but memory-safe) results.
- *   - Calls are stateless and reentrant.
+ *   - Debug check: with the environment variable KDA_DEBUG_VALIDATE set (to anything but "" or
+ *     "0"), kda_chunk_fwd, kda_chunk_fwd_checkpointed and the three decode calls first test those
+ *     preconditions on the device (kda_chunk_fwd_gated tests cu_seqlens only: its g is in range
+ *     by construction), wait for the answer on `stream` and return KDA_ERR_INVALID_ARGUMENT,
+ *     with nothing else enqueued, on a violation.  This synchronises the host, shares one word
+ *     of library-owned device memory between all calls on a device (overlapping checked calls
+ *     race on it) and must not be used under stream capture.
+ *   - Calls are stateless and reentrant (the debug check aside).
  */
 #ifndef KDA_H
 #define KDA_H
