@@ -60,6 +60,9 @@ constexpr int STATE_WAVES = 4;   // waves per state-kernel workgroup (16 state c
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// s_waitcnt immediate for "vmcnt <= n", other counters unconstrained.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
 // Buffer resource over [base, base + bytes): raw (unswizzled, stride 0) accesses whose byte offset
 // lies outside the range read 0 and write nothing, so loads and stores need no branches and the
 // compiler can count outstanding memory operations exactly.  Word 3 selects 32-bit data format.
@@ -530,11 +533,288 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
         *reinterpret_cast<uint4*>(rec + R::OFF_T + 16 * j) = *reinterpret_cast<const uint4*>(stg + 16 * j);
 }
 
+// LDS ordering inside a one-wave workgroup: a wave's LDS operations execute in order, so only the
+// compiler must keep them in place.  A wavefront-scope fence does that and emits no wait (a
+// workgroup barrier's fence would also wait for every transfer still in flight).
+__device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+// ============================================================================================
+// 1b. intra-block kernel for 16-bit inputs: one wave per (block slot, head), token per lane
+// ============================================================================================
+// Lane (m, q) owns token m = lane & 15 of the block and, in every 32-channel group kk, the eight
+// channels 32 kk + 16 (j >> 2) + 4 q + (j & 3), j = 0..7 -- exactly the channels its 16-byte unit of
+// a frag32 record array holds.  Therefore:
+//   * the block cumsum runs across the 16 lanes of a row (DPP shifts), G_15 is lane 15's value;
+//   * A = beta * strict_lower(Kt Kd^T) and P = lower(Qt Kd^T) are fp32 MFMAs (16x16x4) fed straight
+//     from the registers: step (kk, j) contracts the four channels the lanes of rows q = 0..3 own,
+//     so the channel order of the contraction is the record's and no operand is split or staged;
+//   * each lane's fp16 Kt and Qt values are its frag32 units: whole 1 KB wave stores.
+// Only Kb^T (channel-major) goes through LDS.  Same record, same arithmetic per element as the
+// split-operand kernel except the cumsum's association (a prefix tree instead of a running sum).
+template <int DK, int GDT, bool GATE>
+__global__ void __launch_bounds__(64, 4) chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
+    using R = Rec<DK, false>;
+    constexpr int KS = DK / 32;           // 32-channel groups
+    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr int E2 = 2 * R::E;          // bytes of one 16-bit record array
+    constexpr int TAIL = R::OFF_G - R::OFF_T;
+
+    constexpr int PH = DK / 64;           // 64-channel phases: one 128-byte line of a bf16 row
+    constexpr int GSZ = (GDT == KDA_F32) ? 4 : 2;
+    constexpr int CPR = 64 * 2 / 16;      // 16-byte chunks per row of a bf16 phase tile
+    constexpr int CPRG = 64 * GSZ / 16;   // ... of the g / z phase tile
+    constexpr int TB = BLK * 64 * 2;      // bytes of a bf16 phase tile
+    constexpr int TBG = BLK * 64 * GSZ;   // bytes of the g / z phase tile
+    constexpr int PB = 2 * TB + TBG;      // bytes of one phase's inputs: k, q, g / z
+    // Inputs arrive by direct-to-LDS loads, whole lines per instruction, into [16][64]-channel
+    // phase tiles whose 16-byte chunks are XOR-swizzled by row: slot(m, c) = m * CPR + (c ^ m').
+    // Each lane then reads its own channels without bank conflicts.
+    __shared__ __attribute__((aligned(16))) uint8_t sIn[PB];          // one phase's tiles
+    __shared__ __attribute__((aligned(16))) uint16_t sKb[BLK * 32];     // Kb^T of one group, frag16
+    __shared__ __attribute__((aligned(16))) float sRate[GATE ? DK : 4];
+    __shared__ float sBeta[16];
+    // after the last group the input tiles are dead: A (fp32 16 x 16) and the staged T', P hi,
+    // P lo (fragT) reuse them
+    static_assert(1024 + TAIL <= PB, "staging fits the input tiles");
+    float (*const sA)[16] = reinterpret_cast<float (*)[16]>(sIn);
+    uint8_t* const sTail = sIn + 1024;
+
+    const int lane = threadIdx.x;
+    const int m = lane & 15, q = lane >> 4;
+
+    const int64_t H = p.H;
+    const int64_t slot = blockIdx.x / H;
+    const int h = static_cast<int>(blockIdx.x % H);
+    int n;
+    int64_t j0, bos, len;
+    if (!locate_slot(p, slot, n, j0, bos, len)) return;
+    const int64_t t0 = BLK * j0;
+    const int nt = static_cast<int>((len - t0) < BLK ? (len - t0) : BLK);
+    uint8_t* rec = ws + (static_cast<int64_t>(h) * nslots + slot) * R::BYTES;
+    const bool live = m < nt;             // this lane's token exists
+
+    // ---- beta and A into registers, then every phase's tiles; beta and the gate rates go to LDS
+    // afterwards (the compiler counts its own waits for them, and the per-phase waits below only
+    // need the older tile transfers done).  Rows past the block's last token read zeros: the
+    // buffer ranges end there.
+    const int64_t row0 = (bos + t0) * H + h;
+    float av[GATE ? DK / 64 : 1];
+    // beta of token `lane`: lanes 16 .. 63 and tokens past the block fall outside the range
+    const float bval = bf16_val(__builtin_amdgcn_raw_buffer_load_b16(
+        make_rsrc(static_cast<const uint16_t*>(p.beta) + row0, nt * static_cast<uint32_t>(H) * 2),
+        lane * static_cast<uint32_t>(H) * 2, 0, 0));
+    if constexpr (GATE) {
+#pragma unroll
+        for (int i = 0; i < DK / 64; ++i) av[i] = p.gate_A[static_cast<int64_t>(h) * DK + 64 * i + lane];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // these loads stay older than the tile transfers
+    const uint32_t rowb = static_cast<uint32_t>(H * DK * 2);                     // bytes per token
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const uint16_t*>(p.k) + row0 * DK, nt * rowb);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(static_cast<const uint16_t*>(p.q) + row0 * DK, nt * rowb);
+    const __amdgpu_buffer_rsrc_t gr = make_rsrc(static_cast<const uint8_t*>(p.g) + row0 * DK * GSZ,
+                                                nt * rowb / 2 * GSZ);
+    // phase ph's k, q and g / z tiles into sIn: 1 KB per wave instruction, four or eight rows of
+    // whole lines, non-temporal (each input is read once)
+    auto load_phase = [&](int ph) {
+#pragma unroll
+        for (int u = 0; u < TB / 1024; ++u) {
+            const int S = 64 * u + lane, mm = S / CPR, c = (S % CPR) ^ (mm & (CPR - 1));
+            const uint32_t off = mm * rowb + ph * 128 + 16 * c;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(sIn + 1024 * u),
+                                                     16, off, 0, 0, CP_NT);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (__attribute__((address_space(3))) void*)(sIn + TB + 1024 * u),
+                                                     16, off, 0, 0, CP_NT);
+        }
+#pragma unroll
+        for (int u = 0; u < TBG / 1024; ++u) {
+            const int S = 64 * u + lane, mm = S / CPRG, c = (S % CPRG) ^ (mm & (CPRG - 1));
+            const uint32_t off = mm * (rowb / 2 * GSZ) + ph * 64 * GSZ + 16 * c;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(gr, (__attribute__((address_space(3))) void*)(sIn + 2 * TB + 1024 * u),
+                                                     16, off, 0, 0, CP_NT);
+        }
+    };
+    load_phase(0);
+    if (lane < 16) sBeta[lane] = bval;
+    if constexpr (GATE) {   // one rate per (head, channel), shared through LDS
+#pragma unroll
+        for (int i = 0; i < DK / 64; ++i) sRate[64 * i + lane] = gate_rate(av[i]);
+    }
+    // token m's four channels 32 lk + 16 hf + 4 q .. + 3 of phase tile `tile` (bf16: 8 bytes)
+    auto tile_bf16 = [&](const uint8_t* tile, int lk, int hf) -> uint2 {
+        const int byte = (32 * lk + 16 * hf + 4 * q) * 2, c = byte >> 4;
+        return *reinterpret_cast<const uint2*>(tile + (m * CPR + (c ^ (m & (CPR - 1)))) * 16 + (byte & 15));
+    };
+    auto tile_f32 = [&](const uint8_t* tile, int lk, int hf) -> uint4 {
+        const int c = 8 * lk + 4 * hf + q;
+        return *reinterpret_cast<const uint4*>(tile + (m * CPRG + (c ^ (m & (CPRG - 1)))) * 16);
+    };
+    auto raw16 = [](const uint32_t* w, int j) -> float {      // element j of packed bf16 words
+        return (j & 1) ? __uint_as_float(w[j >> 1] & 0xffff0000u) : __uint_as_float(w[j >> 1] << 16);
+    };
+    wave_fence();   // beta and the gate rates are read across lanes
+
+    // Per 32-channel group, in stages so that independent work covers each latency: the gate
+    // and the eight scans side by side, the factors, the G_15 broadcasts (LDS swizzles) issued
+    // together, the MFMAs (which do not need G_15) while they are in flight, then Kb.
+    f32x4 accA0 = zero4(), accA1 = zero4(), accP0 = zero4(), accP1 = zero4();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        const int ph = kk >> 1, lk = kk & 1;
+        if (lk == 0) {   // this phase's tiles have landed
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            wave_fence();
+        }
+        const uint8_t* tk = sIn;
+        uint32_t rk[4], rq[4], rg[2 * (GSZ / 2) * 2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const uint2 a = tile_bf16(tk, lk, hf), b = tile_bf16(tk + TB, lk, hf);
+            rk[2 * hf] = a.x; rk[2 * hf + 1] = a.y;
+            rq[2 * hf] = b.x; rq[2 * hf + 1] = b.y;
+            if constexpr (GSZ == 4) {
+                const uint4 g4 = tile_f32(tk + 2 * TB, lk, hf);
+                rg[4 * hf] = g4.x; rg[4 * hf + 1] = g4.y; rg[4 * hf + 2] = g4.z; rg[4 * hf + 3] = g4.w;
+            } else {
+                const uint2 g2 = tile_bf16(tk + 2 * TB, lk, hf);
+                rg[2 * hf] = g2.x; rg[2 * hf + 1] = g2.y;
+            }
+        }
+        if (lk == 1 && ph + 1 < PH) {
+            // the phase's tiles are read: the next phase's transfers overwrite them while this
+            // group computes
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the tile reads above are done
+            wave_fence();
+            load_phase(ph + 1);
+        }
+        float x[8], e1[8], kt[8], qt[8], kd[8], gm[8];
+        float4 rate[2];
+        if constexpr (GATE) {
+            rate[0] = *reinterpret_cast<const float4*>(&sRate[32 * kk + 4 * q]);
+            rate[1] = *reinterpret_cast<const float4*>(&sRate[32 * kk + 16 + 4 * q]);
+        }
+        const float keep = live ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            // g of token m (0 past the block's tokens, as in the unfused path's zero fill)
+            float gv;
+            if constexpr (GATE) {
+                const float z = (GDT == KDA_F32) ? __uint_as_float(rg[j]) : raw16(rg, j);
+                const float4& r4 = rate[j >> 2];
+                const float rt = (j & 3) == 0 ? r4.x : (j & 3) == 1 ? r4.y : (j & 3) == 2 ? r4.z : r4.w;
+                gv = gate_log_decay(rt, z, p.g_min) * keep;
+            } else if constexpr (GDT == KDA_F32) {
+                gv = __uint_as_float(rg[j]);
+            } else {
+                gv = raw16(rg, j);
+            }
+            x[j] = gv * LOG2E;
+        }
+        // inclusive cumsum over the 16 tokens of each row (log2 units): a Hillis-Steele scan
+#define KDA_SCAN_STEP(CTRL)                                                                          \
+        _Pragma("unroll") for (int j = 0; j < 8; ++j)                                              \
+            x[j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[j]), CTRL, 0xf, 0xf, true));
+        KDA_SCAN_STEP(0x111)
+        KDA_SCAN_STEP(0x112)
+        KDA_SCAN_STEP(0x114)
+        KDA_SCAN_STEP(0x118)
+#undef KDA_SCAN_STEP
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e1[j] = fexp2(x[j]);                 // e^{G} <= 1
+        // e^{G_15}: lane 15 of the row (bitmask swizzle: lane -> (lane & 16) | 15)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gm[j] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(e1[j]), 0x1F0));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float kv = raw16(rk, j), qv = raw16(rq, j);
+            kt[j] = kv * e1[j];
+            qt[j] = qv * (e1[j] * p.scale);                              // the output scale rides on Qt and P
+            kd[j] = kv * fexp2(-x[j]);                                   // e^{-G} <= e^80
+            if (j & 1) {
+                accA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[j], kd[j], accA1, 0, 0, 0);
+                accP1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qt[j], kd[j], accP1, 0, 0, 0);
+            } else {
+                accA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[j], kd[j], accA0, 0, 0, 0);
+                accP0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qt[j], kd[j], accP0, 0, 0, 0);
+            }
+        }
+        // the frag32 units of Kt and Qt
+        *reinterpret_cast<uint4*>(rec + (64 * kk + lane) * 16) =
+            make_uint4(f16_pair(kt[0], kt[1]), f16_pair(kt[2], kt[3]), f16_pair(kt[4], kt[5]), f16_pair(kt[6], kt[7]));
+        *reinterpret_cast<uint4*>(rec + E2 + (64 * kk + lane) * 16) =
+            make_uint4(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]), f16_pair(qt[4], qt[5]), f16_pair(qt[6], qt[7]));
+        // Kb = Kd e^{G_15} <= 1, staged channel-major; e^{G_15} - 1 per channel from the row's
+        // last lane
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = 32 * kk + 16 * (j >> 2) + 4 * q + (j & 3);
+            sKb[frag16(c, m) - 512 * kk] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kd[j] * gm[j]));
+        }
+        wave_fence();   // the group's Kb^T is read across lanes, then leaves as one 1 KB store
+        *reinterpret_cast<uint4*>(rec + 2 * E2 + 1024 * kk + 16 * lane) =
+            *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(sKb) + 16 * lane);
+        if (m == 15) {
+            float* gr = reinterpret_cast<float*>(rec + R::OFF_G) + 32 * kk + 4 * q;
+            *reinterpret_cast<float4*>(gr) = make_float4(gm[0] - 1.f, gm[1] - 1.f, gm[2] - 1.f, gm[3] - 1.f);
+            *reinterpret_cast<float4*>(gr + 16) = make_float4(gm[4] - 1.f, gm[5] - 1.f, gm[6] - 1.f, gm[7] - 1.f);
+        }
+    }
+    const f32x4 accA = accA0 + accA1, accP = accP0 + accP1;
+
+    // ---- A to LDS (for the substitution), P staged as bf16 hi / lo; lane (m, q) holds rows
+    // 4q + i of column m
+    uint16_t* const tT = reinterpret_cast<uint16_t*>(sTail);
+    uint16_t* const Ph = reinterpret_cast<uint16_t*>(sTail + (R::OFF_P - R::OFF_T));
+    uint16_t* const Pl = Ph + 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * q + i, sc = m;
+        sA[r][sc] = (sc < r) ? accA[i] * sBeta[r] : 0.f;
+        const float pval = (sc <= r) ? accP[i] : 0.f;
+        const uint16_t ph = bf16_bits(pval);
+        Ph[fragT(r, sc)] = ph;
+        Pl[fragT(r, sc)] = bf16_bits(pval - bf16_val(ph));
+    }
+    wave_fence();   // sA and sBeta are read across lanes below
+
+    // ---- T' = (I + A)^{-1} Diag(beta): forward substitution, lane j = column j
+    if (lane < 16) {
+        const int jc = lane;
+        float t[16];
+        float4 nxt[4], cur[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) nxt[u] = *reinterpret_cast<const float4*>(&sA[1][4 * u]);
+        t[0] = (jc == 0) ? 1.f : 0.f;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+            if (r + 1 < 16) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (4 * u < r + 1) nxt[u] = *reinterpret_cast<const float4*>(&sA[r + 1][4 * u]);
+            }
+            float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sp = 0; sp < r; ++sp) {
+                const float4& c4 = cur[sp >> 2];
+                const float a = (sp & 3) == 0 ? c4.x : (sp & 3) == 1 ? c4.y : (sp & 3) == 2 ? c4.z : c4.w;
+                part[sp & 3] += a * t[sp];
+            }
+            t[r] = ((r == jc) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
+        }
+        const float bj = sBeta[jc];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            tT[fragT(r, jc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(t[r] * bj));
+    }
+    wave_fence();   // T' and P staged
+    for (int u = lane; u < TAIL / 16; u += 64)
+        *reinterpret_cast<uint4*>(rec + R::OFF_T + 16 * u) = *reinterpret_cast<const uint4*>(sTail + 16 * u);
+}
+
 // ============================================================================================
 // 2. state-passing kernel: one workgroup of NW waves per (sequence, head, 16 NW state columns)
 // ============================================================================================
-// s_waitcnt immediate for "vmcnt <= n", other counters unconstrained.
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // ---- segments of long sequences ---------------------------------------------------------------
 // A sequence longer than SEG_TOK tokens is cut into segments of SEG_TOK tokens [bagrov § Уровень
@@ -1049,12 +1329,22 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
     const int64_t intra_wgs = nslots * a.H;
     if (intra_wgs > 0) {
-        if (a.gate_A)
+        // 16-bit inputs: the token-per-lane kernel; fp32 inputs (split-bf16 records): the
+        // split-operand kernel
+        if constexpr (!PRECISE) {
+            if (a.gate_A)
+                hipLaunchKernelGGL((chunk_intra_tok_kernel<DK, GDT, true>),
+                                   dim3(static_cast<unsigned>(intra_wgs)), dim3(64), 0, stream, a, nslots, ws);
+            else
+                hipLaunchKernelGGL((chunk_intra_tok_kernel<DK, GDT, false>),
+                                   dim3(static_cast<unsigned>(intra_wgs)), dim3(64), 0, stream, a, nslots, ws);
+        } else if (a.gate_A) {
             hipLaunchKernelGGL((chunk_intra_kernel<DK, IDT, GDT, PRECISE, true>),
                                dim3(static_cast<unsigned>(intra_wgs)), dim3(64), 0, stream, a, nslots, ws);
-        else
+        } else {
             hipLaunchKernelGGL((chunk_intra_kernel<DK, IDT, GDT, PRECISE, false>),
                                dim3(static_cast<unsigned>(intra_wgs)), dim3(64), 0, stream, a, nslots, ws);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
