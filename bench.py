@@ -372,7 +372,7 @@ def main():
                      "traffic": measured_traffic(
                          "chunk_fwd_gated_prefill_bf16_B4_H16_T4096.md",
                          source_digest("kda_chunk.hip", "kda_common.hpp", "kda_internal.hpp")),
-                     "kernel": "kda_chunk_fwd_gated = chunk_intra_kernel (gate fused) + "
+                     "kernel": "kda_chunk_fwd_gated = chunk_intra_tok_kernel (gate fused) + "
                                "chunk_state_kernel",
                      "kernel_ms": round(fused_avg, 4), "bytes_per_launch": fused_bytes,
                      "workspace_bytes": ws.numel()},

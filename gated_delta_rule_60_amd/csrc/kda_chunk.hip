@@ -24,10 +24,13 @@
 // 64 x 64 triangular system is solved blockwise, the coupling going through the state.
 //
 // 1. Intra-block kernel (everything that does not depend on S; fully parallel): one wave per
-//    (16-token block, head).  Block cumsum by quad-lane DPP moves, decay factors, A and P on
-//    MFMA from split-bf16 operands staged in LDS, T' by substitution; writes one record per
-//    (head, block) to the workspace -- Kt, Qt, Kb^T in their MFMA formats, T', P, e^{G_15} - 1 --
-//    staged through LDS so that it leaves in whole 1 KB wave stores.
+//    (16-token block, head); writes one record per (head, block) to the workspace -- Kt, Qt,
+//    Kb^T in their MFMA formats, T', P, e^{G_15} - 1 -- in whole 1 KB wave stores.
+//    16-bit inputs (chunk_intra_tok_kernel): each lane owns one token and the channels of its
+//    record unit; inputs arrive by direct-to-LDS loads, the block cumsum is a DPP scan across
+//    the lanes, A and P are fp32 MFMAs fed from registers, T' by substitution.
+//    fp32 inputs (chunk_intra_kernel, split-bf16 records): each lane owns 4 tokens x 4 channels;
+//    quad-lane cumsum, A and P on MFMA from split-bf16 operands staged in LDS.
 // 2. State-passing kernel (the sequential part): one 256-lane workgroup per (sequence, head,
 //    64 state columns); each wave owns 16 state columns in fp32 accumulators for the whole
 //    sequence.  A chunk's four records and its V rows stream into double-buffered LDS while the
@@ -255,7 +258,7 @@ __device__ __forceinline__ bool locate_slot(const ChunkArgs& p, int64_t slot, in
 }
 
 // ============================================================================================
-// 1. intra-block kernel: one wave per (block slot, head)
+// 1. intra-block kernel for fp32 inputs (split-bf16 records): one wave per (block slot, head)
 // ============================================================================================
 template <int DK, int IDT, int GDT, bool PRECISE, bool GATE>
 __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
