@@ -160,8 +160,8 @@ __device__ __forceinline__ int fragT(int r, int s) { return (r + 16 * (s >> 2)) 
 // Record of one (head, block) in the workspace (byte offsets).  E = 16 * DK elements per array.
 //   fast   : [Kt fp16 frag32][Qt fp16 frag32][Kb^T fp16 frag16]
 //   precise: [Kt hi][Kt lo][Qt hi][Qt lo] (bf16 frag32) [Kb^T hi][Kb^T lo] (bf16 frag16)
-//   then T' (fast: fp16; precise: bf16 hi, lo), P hi, P lo (bf16; all fragT),
-//   then e^{G_15} - 1 (DK fp32).  Qt and P carry the output scale.
+//   then T' and P (fast: fp16; precise: bf16 hi, lo; all fragT), then e^{G_15} - 1 (DK fp32).
+//   Qt and P carry the output scale.  |P| <= |q| |k| <= 1 for L2-normalised q, k, inside fp16.
 // An all-zero record is the identity step (W = 0, S unchanged), which lets the state pass run
 // every chunk as four blocks without branches: blocks past a sequence's end read zeros.
 template <int DK, bool PRECISE>
@@ -170,7 +170,7 @@ struct Rec {
     static constexpr int NA = PRECISE ? 6 : 3;
     static constexpr int OFF_T = NA * E * 2;
     static constexpr int OFF_P = OFF_T + (PRECISE ? 1024 : 512);
-    static constexpr int OFF_G = OFF_P + 1024;
+    static constexpr int OFF_G = OFF_P + (PRECISE ? 1024 : 512);
     static constexpr int BYTES = OFF_G + DK * 4;
     static_assert(BYTES % 16 == 0, "record alignment");
 };
@@ -262,6 +262,7 @@ __device__ __forceinline__ bool locate_slot(const ChunkArgs& p, int64_t slot, in
 // ============================================================================================
 template <int DK, int IDT, int GDT, bool PRECISE, bool GATE>
 __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
+    static_assert(PRECISE, "16-bit inputs use chunk_intra_tok_kernel");
     using R = Rec<DK, PRECISE>;
     constexpr int PH = DK / 64;           // the channels are processed in phases of 64
     constexpr int LE = BLK * 64;          // elements of one [16][64] LDS operand array
@@ -763,19 +764,15 @@ __global__ void __launch_bounds__(64, 4) chunk_intra_tok_kernel(ChunkArgs p, int
     }
     const f32x4 accA = accA0 + accA1, accP = accP0 + accP1;
 
-    // ---- A to LDS (for the substitution), P staged as bf16 hi / lo; lane (m, q) holds rows
-    // 4q + i of column m
+    // ---- A to LDS (for the substitution), P staged in fp16; lane (m, q) holds rows 4q + i of
+    // column m
     uint16_t* const tT = reinterpret_cast<uint16_t*>(sTail);
-    uint16_t* const Ph = reinterpret_cast<uint16_t*>(sTail + (R::OFF_P - R::OFF_T));
-    uint16_t* const Pl = Ph + 256;
+    uint16_t* const tP = reinterpret_cast<uint16_t*>(sTail + (R::OFF_P - R::OFF_T));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * q + i, sc = m;
         sA[r][sc] = (sc < r) ? accA[i] * sBeta[r] : 0.f;
-        const float pval = (sc <= r) ? accP[i] : 0.f;
-        const uint16_t ph = bf16_bits(pval);
-        Ph[fragT(r, sc)] = ph;
-        Pl[fragT(r, sc)] = bf16_bits(pval - bf16_val(ph));
+        tP[fragT(r, sc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>((sc <= r) ? accP[i] : 0.f));
     }
     wave_fence();   // sA and sBeta are read across lanes below
 
@@ -1075,8 +1072,9 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
             const uint8_t* rb = buf + b * R::BYTES;
             if (b + 1 < NB) load_fa(rb + R::BYTES, fn);
             const uint16_t* Tp = reinterpret_cast<const uint16_t*>(rb + R::OFF_T) + 4 * lane;
-            const s16x4 ph = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 8 * lane);
-            const s16x4 pl = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 512 + 8 * lane);
+            const s16x4 ph = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 8 * lane);   // fast: fp16 P
+            s16x4 pl;
+            if constexpr (PRECISE) pl = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 512 + 8 * lane);
             const float* gam = reinterpret_cast<const float*>(rb + R::OFF_G);   // e^{G_15} - 1
             float4 gm[CT];
 #pragma unroll
@@ -1131,8 +1129,15 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
             }
             // O += P W (P and Qt carry the output scale)
             s16x4 wh, wl;
-            split4(W, wh, wl);
-            O = mfma16_bf16_x3(ph, pl, wh, wl, O);
+            f16x4 w16;
+            if constexpr (!PRECISE) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w16[i] = static_cast<_Float16>(W[i]);
+                O = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ph), w16, O, 0, 0, 0);
+            } else {
+                split4(W, wh, wl);
+                O = mfma16_bf16_x3(ph, pl, wh, wl, O);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int off = ((16 * b + 4 * lq + i) * vstride + n0 + ln) * OSZ;
@@ -1144,9 +1149,6 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
             // S <- Diag(e^{G_15}) S + Kb^T W = S + Diag(e^{G_15} - 1) S + Kb^T W
             if constexpr (!PRECISE) {
                 const uint8_t* kbt = rb + 2 * E2 + 8 * lane;   // frag16 Kb^T
-                f16x4 w16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w16[i] = static_cast<_Float16>(W[i]);
 #pragma unroll
                 for (int i = 0; i < CT; ++i) {
                     const f16x4 ka = *reinterpret_cast<const f16x4*>(kbt + 512 * i);

@@ -120,9 +120,9 @@ def test_workspace_size(lib):
     # the bf16 prefill workload runs unsegmented; the long one (1 x 65536 tokens, 32 heads) and
     # the packed one (8 sequences, 2^20 tokens, 8 heads) are segmented
     bf = K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128)
-    assert bf == ((1024 + 5) * 16 * 14336 + 255) // 256 * 256
+    assert bf == ((1024 + 5) * 16 * 13824 + 255) // 256 * 256
     for n, tok, H in [(1, 1 << 16, 32), (8, 1 << 20, 8)]:
-        area = ((tok // 16 + n + 1) * H * 14336 + 255) // 256 * 256
+        area = ((tok // 16 + n + 1) * H * 13824 + 255) // 256 * 256
         assert K.kda_chunk_fwd_workspace_size(n, tok, H, 128, 128) == \
             area + (tok // 8192 + n + 1) * H * 128 * 384 * 4
     f32 = K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128, in_dtype=torch.float32)
