@@ -246,6 +246,31 @@ def test_fused_gate_parity_full_size():
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("case", ["g_bf16", "g_bf16_dk64", "z_f32", "z_f32_dk64"])
+def test_prefill_gate_input_dtypes(case):
+    """bf16 q, k, v, beta with g given in bf16 (kda_chunk_fwd), or with z given in fp32 through the
+    fused gate; both sides consume the same stored values."""
+    dk = 64 if case.endswith("dk64") else 128
+    d = prefill_case("prefill_bf16", B=2, H=3, T=300, dk=dk, dv=128)
+    say("gate input dtypes", case)
+    h0 = d["S0"].to(DEV)
+    qkvb = [d[x].to(DEV) for x in ("q", "k", "v", "beta")]
+    if case.startswith("g_bf16"):
+        g = oracle_g(d, torch.bfloat16)
+        o, hT = K.kda_chunk_fwd(*qkvb, g.to(DEV), initial_state=h0, o_dtype=torch.float32)
+        g_ref = g
+    else:
+        z32 = d["z"].to(torch.float32)
+        o, hT = K.kda_chunk_fwd_gated(*qkvb, d["A"].to(DEV), z32.to(DEV), initial_state=h0,
+                                      o_dtype=torch.float32)
+        g_ref = oracle.gate(d["A"], z32)
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = oracle.forward(d["q"], d["k"], d["v"], d["beta"], g_ref, S0=d["S0"])
+    eo, es = rel_err(o, o_ref), rel_err(hT, S_ref)
+    say(f"  o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_fused_gate_f32_config():
     d = prefill_case("prefill_f32_small")
     o, hT = _gated(d)
