@@ -60,6 +60,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BLK = 16;     // tokens per block (one state step)
 constexpr int STATE_WAVES = 4;   // waves per state-kernel workgroup (16 state columns each)
+constexpr int STATE_SLICES = 2;  // slices a chunk's transfers are issued in (at most NB - 1)
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -1008,10 +1009,11 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     };
     // Chunk c's records and its V slice go straight from memory into an LDS buffer (records past
     // the sequence's last block, V rows past its last token, and the padding read as zeros:
-    // identity steps).  The transfers are issued in NB - 1 slices, one at the start of each
-    // block but the last, so that they do not queue up in front of the block computations.
+    // identity steps).  The transfers are issued in NSLICE slices, one at the start of each of the
+    // chunk's first blocks: all at once they collide with the blocks' own LDS reads (measured
+    // slower), in three slices fewer bytes are in flight.
     constexpr int NITEM = ROUNDS + VROUNDS;
-    constexpr int NSLICE = NB - 1;
+    constexpr int NSLICE = STATE_SLICES < NB ? STATE_SLICES : NB - 1;
     auto prefetch_slice = [&](uint8_t* buf, int64_t c, int slice) {
         const int nt = tokens_in(c);
         const int nbk = (nt + BLK - 1) / BLK;
@@ -1180,9 +1182,10 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     };
 
     // Each half-iteration runs the current chunk while the next chunk's transfers go out, then
-    // waits for those transfers -- the o stores of the chunk's last two blocks (4 each) may stay
-    // in flight, every load is older -- and meets the other waves at the barrier.
-    constexpr int WAIT_LOADS = vmcnt_imm(8);
+    // waits for those transfers -- the o stores of the blocks from the one that issued the last
+    // slice on (4 each) may stay in flight, every load is older -- and meets the other waves at
+    // the barrier.
+    constexpr int WAIT_LOADS = vmcnt_imm(4 * (NB - NSLICE + 1));
 #pragma unroll
     for (int sl = 0; sl < NSLICE; ++sl) prefetch_slice(bufA, c_begin, sl);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
