@@ -271,6 +271,28 @@ def test_prefill_gate_input_dtypes(case):
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("g_min", [-1.0, -2.5])
+def test_fused_gate_other_g_min(g_min):
+    """The gate bound g_min is a parameter (any value in [-5, 0)): the fused prefill with a milder
+    bound, and the standalone gate with it, against the fp64 oracle; the fused path still equals
+    kda_gate followed by kda_chunk_fwd bit for bit."""
+    d = prefill_case("prefill_bf16", B=2, H=3, T=200)
+    say("fused gate g_min", g_min)
+    qkvb = [d[x].to(DEV) for x in ("q", "k", "v", "beta")]
+    A, z, h0 = d["A"].to(DEV), d["z"].to(DEV), d["S0"].to(DEV)
+    o, hT = K.kda_chunk_fwd_gated(*qkvb, A, z, g_min=g_min, initial_state=h0, o_dtype=torch.float32)
+    g = K.kda_gate(A, z, g_min=g_min)
+    o2, h2 = K.kda_chunk_fwd(*qkvb, g, initial_state=h0, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(hT, h2)
+    g64 = oracle.gate(d["A"], d["z"], g_min=g_min)
+    assert rel_err(g, g64) <= 1e-6
+    o_ref, S_ref, _ = oracle.forward(d["q"], d["k"], d["v"], d["beta"], g64, S0=d["S0"])
+    eo, es = rel_err(o, o_ref), rel_err(hT, S_ref)
+    say(f"  o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_fused_gate_f32_config():
     d = prefill_case("prefill_f32_small")
     o, hT = _gated(d)
