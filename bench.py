@@ -7,8 +7,9 @@ the intra-block work and the state pass, from A and z (bf16) to o (bf16) and the
 and reported under "unfused".  Inputs are synthetic (seeded generators, the workload's shapes
 and distributions) and resident in HBM before the timed region starts.  The decode workload
 (256 sequences x 32 heads, 64 in-place steps, plus speculative-decode verify and commit) is
-timed in the same run and reported under "decode", and the long workload (1 x 65536 tokens, 32
-heads, run in 8192-token segments) under "long_prefill".
+timed in the same run and reported under "decode", the long workload (1 x 65536 tokens, 32
+heads, run in 8192-token segments) under "long_prefill", and the packed workload (8 sequences of
+seeded log-uniform lengths summing to 2^20 tokens, 8 heads, cu_seqlens) under "packed_prefill".
 
 Prints ONE JSON line.  ``value`` is prefill tokens/s (B*T tokens per step / step time).
 ``roofline`` describes the step's one operation, kda_chunk_fwd_gated (its two kernels: the
@@ -58,8 +59,9 @@ def parse():
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the long-sequence prefill leg")
+    ap.add_argument("--no-packed", action="store_true", help="skip the packed-batch prefill leg")
     ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--mode", choices=("all", "prefill", "decode"), default="all",
+    ap.add_argument("--mode", choices=("all", "prefill", "decode", "packed"), default="all",
                     help="prefill / decode: run only that workload and print no JSON line "
                          "(for profiler counter passes)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -232,6 +234,46 @@ def run_long(args, dev, inputs, K, stream):
             "frac_hbm": round(alg / (ms * 1e-3) / HBM_PEAK, 4)}
 
 
+def run_packed(args, dev, inputs, K, stream, reps=5):
+    """The packed workload: 8 sequences of seeded log-uniform lengths summing to 2^20 tokens, 8
+    heads, per-sequence initial states, packed with cu_seqlens (every sequence runs in 8192-token
+    segments).  kda_chunk_fwd_gated, timed with HIP events over `reps` calls."""
+    cfg = inputs.config("prefill_varlen")
+    log("generating", cfg)
+    d = inputs.make_prefill(cfg)
+    q, k, v, beta, z = (d[x].to(dev) for x in ("q", "k", "v", "beta", "z"))
+    A, S0, cu = d["A"].to(dev), d["S0"].to(dev), d["cu_seqlens"].to(dev)
+    lens = d["cu_seqlens"].diff().tolist()
+    del d
+    T, H, dk, dv = q.shape[1], cfg.H, cfg.dk, cfg.dv
+    N = len(lens)
+    o = torch.empty((1, T, H, dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty_like(S0)
+    ws = torch.empty(K.kda_chunk_fwd_workspace_size(N, T, H, dk, dv), dtype=torch.uint8,
+                     device=dev)
+
+    def call():
+        K.kda_chunk_fwd_gated(q, k, v, beta, A, z, initial_state=S0, final_state=hT,
+                              cu_seqlens=cu, o=o, workspace=ws, stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    alg = T * H * FUSED_BYTES_PER_TH + H * dk * 4 + 2 * N * H * dk * dv * 4
+    return {"config": f"{N} packed sequences (lengths {', '.join(str(x) for x in lens)}), "
+                      f"{T} tokens, {H} heads, d_k=d_v={dk}, bf16, gate fused",
+            "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "algorithmic_gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(alg / (ms * 1e-3) / HBM_PEAK, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -258,6 +300,10 @@ def main():
     if args.mode == "decode":
         r = run_decode(args, dev, inputs, K, torch.cuda.current_stream())
         log(f"decode: {r['ms_per_step']:.4f} ms/step; spec decode {r['spec_decode']}")
+        return
+    if args.mode == "packed":
+        r = run_packed(args, dev, inputs, K, torch.cuda.current_stream(), reps=args.steps)
+        log(f"packed prefill: {r['ms_per_call']:.4f} ms/call, {r['tokens_per_s']:.0f} tokens/s")
         return
 
     # ------------------------------------------------------------------ prefill workload
@@ -332,6 +378,7 @@ def main():
 
     dec = run_decode(args, dev, inputs, K, stream)
     long_ = None if args.no_long else run_long(args, dev, inputs, K, stream)
+    packed = None if args.no_packed else run_packed(args, dev, inputs, K, stream)
     copy_bps = copy_ceiling(dev, stream)
     dec["roofline"]["frac_of_copy"] = round(dec["roofline"]["achieved"] * 1e9 / copy_bps, 4)
 
@@ -384,6 +431,7 @@ def main():
                     "tokens_per_s": round(tokens / ((gate_avg + chunk_avg) * 1e-3), 1)},
         "decode": dec,
         "long_prefill": long_,
+        "packed_prefill": packed,
         "copy_ceiling_gbs": round(copy_bps / 1e9, 1),
         "cpu_baseline": cpu,
     }
