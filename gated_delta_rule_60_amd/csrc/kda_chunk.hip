@@ -1219,13 +1219,20 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
 
 // Segment scan: one workgroup per (sequence, head, 16 state columns) walks the sequence's
 // segments, S_start(s + 1) = M_s S_start(s) + B_s for s = 1 .. nseg - 2, in fp32.  The column
-// blocks are independent (M acts on the rows), so they run apart.  The next step's M is loaded
-// into registers (16-byte loads) while the current step computes.
+// blocks are independent (M acts on the rows), so they run apart.  Each step is a d_k x d_k by
+// d_k x 16 product on fp32 MFMAs (16x16x4): wave w owns output row tiles w, w + 4, ..., B_s seeds
+// the accumulators, S_start(s) is read from LDS (double-buffered, one barrier per step), and the
+// next step's M rows and B are loaded into registers while the current step computes.
+// MFMA step (m, e) of a tile contracts over the four columns 16 m + 4 c + e, c = 0..3: lane
+// (i, c) supplies M[row i][16 m + 4 c + e] from its float4 of M[row i][16 m + 4 c .. + 3], and
+// S_start[16 m + 4 c + e][j] for lane (j, c) comes from LDS.
 template <int DK>
 __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) {
-    constexpr int NM = DK * DK / 4 / 256;            // float4s of M per thread
-    __shared__ float sM[DK][DK + 1];
-    __shared__ float sS[DK][16];
+    constexpr int NT = DK / 16;                      // row tiles
+    constexpr int TPW = NT / 4;                      // row tiles per wave
+    constexpr int NM = DK / 16;                      // float4s of one M row a lane holds
+    constexpr int SP = 17;                           // LDS row pitch of S_start (floats)
+    __shared__ float sS[2][DK * SP];
     const int DV = p.dv, ncb = DV / 16;
     const int64_t H = p.H;
     const int cb = static_cast<int>(blockIdx.x % ncb);
@@ -1241,47 +1248,71 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
     }
     const int64_t nseg = seg_count(len);
     if (nseg < 3) return;                             // no middle segment: nothing to combine
-    const int t = threadIdx.x;
-    const int i = t >> 1, j0 = (t & 1) * 8;         // this thread: row i, columns j0 .. j0+7
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int li = lane & 15, lc = lane >> 4;         // row / column within a tile; K group
     auto m_of = [&](int64_t s) { return sg.M + ((slot0 + s) * H + h) * DK * DK; };
-    float4 mr[NM];
-    auto load_m = [&](int64_t s) {
-        const float4* src = reinterpret_cast<const float4*>(m_of(s));
+    auto b_of = [&](int64_t s) { return sg.B + ((slot0 + s) * H + h) * DK * DV + cb * 16; };
+
+    float4 mr[TPW][NM];                               // this lane's M values of the wave's tiles
+    f32x4 br[TPW];                                    // B seeds: rows 16 r + 4 lc + v, column li
+    auto load_step = [&](int64_t s) {
+        const float* M = m_of(s);
+        const float* Bm = b_of(s);
 #pragma unroll
-        for (int u = 0; u < NM; ++u) mr[u] = src[u * 256 + t];
+        for (int q = 0; q < TPW; ++q) {
+            const int r = wave + 4 * q;
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                mr[q][m] = *reinterpret_cast<const float4*>(M + (16 * r + li) * DK + 16 * m + 4 * lc);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) br[q][v] = Bm[static_cast<int64_t>(16 * r + 4 * lc + v) * DV + li];
+        }
     };
-    const float* S1 = sg.S + ((slot0 + 1) * H + h) * DK * DV + cb * 16;
-    for (int e = t; e < DK * 16; e += 256) sS[e >> 4][e & 15] = S1[(e >> 4) * DV + (e & 15)];
-    load_m(1);
+    {
+        const float* S1 = sg.S + ((slot0 + 1) * H + h) * DK * DV + cb * 16;
+        for (int e = t; e < DK * 16; e += 256) sS[0][(e >> 4) * SP + (e & 15)] = S1[(e >> 4) * DV + (e & 15)];
+    }
+    load_step(1);
+    __syncthreads();
+    int cur = 0;
     for (int64_t s = 1; s + 1 < nseg; ++s) {
-        const float* Bm = sg.B + ((slot0 + s) * H + h) * DK * DV + cb * 16;
-        __syncthreads();                             // sS written, the previous sM reads done
+        f32x4 acc[TPW];
+        float4 mc[TPW][NM];
 #pragma unroll
-        for (int u = 0; u < NM; ++u) {
-            const int e = 4 * (u * 256 + t), r = e / DK, c = e % DK;
-            sM[r][c] = mr[u].x; sM[r][c + 1] = mr[u].y; sM[r][c + 2] = mr[u].z; sM[r][c + 3] = mr[u].w;
+        for (int q = 0; q < TPW; ++q) {
+            acc[q] = br[q];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) mc[q][m] = mr[q][m];
         }
-        __syncthreads();
-        if (s + 2 < nseg) load_m(s + 1);             // in flight during this step
-        float acc[8];
-        if (i < DK) {
+        if (s + 2 < nseg) load_step(s + 1);          // in flight during this step
+        const float* Sc = sS[cur];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) acc[jj] = Bm[static_cast<int64_t>(i) * DV + j0 + jj];
-            for (int k = 0; k < DK; ++k) {
-                const float m = sM[i][k];
+        for (int m = 0; m < NM; ++m)
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) acc[jj] = fmaf(m, sS[k][j0 + jj], acc[jj]);
+            for (int e = 0; e < 4; ++e) {
+                const float sb = Sc[(16 * m + 4 * lc + e) * SP + li];
+#pragma unroll
+                for (int q = 0; q < TPW; ++q) {
+                    const float4& a4 = mc[q][m];
+                    const float av = e == 0 ? a4.x : e == 1 ? a4.y : e == 2 ? a4.z : a4.w;
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, sb, acc[q], 0, 0, 0);
+                }
+            }
+        float* dst = sg.S + ((slot0 + s + 1) * H + h) * DK * DV + cb * 16;
+        float* Sn = sS[cur ^ 1];
+#pragma unroll
+        for (int q = 0; q < TPW; ++q) {
+            const int r = wave + 4 * q;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = 16 * r + 4 * lc + v;
+                Sn[row * SP + li] = acc[q][v];
+                dst[static_cast<int64_t>(row) * DV + li] = acc[q][v];
             }
         }
-        __syncthreads();                             // every read of sS done
-        if (i < DK) {
-            float* dst = sg.S + ((slot0 + s + 1) * H + h) * DK * DV + cb * 16 + static_cast<int64_t>(i) * DV;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                sS[i][j0 + jj] = acc[jj];
-                dst[j0 + jj] = acc[jj];
-            }
-        }
+        __syncthreads();                             // S_start(s + 1) complete in LDS
+        cur ^= 1;
     }
 }
 
