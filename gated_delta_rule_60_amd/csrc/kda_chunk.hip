@@ -93,6 +93,11 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
     const float r1 = x1 - __uint_as_float(hi & 0xffff0000u);
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
 }
+// Staged tiles are written as 16-bit (or fp32) elements and read back as whole 16-byte units:
+// the reads go through may_alias types, or type-based alias analysis may take the element stores
+// for dead (nothing of their type reads them before the next group overwrites them).
+typedef uint4 __attribute__((may_alias)) uint4_ma;
+typedef float4 __attribute__((may_alias)) float4_ma;
 __device__ __forceinline__ uint32_t f16_pair(float x0, float x1) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, f16x2));
 }
@@ -158,20 +163,26 @@ __device__ __forceinline__ int frag32(int r, int c) {
 __device__ __forceinline__ int frag16(int c, int t) { return ((c >> 4) * 64 + (c & 15) + 16 * (t >> 2)) * 4 + (t & 3); }
 __device__ __forceinline__ int fragT(int r, int s) { return (r + 16 * (s >> 2)) * 4 + (s & 3); }
 
-// Record of one (head, block) in the workspace (byte offsets).  E = 16 * DK elements per array.
-//   fast   : [Kt fp16 frag32][Qt fp16 frag32][Kb^T fp16 frag16]
-//   precise: [Kt hi][Kt lo][Qt hi][Qt lo] (bf16 frag32) [Kb^T hi][Kb^T lo] (bf16 frag16)
-//   then T' and P (fast: fp16; precise: bf16 hi, lo; all fragT), then e^{G_15} - 1 (DK fp32).
+// Record of one (head, block slot) in the workspace (byte offsets).  E = 16 * DK elements per
+// array.  A fast record covers 32 tokens: two 16-token sub-blocks, one 32-token state step; a
+// precise record covers one 16-token block.
+//   fast   : per sub-block s = 0, 1: [Kt fp16 frag32][Qt fp16 frag32][Kb^T fp16 frag16]; then
+//            T'_00, T'_10, T'_11 and P_00, P_10, P_11 (fp16 fragT, [row sub-block][column
+//            sub-block]); then e^{G_31} - 1 (DK fp32).  Kt, Qt are scaled from the record's first
+//            token, Kb from its last, so every exponent is <= 0.
+//   precise: [Kt hi][Kt lo][Qt hi][Qt lo] (bf16 frag32) [Kb^T hi][Kb^T lo] (bf16 frag16), then T'
+//            and P (bf16 hi, lo; fragT), then e^{G_15} - 1 (DK fp32).
 //   Qt and P carry the output scale.  |P| <= |q| |k| <= 1 for L2-normalised q, k, inside fp16.
 // An all-zero record is the identity step (W = 0, S unchanged), which lets the state pass run
-// every chunk as four blocks without branches: blocks past a sequence's end read zeros.
+// every chunk as two records without branches: records past a sequence's end read zeros.
 template <int DK, bool PRECISE>
 struct Rec {
+    static constexpr int TOK = PRECISE ? 16 : 32;       // tokens per record
     static constexpr int E = BLK * DK;
-    static constexpr int NA = PRECISE ? 6 : 3;
+    static constexpr int NA = 6;                        // 16-bit [16][DK] arrays
     static constexpr int OFF_T = NA * E * 2;
-    static constexpr int OFF_P = OFF_T + (PRECISE ? 1024 : 512);
-    static constexpr int OFF_G = OFF_P + (PRECISE ? 1024 : 512);
+    static constexpr int OFF_P = OFF_T + (PRECISE ? 1024 : 1536);
+    static constexpr int OFF_G = OFF_P + (PRECISE ? 1024 : 1536);
     static constexpr int BYTES = OFF_G + DK * 4;
     static_assert(BYTES % 16 == 0, "record alignment");
 };
@@ -230,32 +241,34 @@ __device__ __forceinline__ void store_words(void* dst, const uint32_t (&w)[NP]) 
     else *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
 }
 
-// Locate the block slot of a workgroup: sequence n, block j inside it, or false when the slot
-// is past its sequence's end.  Slot bases: n * ceil(T/16) for fixed-length batches,
-// floor(cu[n]/16) + n for packed ones (ceil(len/16) <= floor(len/16) + 1 keeps them disjoint).
+// Locate the record slot of a workgroup: sequence n, record j inside it (TOK tokens each), or
+// false when the slot is past its sequence's end.  Slot bases: n * ceil(T/TOK) for fixed-length
+// batches, floor(cu[n]/TOK) + n for packed ones (ceil(len/TOK) <= floor(len/TOK) + 1 keeps them
+// disjoint).
+template <int TOK>
 __device__ __forceinline__ bool locate_slot(const ChunkArgs& p, int64_t slot, int& n,
                                             int64_t& j, int64_t& bos, int64_t& len) {
     if (p.cu) {
         int lo = 0, hi = p.n_seqs - 1;
         while (lo < hi) {                 // largest n with base(n) <= slot
             const int mid = (lo + hi + 1) >> 1;
-            const int64_t base = static_cast<int64_t>(p.cu[mid] / BLK) + mid;
+            const int64_t base = static_cast<int64_t>(p.cu[mid] / TOK) + mid;
             if (base <= slot) lo = mid; else hi = mid - 1;
         }
         n = lo;
         bos = p.cu[n];
         len = static_cast<int64_t>(p.cu[n + 1]) - bos;
-        j = slot - (static_cast<int64_t>(p.cu[n] / BLK) + n);
+        j = slot - (static_cast<int64_t>(p.cu[n] / TOK) + n);
     } else {
-        const int64_t nblk = (p.T + BLK - 1) / BLK;
-        if (nblk == 0) return false;
-        n = static_cast<int>(slot / nblk);
-        j = slot % nblk;
+        const int64_t nrec = (p.T + TOK - 1) / TOK;
+        if (nrec == 0) return false;
+        n = static_cast<int>(slot / nrec);
+        j = slot % nrec;
         if (n >= p.n_seqs) return false;
         bos = static_cast<int64_t>(n) * p.T;
         len = p.T;
     }
-    return j >= 0 && BLK * j < len;
+    return j >= 0 && TOK * j < len;
 }
 
 // ============================================================================================
@@ -293,7 +306,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
     const int h = static_cast<int>(blockIdx.x % H);
     int n;
     int64_t j, bos, len;
-    if (!locate_slot(p, slot, n, j, bos, len)) return;
+    if (!locate_slot<BLK>(p, slot, n, j, bos, len)) return;
     const int64_t t0 = BLK * j;
     const int nt = static_cast<int>((len - t0) < BLK ? (len - t0) : BLK);
     uint8_t* rec = ws + (static_cast<int64_t>(h) * nslots + slot) * R::BYTES;
@@ -468,7 +481,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
 #pragma unroll
             for (int u = 0; u < WIN / 1024; ++u)
                 *reinterpret_cast<uint4*>(rec + a * 2 * R::E + WIN * ph + (64 * u + lane) * 16) =
-                    *reinterpret_cast<const uint4*>(stg + a * WIN + (64 * u + lane) * 16);
+                    *reinterpret_cast<const uint4_ma*>(stg + a * WIN + (64 * u + lane) * 16);
     }
     // T' and P are staged too, then written with e^{G_15} - 1 already in place: bytes
     // [OFF_T, OFF_G) of the record
@@ -499,7 +512,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
         float t[16];
         float4 nxt[4], cur[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) nxt[u] = *reinterpret_cast<const float4*>(&sA[1][4 * u]);
+        for (int u = 0; u < 4; ++u) nxt[u] = *reinterpret_cast<const float4_ma*>(&sA[1][4 * u]);
         t[0] = (jc == 0) ? 1.f : 0.f;
 #pragma unroll
         for (int r = 1; r < 16; ++r) {
@@ -508,7 +521,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
             if (r + 1 < 16) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (4 * u < r + 1) nxt[u] = *reinterpret_cast<const float4*>(&sA[r + 1][4 * u]);
+                    if (4 * u < r + 1) nxt[u] = *reinterpret_cast<const float4_ma*>(&sA[r + 1][4 * u]);
             }
             float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -535,30 +548,36 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
     }
     __syncthreads();   // T' and P staged
     for (int j = lane; j < TAIL / 16; j += 64)
-        *reinterpret_cast<uint4*>(rec + R::OFF_T + 16 * j) = *reinterpret_cast<const uint4*>(stg + 16 * j);
+        *reinterpret_cast<uint4*>(rec + R::OFF_T + 16 * j) = *reinterpret_cast<const uint4_ma*>(stg + 16 * j);
 }
 
 // LDS ordering inside a one-wave workgroup: a wave's LDS operations execute in order, so only the
 // compiler must keep them in place.  A wavefront-scope fence does that and emits no wait (a
-// workgroup barrier's fence would also wait for every transfer still in flight).
+// workgroup barrier's fence would also wait for every transfer in flight).
 __device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
 // ============================================================================================
-// 1b. intra-block kernel for 16-bit inputs: one wave per (block slot, head), token per lane
+// 1b. intra-block kernel for 16-bit inputs: one wave per (32-token record slot, head)
 // ============================================================================================
-// Lane (m, q) owns token m = lane & 15 of the block and, in every 32-channel group kk, the eight
-// channels 32 kk + 16 (j >> 2) + 4 q + (j & 3), j = 0..7 -- exactly the channels its 16-byte unit of
-// a frag32 record array holds.  Therefore:
-//   * the block cumsum runs across the 16 lanes of a row (DPP shifts), G_15 is lane 15's value;
-//   * A = beta * strict_lower(Kt Kd^T) and P = lower(Qt Kd^T) are fp32 MFMAs (16x16x4) fed straight
-//     from the registers: step (kk, j) contracts the four channels the lanes of rows q = 0..3 own,
-//     so the channel order of the contraction is the record's and no operand is split or staged;
-//   * each lane's fp16 Kt and Qt values are its frag32 units: whole 1 KB wave stores.
-// Only Kb^T (channel-major) goes through LDS.  Same record, same arithmetic per element as the
-// split-operand kernel except the cumsum's association (a prefix tree instead of a running sum).
+// A record covers two 16-token sub-blocks s = 0, 1.  Lane (m, q) owns token m of each sub-block
+// and, in every 32-channel group kk, the eight channels 32 kk + 16 (j >> 2) + 4 q + (j & 3),
+// j = 0..7 -- exactly the channels its 16-byte unit of a frag32 record array holds.  Therefore:
+//   * each sub-block's cumsum runs across the 16 lanes of a row (DPP shifts); G_15 is lane 15's;
+//   * A_ss = beta * strict_lower(Kt_s Kd_s^T) and P_ss = lower(Qt_s Kd_s^T) are fp32 MFMAs
+//     (16x16x4) fed straight from the registers, with each sub-block's own cumsum, so that no
+//     factor exceeds e^80;
+//   * the cross-sub-block terms use factors <= 1 only: with Kb_0 = e^{G_15 - G} K of sub-block 0,
+//     C = Kt_1 Kb_0^T gives A_10 = Diag(beta_1) C and P_10 = Qt_1 Kb_0^T, on fp16 16x16x32
+//     MFMAs (fp16 operands, as the state pass uses them);
+//   * T' of the record is block lower-triangular: T'_00 and T'_11 by forward substitution, and
+//     T'_10 = -T'_11 C T'_00, the lower-left block of the inverse;
+//   * the record's Kt_1 and Qt_1 are scaled by sub-block 0's e^{G_15} (from the record's first
+//     token) and its Kb_0 by sub-block 1's (to the record's last token).
+// Kt and Qt leave as whole 1 KB wave stores from registers; Kb^T (channel-major) goes through LDS.
 template <int DK, int GDT, bool GATE>
-__global__ void __launch_bounds__(64, 4) chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
+__global__ void __launch_bounds__(64, 3) chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     using R = Rec<DK, false>;
+    constexpr int TOKR = R::TOK;          // tokens per record: two sub-blocks
     constexpr int KS = DK / 32;           // 32-channel groups
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr int E2 = 2 * R::E;          // bytes of one 16-bit record array
@@ -568,21 +587,25 @@ __global__ void __launch_bounds__(64, 4) chunk_intra_tok_kernel(ChunkArgs p, int
     constexpr int GSZ = (GDT == KDA_F32) ? 4 : 2;
     constexpr int CPR = 64 * 2 / 16;      // 16-byte chunks per row of a bf16 phase tile
     constexpr int CPRG = 64 * GSZ / 16;   // ... of the g / z phase tile
-    constexpr int TB = BLK * 64 * 2;      // bytes of a bf16 phase tile
-    constexpr int TBG = BLK * 64 * GSZ;   // bytes of the g / z phase tile
+    constexpr int TB = TOKR * 64 * 2;     // bytes of a bf16 phase tile
+    constexpr int TBG = TOKR * 64 * GSZ;  // bytes of the g / z phase tile
     constexpr int PB = 2 * TB + TBG;      // bytes of one phase's inputs: k, q, g / z
-    // Inputs arrive by direct-to-LDS loads, whole lines per instruction, into [16][64]-channel
-    // phase tiles whose 16-byte chunks are XOR-swizzled by row: slot(m, c) = m * CPR + (c ^ m').
+    // Inputs arrive by direct-to-LDS loads, whole lines per instruction, into [32][64]-channel
+    // phase tiles whose 16-byte chunks are XOR-swizzled by row: slot(r, c) = r * CPR + (c ^ r').
     // Each lane then reads its own channels without bank conflicts.
     __shared__ __attribute__((aligned(16))) uint8_t sIn[PB];          // one phase's tiles
-    __shared__ __attribute__((aligned(16))) uint16_t sKb[BLK * 32];     // Kb^T of one group, frag16
+    __shared__ __attribute__((aligned(16))) uint16_t sKb[2][BLK * 32];  // Kb^T of one group, frag16
     __shared__ __attribute__((aligned(16))) float sRate[GATE ? DK : 4];
-    __shared__ float sBeta[16];
-    // after the last group the input tiles are dead: A (fp32 16 x 16) and the staged T', P hi,
-    // P lo (fragT) reuse them
-    static_assert(1024 + TAIL <= PB, "staging fits the input tiles");
-    float (*const sA)[16] = reinterpret_cast<float (*)[16]>(sIn);
-    uint8_t* const sTail = sIn + 1024;
+    __shared__ float sBeta[TOKR];
+    // After the last group the input tiles are dead and hold: A_00, A_11, C, T'_00 and T'_11 in
+    // fp32 (for the cross product), the product C T'_00, then the staged T' and P tiles (fp16).
+    constexpr int O_C = 2048, O_TF = 3072, O_U = 5120, O_TAIL = 6144;
+    static_assert(O_TAIL + TAIL <= PB, "staging fits the input tiles");
+    float (*const sA)[16][16] = reinterpret_cast<float (*)[16][16]>(sIn);
+    float (*const sC)[16] = reinterpret_cast<float (*)[16]>(sIn + O_C);
+    float (*const sTf)[16][16] = reinterpret_cast<float (*)[16][16]>(sIn + O_TF);
+    float (*const sU)[16] = reinterpret_cast<float (*)[16]>(sIn + O_U);
+    uint8_t* const sTail = sIn + O_TAIL;
 
     const int lane = threadIdx.x;
     const int m = lane & 15, q = lane >> 4;
@@ -592,19 +615,19 @@ __global__ void __launch_bounds__(64, 4) chunk_intra_tok_kernel(ChunkArgs p, int
     const int h = static_cast<int>(blockIdx.x % H);
     int n;
     int64_t j0, bos, len;
-    if (!locate_slot(p, slot, n, j0, bos, len)) return;
-    const int64_t t0 = BLK * j0;
-    const int nt = static_cast<int>((len - t0) < BLK ? (len - t0) : BLK);
+    if (!locate_slot<TOKR>(p, slot, n, j0, bos, len)) return;
+    const int64_t t0 = TOKR * j0;
+    const int nt = static_cast<int>((len - t0) < TOKR ? (len - t0) : TOKR);
     uint8_t* rec = ws + (static_cast<int64_t>(h) * nslots + slot) * R::BYTES;
-    const bool live = m < nt;             // this lane's token exists
+    const float keep[2] = {m < nt ? 1.f : 0.f, 16 + m < nt ? 1.f : 0.f};   // the lane's tokens exist
 
     // ---- beta and A into registers, then every phase's tiles; beta and the gate rates go to LDS
     // afterwards (the compiler counts its own waits for them, and the per-phase waits below only
-    // need the older tile transfers done).  Rows past the block's last token read zeros: the
+    // need the older tile transfers done).  Rows past the record's last token read zeros: the
     // buffer ranges end there.
     const int64_t row0 = (bos + t0) * H + h;
     float av[GATE ? DK / 64 : 1];
-    // beta of token `lane`: lanes 16 .. 63 and tokens past the block fall outside the range
+    // beta of token `lane`: lanes 32 .. 63 and tokens past the record fall outside the range
     const float bval = bf16_val(__builtin_amdgcn_raw_buffer_load_b16(
         make_rsrc(static_cast<const uint16_t*>(p.beta) + row0, nt * static_cast<uint32_t>(H) * 2),
         lane * static_cast<uint32_t>(H) * 2, 0, 0));
@@ -618,13 +641,13 @@ __global__ void __launch_bounds__(64, 4) chunk_intra_tok_kernel(ChunkArgs p, int
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(static_cast<const uint16_t*>(p.q) + row0 * DK, nt * rowb);
     const __amdgpu_buffer_rsrc_t gr = make_rsrc(static_cast<const uint8_t*>(p.g) + row0 * DK * GSZ,
                                                 nt * rowb / 2 * GSZ);
-    // phase ph's k, q and g / z tiles into sIn: 1 KB per wave instruction, four or eight rows of
-    // whole lines, non-temporal (each input is read once)
+    // phase ph's k, q and g / z tiles into sIn: 1 KB per wave instruction, eight or sixteen rows
+    // of whole lines, non-temporal (each input is read once)
     auto load_phase = [&](int ph) {
 #pragma unroll
         for (int u = 0; u < TB / 1024; ++u) {
-            const int S = 64 * u + lane, mm = S / CPR, c = (S % CPR) ^ (mm & (CPR - 1));
-            const uint32_t off = mm * rowb + ph * 128 + 16 * c;
+            const int S = 64 * u + lane, rr = S / CPR, c = (S % CPR) ^ (rr & (CPR - 1));
+            const uint32_t off = rr * rowb + ph * 128 + 16 * c;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(sIn + 1024 * u),
                                                      16, off, 0, 0, CP_NT);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (__attribute__((address_space(3))) void*)(sIn + TB + 1024 * u),
@@ -632,36 +655,36 @@ __global__ void __launch_bounds__(64, 4) chunk_intra_tok_kernel(ChunkArgs p, int
         }
 #pragma unroll
         for (int u = 0; u < TBG / 1024; ++u) {
-            const int S = 64 * u + lane, mm = S / CPRG, c = (S % CPRG) ^ (mm & (CPRG - 1));
-            const uint32_t off = mm * (rowb / 2 * GSZ) + ph * 64 * GSZ + 16 * c;
+            const int S = 64 * u + lane, rr = S / CPRG, c = (S % CPRG) ^ (rr & (CPRG - 1));
+            const uint32_t off = rr * (rowb / 2 * GSZ) + ph * 64 * GSZ + 16 * c;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(gr, (__attribute__((address_space(3))) void*)(sIn + 2 * TB + 1024 * u),
                                                      16, off, 0, 0, CP_NT);
         }
     };
     load_phase(0);
-    if (lane < 16) sBeta[lane] = bval;
+    if (lane < TOKR) sBeta[lane] = bval;
     if constexpr (GATE) {   // one rate per (head, channel), shared through LDS
 #pragma unroll
         for (int i = 0; i < DK / 64; ++i) sRate[64 * i + lane] = gate_rate(av[i]);
     }
-    // token m's four channels 32 lk + 16 hf + 4 q .. + 3 of phase tile `tile` (bf16: 8 bytes)
-    auto tile_bf16 = [&](const uint8_t* tile, int lk, int hf) -> uint2 {
-        const int byte = (32 * lk + 16 * hf + 4 * q) * 2, c = byte >> 4;
-        return *reinterpret_cast<const uint2*>(tile + (m * CPR + (c ^ (m & (CPR - 1)))) * 16 + (byte & 15));
+    // token m of sub-block s: its four channels 32 lk + 16 hf + 4 q .. + 3 of phase tile `tile`
+    // (bf16: 8 bytes)
+    auto tile_bf16 = [&](const uint8_t* tile, int s, int lk, int hf) -> uint2 {
+        const int r = 16 * s + m, byte = (32 * lk + 16 * hf + 4 * q) * 2, c = byte >> 4;
+        return *reinterpret_cast<const uint2*>(tile + (r * CPR + (c ^ (r & (CPR - 1)))) * 16 + (byte & 15));
     };
-    auto tile_f32 = [&](const uint8_t* tile, int lk, int hf) -> uint4 {
-        const int c = 8 * lk + 4 * hf + q;
-        return *reinterpret_cast<const uint4*>(tile + (m * CPRG + (c ^ (m & (CPRG - 1)))) * 16);
+    auto tile_f32 = [&](const uint8_t* tile, int s, int lk, int hf) -> uint4 {
+        const int r = 16 * s + m, c = 8 * lk + 4 * hf + q;
+        return *reinterpret_cast<const uint4*>(tile + (r * CPRG + (c ^ (r & (CPRG - 1)))) * 16);
     };
     auto raw16 = [](const uint32_t* w, int j) -> float {      // element j of packed bf16 words
         return (j & 1) ? __uint_as_float(w[j >> 1] & 0xffff0000u) : __uint_as_float(w[j >> 1] << 16);
     };
     wave_fence();   // beta and the gate rates are read across lanes
 
-    // Per 32-channel group, in stages so that independent work covers each latency: the gate
-    // and the eight scans side by side, the factors, the G_15 broadcasts (LDS swizzles) issued
-    // together, the MFMAs (which do not need G_15) while they are in flight, then Kb.
-    f32x4 accA0 = zero4(), accA1 = zero4(), accP0 = zero4(), accP1 = zero4();
+    // Per 32-channel group, both sub-blocks side by side: the gate and the scans, the factors,
+    // the G_15 broadcasts (LDS swizzles) issued together, the MFMAs, then Kb.
+    f32x4 accA[2] = {zero4(), zero4()}, accP[2] = {zero4(), zero4()}, accC = zero4(), accQ = zero4();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
         const int ph = kk >> 1, lk = kk & 1;
@@ -670,20 +693,22 @@ __global__ void __launch_bounds__(64, 4) chunk_intra_tok_kernel(ChunkArgs p, int
             wave_fence();
         }
         const uint8_t* tk = sIn;
-        uint32_t rk[4], rq[4], rg[2 * (GSZ / 2) * 2];
+        uint32_t rk[2][4], rq[2][4], rg[2][2 * (GSZ / 2) * 2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const uint2 a = tile_bf16(tk, lk, hf), b = tile_bf16(tk + TB, lk, hf);
-            rk[2 * hf] = a.x; rk[2 * hf + 1] = a.y;
-            rq[2 * hf] = b.x; rq[2 * hf + 1] = b.y;
-            if constexpr (GSZ == 4) {
-                const uint4 g4 = tile_f32(tk + 2 * TB, lk, hf);
-                rg[4 * hf] = g4.x; rg[4 * hf + 1] = g4.y; rg[4 * hf + 2] = g4.z; rg[4 * hf + 3] = g4.w;
-            } else {
-                const uint2 g2 = tile_bf16(tk + 2 * TB, lk, hf);
-                rg[2 * hf] = g2.x; rg[2 * hf + 1] = g2.y;
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const uint2 a = tile_bf16(tk, s, lk, hf), b = tile_bf16(tk + TB, s, lk, hf);
+                rk[s][2 * hf] = a.x; rk[s][2 * hf + 1] = a.y;
+                rq[s][2 * hf] = b.x; rq[s][2 * hf + 1] = b.y;
+                if constexpr (GSZ == 4) {
+                    const uint4 g4 = tile_f32(tk + 2 * TB, s, lk, hf);
+                    rg[s][4 * hf] = g4.x; rg[s][4 * hf + 1] = g4.y; rg[s][4 * hf + 2] = g4.z; rg[s][4 * hf + 3] = g4.w;
+                } else {
+                    const uint2 g2 = tile_bf16(tk + 2 * TB, s, lk, hf);
+                    rg[s][2 * hf] = g2.x; rg[s][2 * hf + 1] = g2.y;
+                }
             }
-        }
         if (lk == 1 && ph + 1 < PH) {
             // the phase's tiles are read: the next phase's transfers overwrite them while this
             // group computes
@@ -691,99 +716,154 @@ __global__ void __launch_bounds__(64, 4) chunk_intra_tok_kernel(ChunkArgs p, int
             wave_fence();
             load_phase(ph + 1);
         }
-        float x[8], e1[8], kt[8], qt[8], kd[8], gm[8];
+        float x[2][8], e1[2][8], gm[2][8];
         float4 rate[2];
         if constexpr (GATE) {
-            rate[0] = *reinterpret_cast<const float4*>(&sRate[32 * kk + 4 * q]);
-            rate[1] = *reinterpret_cast<const float4*>(&sRate[32 * kk + 16 + 4 * q]);
+            rate[0] = *reinterpret_cast<const float4_ma*>(&sRate[32 * kk + 4 * q]);
+            rate[1] = *reinterpret_cast<const float4_ma*>(&sRate[32 * kk + 16 + 4 * q]);
         }
-        const float keep = live ? 1.f : 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            // g of token m (0 past the block's tokens, as in the unfused path's zero fill)
-            float gv;
-            if constexpr (GATE) {
-                const float z = (GDT == KDA_F32) ? __uint_as_float(rg[j]) : raw16(rg, j);
-                const float4& r4 = rate[j >> 2];
-                const float rt = (j & 3) == 0 ? r4.x : (j & 3) == 1 ? r4.y : (j & 3) == 2 ? r4.z : r4.w;
-                gv = gate_log_decay(rt, z, p.g_min) * keep;
-            } else if constexpr (GDT == KDA_F32) {
-                gv = __uint_as_float(rg[j]);
-            } else {
-                gv = raw16(rg, j);
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                // g of token m (0 past the record's tokens, as in the unfused path's zero fill)
+                float gv;
+                if constexpr (GATE) {
+                    const float z = (GDT == KDA_F32) ? __uint_as_float(rg[s][j]) : raw16(rg[s], j);
+                    const float4& r4 = rate[j >> 2];
+                    const float rt = (j & 3) == 0 ? r4.x : (j & 3) == 1 ? r4.y : (j & 3) == 2 ? r4.z : r4.w;
+                    gv = gate_log_decay(rt, z, p.g_min) * keep[s];
+                } else if constexpr (GDT == KDA_F32) {
+                    gv = __uint_as_float(rg[s][j]);
+                } else {
+                    gv = raw16(rg[s], j);
+                }
+                x[s][j] = gv * LOG2E;
             }
-            x[j] = gv * LOG2E;
-        }
-        // inclusive cumsum over the 16 tokens of each row (log2 units): a Hillis-Steele scan
+        // inclusive cumsum over the 16 tokens of each row and sub-block (log2 units): a
+        // Hillis-Steele scan
 #define KDA_SCAN_STEP(CTRL)                                                                          \
+        _Pragma("unroll") for (int s = 0; s < 2; ++s)                                              \
         _Pragma("unroll") for (int j = 0; j < 8; ++j)                                              \
-            x[j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[j]), CTRL, 0xf, 0xf, true));
+            x[s][j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[s][j]), CTRL, 0xf, 0xf, true));
         KDA_SCAN_STEP(0x111)
         KDA_SCAN_STEP(0x112)
         KDA_SCAN_STEP(0x114)
         KDA_SCAN_STEP(0x118)
 #undef KDA_SCAN_STEP
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e1[j] = fexp2(x[j]);                 // e^{G} <= 1
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e1[s][j] = fexp2(x[s][j]);         // e^{G} <= 1
         // e^{G_15}: lane 15 of the row (bitmask swizzle: lane -> (lane & 16) | 15)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) gm[j] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(e1[j]), 0x1F0));
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float kv = raw16(rk, j), qv = raw16(rq, j);
-            kt[j] = kv * e1[j];
-            qt[j] = qv * (e1[j] * p.scale);                              // the output scale rides on Qt and P
-            kd[j] = kv * fexp2(-x[j]);                                   // e^{-G} <= e^80
-            if (j & 1) {
-                accA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[j], kd[j], accA1, 0, 0, 0);
-                accP1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qt[j], kd[j], accP1, 0, 0, 0);
-            } else {
-                accA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[j], kd[j], accA0, 0, 0, 0);
-                accP0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qt[j], kd[j], accP0, 0, 0, 0);
+            for (int j = 0; j < 8; ++j)
+                gm[s][j] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(e1[s][j]), 0x1F0));
+        // sub-block 0: Kt, Qt, Kd with its own cumsum; Kb_0 = Kd e^{G_15} <= 1 is kept for the
+        // cross products
+        float kb0[8];
+        {
+            float kt[8], qt[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float kv = raw16(rk[0], j), qv = raw16(rq[0], j);
+                kt[j] = kv * e1[0][j];
+                qt[j] = qv * (e1[0][j] * p.scale);                       // the output scale rides on Qt and P
+                const float kd = kv * fexp2(-x[0][j]);                   // e^{-G} <= e^80
+                accA[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[j], kd, accA[0], 0, 0, 0);
+                accP[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt[j], kd, accP[0], 0, 0, 0);
+                kb0[j] = kd * gm[0][j];
+            }
+            *reinterpret_cast<uint4*>(rec + (64 * kk + lane) * 16) =
+                make_uint4(f16_pair(kt[0], kt[1]), f16_pair(kt[2], kt[3]), f16_pair(kt[4], kt[5]), f16_pair(kt[6], kt[7]));
+            *reinterpret_cast<uint4*>(rec + E2 + (64 * kk + lane) * 16) =
+                make_uint4(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]), f16_pair(qt[4], qt[5]), f16_pair(qt[6], qt[7]));
+        }
+        // sub-block 1: the same with its own cumsum, plus C = Kt_1 Kb_0^T and Qt_1 Kb_0^T; the
+        // record holds Kt_1, Qt_1 scaled from the record's first token
+        {
+            float kt[8], qt[8], kb1[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float kv = raw16(rk[1], j), qv = raw16(rq[1], j);
+                kt[j] = kv * e1[1][j];
+                qt[j] = qv * (e1[1][j] * p.scale);
+                const float kd = kv * fexp2(-x[1][j]);
+                accA[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[j], kd, accA[1], 0, 0, 0);
+                accP[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt[j], kd, accP[1], 0, 0, 0);
+                kb1[j] = kd * gm[1][j];
+            }
+            // the cross products on one fp16 MFMA each: slot j of a lane is the same channel in
+            // both operands, and the record keeps these factors in fp16 anyway
+            f16x8 k1h, q1h, b0h;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                k1h[j] = static_cast<_Float16>(kt[j]);
+                q1h[j] = static_cast<_Float16>(qt[j]);
+                b0h[j] = static_cast<_Float16>(kb0[j]);
+            }
+            accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1h, b0h, accC, 0, 0, 0);
+            accQ = __builtin_amdgcn_mfma_f32_16x16x32_f16(q1h, b0h, accQ, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                kt[j] *= gm[0][j];
+                qt[j] *= gm[0][j];
+            }
+            *reinterpret_cast<uint4*>(rec + 3 * E2 + (64 * kk + lane) * 16) =
+                make_uint4(f16_pair(kt[0], kt[1]), f16_pair(kt[2], kt[3]), f16_pair(kt[4], kt[5]), f16_pair(kt[6], kt[7]));
+            *reinterpret_cast<uint4*>(rec + 4 * E2 + (64 * kk + lane) * 16) =
+                make_uint4(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]), f16_pair(qt[4], qt[5]), f16_pair(qt[6], qt[7]));
+            // Kb^T of both sub-blocks, staged channel-major: Kb_0 scaled to the record's last token
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = 32 * kk + 16 * (j >> 2) + 4 * q + (j & 3);
+                sKb[0][frag16(c, m) - 512 * kk] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb0[j] * gm[1][j]));
+                sKb[1][frag16(c, m) - 512 * kk] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb1[j]));
             }
         }
-        // the frag32 units of Kt and Qt
-        *reinterpret_cast<uint4*>(rec + (64 * kk + lane) * 16) =
-            make_uint4(f16_pair(kt[0], kt[1]), f16_pair(kt[2], kt[3]), f16_pair(kt[4], kt[5]), f16_pair(kt[6], kt[7]));
-        *reinterpret_cast<uint4*>(rec + E2 + (64 * kk + lane) * 16) =
-            make_uint4(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]), f16_pair(qt[4], qt[5]), f16_pair(qt[6], qt[7]));
-        // Kb = Kd e^{G_15} <= 1, staged channel-major; e^{G_15} - 1 per channel from the row's
-        // last lane
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int c = 32 * kk + 16 * (j >> 2) + 4 * q + (j & 3);
-            sKb[frag16(c, m) - 512 * kk] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kd[j] * gm[j]));
-        }
-        wave_fence();   // the group's Kb^T is read across lanes, then leaves as one 1 KB store
+        wave_fence();   // the group's Kb^T is read across lanes, then leaves as 1 KB stores
         *reinterpret_cast<uint4*>(rec + 2 * E2 + 1024 * kk + 16 * lane) =
-            *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(sKb) + 16 * lane);
-        if (m == 15) {
-            float* gr = reinterpret_cast<float*>(rec + R::OFF_G) + 32 * kk + 4 * q;
-            *reinterpret_cast<float4*>(gr) = make_float4(gm[0] - 1.f, gm[1] - 1.f, gm[2] - 1.f, gm[3] - 1.f);
-            *reinterpret_cast<float4*>(gr + 16) = make_float4(gm[4] - 1.f, gm[5] - 1.f, gm[6] - 1.f, gm[7] - 1.f);
+            *reinterpret_cast<const uint4_ma*>(reinterpret_cast<const uint8_t*>(sKb[0]) + 16 * lane);
+        *reinterpret_cast<uint4*>(rec + 5 * E2 + 1024 * kk + 16 * lane) =
+            *reinterpret_cast<const uint4_ma*>(reinterpret_cast<const uint8_t*>(sKb[1]) + 16 * lane);
+        if (m == 15) {   // e^{G_31} - 1 per channel: the product of the sub-blocks' e^{G_15}
+            float* gp = reinterpret_cast<float*>(rec + R::OFF_G) + 32 * kk + 4 * q;
+            float d[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) d[j] = fmaf(gm[0][j], gm[1][j], -1.f);
+            *reinterpret_cast<float4*>(gp) = make_float4(d[0], d[1], d[2], d[3]);
+            *reinterpret_cast<float4*>(gp + 16) = make_float4(d[4], d[5], d[6], d[7]);
         }
     }
-    const f32x4 accA = accA0 + accA1, accP = accP0 + accP1;
 
-    // ---- A to LDS (for the substitution), P staged in fp16; lane (m, q) holds rows 4q + i of
-    // column m
+    // ---- A_00, A_11 and C to LDS (for the substitutions and the cross product); P staged in
+    // fp16.  Lane (m, q) holds rows 4q + i of column m.  Staged tiles: T'_00, T'_10, T'_11, then
+    // P_00, P_10, P_11.
     uint16_t* const tT = reinterpret_cast<uint16_t*>(sTail);
     uint16_t* const tP = reinterpret_cast<uint16_t*>(sTail + (R::OFF_P - R::OFF_T));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * q + i, sc = m;
-        sA[r][sc] = (sc < r) ? accA[i] * sBeta[r] : 0.f;
-        tP[fragT(r, sc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>((sc <= r) ? accP[i] : 0.f));
+        sA[0][r][sc] = (sc < r) ? accA[0][i] * sBeta[r] : 0.f;
+        sA[1][r][sc] = (sc < r) ? accA[1][i] * sBeta[16 + r] : 0.f;
+        sC[r][sc] = accC[i];
+        tP[fragT(r, sc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>((sc <= r) ? accP[0][i] : 0.f));
+        tP[256 + fragT(r, sc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(accQ[i]));
+        tP[512 + fragT(r, sc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>((sc <= r) ? accP[1][i] : 0.f));
     }
     wave_fence();   // sA and sBeta are read across lanes below
 
-    // ---- T' = (I + A)^{-1} Diag(beta): forward substitution, lane j = column j
-    if (lane < 16) {
-        const int jc = lane;
+    // ---- T'_ss = (I + A_ss)^{-1} Diag(beta_s): forward substitution, lane 16 s + j = column j of
+    // sub-block s
+    if (lane < 32) {
+        const int sb = lane >> 4, jc = lane & 15;
+        float (*const A)[16] = sA[sb];
         float t[16];
         float4 nxt[4], cur[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) nxt[u] = *reinterpret_cast<const float4*>(&sA[1][4 * u]);
+        for (int u = 0; u < 4; ++u) nxt[u] = *reinterpret_cast<const float4_ma*>(&A[1][4 * u]);
         t[0] = (jc == 0) ? 1.f : 0.f;
 #pragma unroll
         for (int r = 1; r < 16; ++r) {
@@ -792,7 +872,7 @@ __global__ void __launch_bounds__(64, 4) chunk_intra_tok_kernel(ChunkArgs p, int
             if (r + 1 < 16) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (4 * u < r + 1) nxt[u] = *reinterpret_cast<const float4*>(&sA[r + 1][4 * u]);
+                    if (4 * u < r + 1) nxt[u] = *reinterpret_cast<const float4_ma*>(&A[r + 1][4 * u]);
             }
             float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -803,14 +883,35 @@ __global__ void __launch_bounds__(64, 4) chunk_intra_tok_kernel(ChunkArgs p, int
             }
             t[r] = ((r == jc) ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
         }
-        const float bj = sBeta[jc];
+        const float bj = sBeta[16 * sb + jc];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            tT[fragT(r, jc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(t[r] * bj));
+        for (int r = 0; r < 16; ++r) {
+            const float v = t[r] * bj;
+            sTf[sb][r][jc] = v;
+            tT[512 * sb + fragT(r, jc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+        }
     }
+    wave_fence();   // T'_00 and T'_11 are read across lanes below
+
+    // ---- T'_10 = -T'_11 (C T'_00): fp32 16x16x4 MFMAs, lane (i, k) supplying row i, column
+    // 4 st + k of the left operand and lane (j, k) row 4 st + k, column j of the right one
+    f32x4 U = zero4();
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+        U = __builtin_amdgcn_mfma_f32_16x16x4f32(sC[m][4 * st + q], sTf[0][4 * st + q][m], U, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sU[4 * q + i][m] = U[i];
+    wave_fence();
+    f32x4 T10 = zero4();
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+        T10 = __builtin_amdgcn_mfma_f32_16x16x4f32(sTf[1][m][4 * st + q], sU[4 * st + q][m], T10, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        tT[256 + fragT(4 * q + i, m)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(-T10[i]));
     wave_fence();   // T' and P staged
     for (int u = lane; u < TAIL / 16; u += 64)
-        *reinterpret_cast<uint4*>(rec + R::OFF_T + 16 * u) = *reinterpret_cast<const uint4*>(sTail + 16 * u);
+        *reinterpret_cast<uint4*>(rec + R::OFF_T + 16 * u) = *reinterpret_cast<const uint4_ma*>(sTail + 16 * u);
 }
 
 // ============================================================================================
@@ -869,8 +970,9 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     using R = Rec<DK, PRECISE>;
     constexpr int KS = DK / 32;
     constexpr int CT = DK / 16;
-    constexpr int NB = PRECISE ? 2 : 4;                // 16-token blocks per streamed chunk
-    constexpr int CHT = NB * BLK;                      // tokens per chunk
+    constexpr int NB = 2;                              // records per streamed chunk
+    constexpr int CHT = NB * R::TOK;                   // tokens per chunk: 64 fast, 32 precise
+    constexpr int OST = R::TOK / 4;                    // o stores per lane and record
     constexpr int ESZ = (IDT == KDA_F32) ? 4 : 2;
     constexpr int OSZ = (ODT == KDA_F32) ? 4 : 2;
     constexpr int WKB = 64 * 16;                       // bytes one wave moves per DMA load
@@ -918,11 +1020,11 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     if (p.cu) {
         bos = p.cu[n];
         len = static_cast<int64_t>(p.cu[n + 1]) - bos;
-        base = static_cast<int64_t>(p.cu[n] / BLK) + n;
+        base = static_cast<int64_t>(p.cu[n] / R::TOK) + n;
     } else {
         bos = static_cast<int64_t>(n) * p.T;
         len = p.T;
-        base = static_cast<int64_t>(n) * ((p.T + BLK - 1) / BLK);
+        base = static_cast<int64_t>(n) * ((p.T + R::TOK - 1) / R::TOK);
     }
     const uint8_t* recs = ws + (static_cast<int64_t>(h) * nslots + base) * R::BYTES;
 
@@ -1016,7 +1118,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     constexpr int NSLICE = STATE_SLICES < NB ? STATE_SLICES : NB - 1;
     auto prefetch_slice = [&](uint8_t* buf, int64_t c, int slice) {
         const int nt = tokens_in(c);
-        const int nbk = (nt + BLK - 1) / BLK;
+        const int nbk = (nt + R::TOK - 1) / R::TOK;
         const __amdgpu_buffer_rsrc_t rr =
             make_rsrc(nt > 0 ? recs + c * NB * R::BYTES : ws, static_cast<uint32_t>(nbk * R::BYTES));
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(
@@ -1042,25 +1144,49 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
         }
     };
 
-    // One chunk: NB state steps of 16 tokens from the records in `buf`.
+    // One chunk: NB state steps from the records in `buf` (32 tokens each fast, 16 precise).
     auto run = [&](const uint8_t* buf, int64_t c, uint8_t* nbuf) {
         const int nt = tokens_in(c);
         // o rows of this chunk and head; rows past the chunk's tokens fall outside the range
         const __amdgpu_buffer_rsrc_t orr =
             make_rsrc(static_cast<char*>(p.o) + ((bos + c * CHT) * H + h) * DV * OSZ,
                       emit_o ? static_cast<uint32_t>(nt * vstride * OSZ) : 0u);
-        // The Kt / Qt fragments of block b + 1 are read from LDS while block b computes (they
-        // are needed first thing in a block); the rest of a block's operands are read at its
-        // start and consumed later in it.
+        auto store_o = [&](const f32x4& O, int row0) {   // rows row0 + 4 lq + i of the chunk
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int off = ((row0 + 4 * lq + i) * vstride + n0 + ln) * OSZ;
+                if constexpr (ODT == KDA_F32)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i]), orr, off, 0, CP_NT);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O[i]), orr, off, 0, CP_NT);
+            }
+        };
+        auto v_minus = [&](const f32x4& Y, int row0) -> f32x4 {   // V - Y, rows as store_o
+            f32x4 X;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ve = (row0 + 4 * lq + i) * BVW + 16 * wave + ln;   // V[token][column]
+                const float vv = (ESZ == 4) ? reinterpret_cast<const float*>(buf + RBYTES)[ve]
+                                            : bf16_val(reinterpret_cast<const uint16_t*>(buf + RBYTES)[ve]);
+                X[i] = vv - Y[i];
+            }
+            return X;
+        };
+        // The Kt / Qt fragments of record b + 1 are read from LDS while record b computes (they
+        // are needed first thing in a step); the rest of a record's operands are read at its
+        // start and consumed later in it.  Fast: Kt_0, Qt_0, Kt_1, Qt_1; precise: Kt hi, lo, Qt
+        // hi, lo.
         using FragA = typename std::conditional<PRECISE, bf16x8, f16x8>::type;
-        constexpr int NFA = PRECISE ? 4 : 2;            // frag32 arrays: Kt (hi, lo), Qt (hi, lo)
+        constexpr int NFA = 4;
         FragA fa[NFA][KS], fn[NFA][KS];
         auto load_fa = [&](const uint8_t* rb, FragA (&f)[NFA][KS]) {
 #pragma unroll
             for (int a = 0; a < NFA; ++a)
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk)
-                    f[a][kk] = *reinterpret_cast<const FragA*>(rb + a * E2 + 1024 * kk + 16 * lane);
+                for (int kk = 0; kk < KS; ++kk) {
+                    const int arr = PRECISE ? a : a + (a >> 1);   // fast: arrays 0, 1, 3, 4
+                    f[a][kk] = *reinterpret_cast<const FragA*>(rb + arr * E2 + 1024 * kk + 16 * lane);
+                }
         };
         load_fa(buf, fa);
 #pragma unroll
@@ -1068,23 +1194,27 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
             if (b < NSLICE) {
                 prefetch_slice(nbuf, c + 1, b);
                 // memory instructions keep their order across this point (the end-of-chunk wait
-                // counts on every load being older than the last two blocks' o stores)
+                // counts on every load being older than the last records' o stores)
                 __builtin_amdgcn_sched_barrier(0x78F);
             }
             const uint8_t* rb = buf + b * R::BYTES;
             if (b + 1 < NB) load_fa(rb + R::BYTES, fn);
-            const uint16_t* Tp = reinterpret_cast<const uint16_t*>(rb + R::OFF_T) + 4 * lane;
-            const s16x4 ph = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 8 * lane);   // fast: fp16 P
-            s16x4 pl;
-            if constexpr (PRECISE) pl = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 512 + 8 * lane);
-            const float* gam = reinterpret_cast<const float*>(rb + R::OFF_G);   // e^{G_15} - 1
+            const float* gam = reinterpret_cast<const float*>(rb + R::OFF_G);   // e^{G_last} - 1
             float4 gm[CT];
 #pragma unroll
             for (int i = 0; i < CT; ++i) gm[i] = *reinterpret_cast<const float4*>(gam + 16 * i + 4 * lq);
-
-            // Y = Kt S and O = Qt S (contraction over d_k; S packed as the B operand)
-            f32x4 Y = zero4(), O = zero4();
             if constexpr (!PRECISE) {
+                // ---- one 32-token step: sub-blocks 0 and 1, S taken at the record's first token
+                const uint8_t* tb = rb + R::OFF_T + 8 * lane;   // T'_00, T'_10, T'_11 (fragT)
+                const uint8_t* pb = rb + R::OFF_P + 8 * lane;   // P_00, P_10, P_11
+                const f16x4 t00 = *reinterpret_cast<const f16x4*>(tb);
+                const f16x8 t1x = __builtin_shufflevector(*reinterpret_cast<const f16x4*>(tb + 512),
+                                                          *reinterpret_cast<const f16x4*>(tb + 1024), 0, 1, 2, 3, 4, 5, 6, 7);
+                const f16x4 p00 = *reinterpret_cast<const f16x4*>(pb);
+                const f16x8 p1x = __builtin_shufflevector(*reinterpret_cast<const f16x4*>(pb + 512),
+                                                          *reinterpret_cast<const f16x4*>(pb + 1024), 0, 1, 2, 3, 4, 5, 6, 7);
+                // Y_s = Kt_s S and O_s = Qt_s S (contraction over d_k; S packed as the B operand)
+                f32x4 Y0 = zero4(), Y1 = zero4(), O0 = zero4(), O1 = zero4();
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
                     f16x8 sb;
@@ -1093,10 +1223,48 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                         sb[i] = static_cast<_Float16>(S[2 * kk][i]);
                         sb[4 + i] = static_cast<_Float16>(S[2 * kk + 1][i]);
                     }
-                    Y = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[0][kk], sb, Y, 0, 0, 0);
-                    O = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[1][kk], sb, O, 0, 0, 0);
+                    Y0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[0][kk], sb, Y0, 0, 0, 0);
+                    Y1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[2][kk], sb, Y1, 0, 0, 0);
+                    O0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[1][kk], sb, O0, 0, 0, 0);
+                    O1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[3][kk], sb, O1, 0, 0, 0);
+                }
+                // X = V - Y (the beta scaling sits in T'); W_0 = T'_00 X_0, W_1 = T'_10 X_0 +
+                // T'_11 X_1 as one K = 32 product: K slots 8k .. 8k + 3 pair with sub-block 0's
+                // tokens 4k .. 4k + 3, slots 8k + 4 .. 8k + 7 with sub-block 1's
+                const f32x4 X0 = v_minus(Y0, 32 * b), X1 = v_minus(Y1, 32 * b + 16);
+                f16x4 x0, x1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { x0[i] = static_cast<_Float16>(X0[i]); x1[i] = static_cast<_Float16>(X1[i]); }
+                const f32x4 W0 = __builtin_amdgcn_mfma_f32_16x16x16f16(t00, x0, zero4(), 0, 0, 0);
+                const f32x4 W1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    t1x, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7), zero4(), 0, 0, 0);
+                f16x4 w0, w1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { w0[i] = static_cast<_Float16>(W0[i]); w1[i] = static_cast<_Float16>(W1[i]); }
+                const f16x8 wx = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
+                // O += P W (P and Qt carry the output scale)
+                O0 = __builtin_amdgcn_mfma_f32_16x16x16f16(p00, w0, O0, 0, 0, 0);
+                O1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(p1x, wx, O1, 0, 0, 0);
+                store_o(O0, 32 * b);
+                store_o(O1, 32 * b + 16);
+                // S <- Diag(e^{G_31}) S + Kb^T W = S + Diag(e^{G_31} - 1) S + [Kb_0^T Kb_1^T] W
+                const uint8_t* kb0 = rb + 2 * E2 + 8 * lane;   // frag16 Kb^T of sub-block 0
+                const uint8_t* kb1 = rb + 5 * E2 + 8 * lane;
+#pragma unroll
+                for (int i = 0; i < CT; ++i) {
+                    const f16x8 ka = __builtin_shufflevector(*reinterpret_cast<const f16x4*>(kb0 + 512 * i),
+                                                             *reinterpret_cast<const f16x4*>(kb1 + 512 * i), 0, 1, 2, 3, 4, 5, 6, 7);
+                    f32x4 acc;
+                    acc[0] = fmaf(S[i][0], gm[i].x, S[i][0]); acc[1] = fmaf(S[i][1], gm[i].y, S[i][1]);
+                    acc[2] = fmaf(S[i][2], gm[i].z, S[i][2]); acc[3] = fmaf(S[i][3], gm[i].w, S[i][3]);
+                    S[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, wx, acc, 0, 0, 0);
                 }
             } else {
+                // ---- one 16-token step, split-bf16 operands
+                const uint16_t* Tp = reinterpret_cast<const uint16_t*>(rb + R::OFF_T) + 4 * lane;
+                const s16x4 ph = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 8 * lane);
+                const s16x4 pl = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 512 + 8 * lane);
+                f32x4 Y = zero4(), O = zero4();
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
                     float sv[8];
@@ -1107,59 +1275,15 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                     Y = mfma32_bf16_x3(fa[0][kk], fa[1][kk], sbh, sbl, Y);
                     O = mfma32_bf16_x3(fa[2][kk], fa[3][kk], sbh, sbl, O);
                 }
-            }
-            // X = V - Y (the beta scaling sits in T'), W = T' X
-            f32x4 X;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ve = (16 * b + 4 * lq + i) * BVW + 16 * wave + ln;   // V[token][column]
-                const float vv = (ESZ == 4) ? reinterpret_cast<const float*>(buf + RBYTES)[ve]
-                                            : bf16_val(reinterpret_cast<const uint16_t*>(buf + RBYTES)[ve]);
-                X[i] = vv - Y[i];
-            }
-            f32x4 W;
-            if constexpr (!PRECISE) {
-                f16x4 x16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x16[i] = static_cast<_Float16>(X[i]);
-                W = __builtin_amdgcn_mfma_f32_16x16x16f16(*reinterpret_cast<const f16x4*>(Tp), x16, zero4(), 0, 0, 0);
-            } else {
+                const f32x4 X = v_minus(Y, 16 * b);
                 s16x4 xh, xl;
                 split4(X, xh, xl);
-                W = mfma16_bf16_x3(*reinterpret_cast<const s16x4*>(Tp), *reinterpret_cast<const s16x4*>(Tp + 256),
-                                   xh, xl, zero4());
-            }
-            // O += P W (P and Qt carry the output scale)
-            s16x4 wh, wl;
-            f16x4 w16;
-            if constexpr (!PRECISE) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w16[i] = static_cast<_Float16>(W[i]);
-                O = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ph), w16, O, 0, 0, 0);
-            } else {
+                const f32x4 W = mfma16_bf16_x3(*reinterpret_cast<const s16x4*>(Tp), *reinterpret_cast<const s16x4*>(Tp + 256),
+                                               xh, xl, zero4());
+                s16x4 wh, wl;
                 split4(W, wh, wl);
                 O = mfma16_bf16_x3(ph, pl, wh, wl, O);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int off = ((16 * b + 4 * lq + i) * vstride + n0 + ln) * OSZ;
-                if constexpr (ODT == KDA_F32)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i]), orr, off, 0, CP_NT);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O[i]), orr, off, 0, CP_NT);
-            }
-            // S <- Diag(e^{G_15}) S + Kb^T W = S + Diag(e^{G_15} - 1) S + Kb^T W
-            if constexpr (!PRECISE) {
-                const uint8_t* kbt = rb + 2 * E2 + 8 * lane;   // frag16 Kb^T
-#pragma unroll
-                for (int i = 0; i < CT; ++i) {
-                    const f16x4 ka = *reinterpret_cast<const f16x4*>(kbt + 512 * i);
-                    f32x4 acc;
-                    acc[0] = fmaf(S[i][0], gm[i].x, S[i][0]); acc[1] = fmaf(S[i][1], gm[i].y, S[i][1]);
-                    acc[2] = fmaf(S[i][2], gm[i].z, S[i][2]); acc[3] = fmaf(S[i][3], gm[i].w, S[i][3]);
-                    S[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(ka, w16, acc, 0, 0, 0);
-                }
-            } else {
+                store_o(O, 16 * b);
                 const uint8_t* kbh = rb + 4 * E2 + 8 * lane;
                 const uint8_t* kbl = rb + 5 * E2 + 8 * lane;
 #pragma unroll
@@ -1182,10 +1306,10 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     };
 
     // Each half-iteration runs the current chunk while the next chunk's transfers go out, then
-    // waits for those transfers -- the o stores of the blocks from the one that issued the last
-    // slice on (4 each) may stay in flight, every load is older -- and meets the other waves at
+    // waits for those transfers -- the o stores of the records from the one that issued the last
+    // slice on (OST each) may stay in flight, every load is older -- and meets the other waves at
     // the barrier.
-    constexpr int WAIT_LOADS = vmcnt_imm(4 * (NB - NSLICE + 1));
+    constexpr int WAIT_LOADS = vmcnt_imm(OST * (NB - NSLICE + 1));
 #pragma unroll
     for (int sl = 0; sl < NSLICE; ++sl) prefetch_slice(bufA, c_begin, sl);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1317,9 +1441,9 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
 }
 
 // ---- host side --------------------------------------------------------------------------------
-int64_t slot_count(int32_t n_seqs, int64_t total_tokens, bool varlen, int32_t B, int64_t T) {
-    if (!varlen) return static_cast<int64_t>(B) * ((T + BLK - 1) / BLK);
-    return total_tokens / BLK + n_seqs + 1;
+int64_t slot_count(int32_t n_seqs, int64_t total_tokens, bool varlen, int32_t B, int64_t T, int tok) {
+    if (!varlen) return static_cast<int64_t>(B) * ((T + tok - 1) / tok);
+    return total_tokens / tok + n_seqs + 1;
 }
 
 size_t record_bytes(int32_t dk, bool precise) {
@@ -1338,7 +1462,7 @@ int64_t seg_slot_bound(int32_t n_seqs, int64_t total_tokens) {   // packed and f
     return total_tokens / SEG_TOK + n_seqs + 1;
 }
 size_t record_area(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk, bool precise) {
-    const int64_t slots = total_tokens / BLK + n_seqs + 1;   // bound for packed and fixed batches
+    const int64_t slots = total_tokens / (precise ? 16 : 32) + n_seqs + 1;   // packed and fixed batches
     const size_t b = static_cast<size_t>(slots) * static_cast<size_t>(H) * record_bytes(dk, precise);
     return (b + 255) & ~static_cast<size_t>(255);
 }
@@ -1364,7 +1488,7 @@ template <int DK, int IDT, int GDT, int ODT>
 hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     constexpr bool PRECISE = (IDT == KDA_F32);
     const int64_t total = static_cast<int64_t>(a.B) * a.T;
-    const int64_t nslots = slot_count(a.n_seqs, total, a.cu != nullptr, a.B, a.T);
+    const int64_t nslots = slot_count(a.n_seqs, total, a.cu != nullptr, a.B, a.T, Rec<DK, PRECISE>::TOK);
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
     const int64_t intra_wgs = nslots * a.H;
     if (intra_wgs > 0) {

@@ -104,25 +104,28 @@ def test_chunk_fwd_gated_rejects(lib):
 
 def test_workspace_size(lib):
     import torch
-    # one fixed-size record per (head, slot): a 16-token block; slots <= tokens/16 + sequences + 1;
-    # the record area is rounded up to 256 bytes.  Launches that split long sequences into
-    # 8192-token segments add, per (segment slot, head), a start state, B (d_k x d_v) and M
-    # (d_k x d_k) in fp32, with segment slots <= tokens/8192 + sequences + 1.
-    for dt in (torch.bfloat16, torch.float32):
+    # one fixed-size record per (head, slot): 32 tokens for 16-bit inputs (two 16-token
+    # sub-blocks), 16 tokens for fp32 inputs; slots <= tokens/tok + sequences + 1; the record area
+    # is rounded up to 256 bytes.  Launches that split long sequences into 8192-token segments
+    # add, per (segment slot, head), a start state, B (d_k x d_v) and M (d_k x d_k) in fp32, with
+    # segment slots <= tokens/8192 + sequences + 1.
+    for dt, tpr in ((torch.bfloat16, 32), (torch.float32, 16)):
         rec = K.kda_chunk_fwd_workspace_size(1, 0, 1, 128, 128, in_dtype=dt) // 2
         assert rec > 0 and rec % 16 == 0
         for n, tok, H in [(4, 4 * 4096, 16), (8, 1 << 20, 8), (1, 1 << 16, 32), (3, 17, 5), (1, 15, 1)]:
-            area = (tok // 16 + n + 1) * H * rec
+            area = (tok // tpr + n + 1) * H * rec
             area = (area + 255) // 256 * 256
             got = K.kda_chunk_fwd_workspace_size(n, tok, H, 128, 128, in_dtype=dt)
             seg = (tok // 8192 + n + 1) * H * 128 * (2 * 128 + 128) * 4
             assert got in (area, area + seg), (n, tok, H, got, area)
+    # 16-bit records: 6 fp16 [16][128] arrays, 3 + 3 fp16 16 x 16 tiles and 128 fp32 decays
+    assert K.kda_chunk_fwd_workspace_size(1, 0, 1, 128, 128) == 2 * 28160
     # the bf16 prefill workload runs unsegmented; the long one (1 x 65536 tokens, 32 heads) and
     # the packed one (8 sequences, 2^20 tokens, 8 heads) are segmented
     bf = K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128)
-    assert bf == ((1024 + 5) * 16 * 13824 + 255) // 256 * 256
+    assert bf == ((512 + 5) * 16 * 28160 + 255) // 256 * 256
     for n, tok, H in [(1, 1 << 16, 32), (8, 1 << 20, 8)]:
-        area = ((tok // 16 + n + 1) * H * 13824 + 255) // 256 * 256
+        area = ((tok // 32 + n + 1) * H * 28160 + 255) // 256 * 256
         assert K.kda_chunk_fwd_workspace_size(n, tok, H, 128, 128) == \
             area + (tok // 8192 + n + 1) * H * 128 * 384 * 4
     f32 = K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128, in_dtype=torch.float32)
