@@ -14,8 +14,8 @@ seeded log-uniform lengths summing to 2^20 tokens, 8 heads, cu_seqlens) under "p
 Prints ONE JSON line.  ``value`` is prefill tokens/s (B*T tokens per step / step time).
 ``roofline`` describes the step's one operation, kda_chunk_fwd_gated (its two kernels: the
 intra-block kernel with the gate fused, and the state-passing kernel, launched back to back on
-one stream), with its algorithmic bytes per call divided by its mean call time, measured with
-HIP events on the launch stream.
+one stream), with its algorithmic bytes per call divided by its mean call time: HIP events on
+the launch stream around the timed region's K steps.
 ``cpu_baseline`` is the fp64 oracle (test infrastructure) timed on this host's cores on the same
 workload.
 """
@@ -336,29 +336,29 @@ def main():
         fused_step()
         unfused_step()
     torch.cuda.synchronize()
-    # wall clock over exactly K steps
+    # exactly K steps: wall clock, and HIP events on the launch stream around the same region
+    e_beg, e_end = ev(), ev()
     t0 = time.perf_counter()
+    e_beg.record(stream)
     for _ in range(args.steps):
         fused_step()
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    # per-call durations with HIP events on the launch stream (separate passes, same work)
-    fused_ms, gate_ms, chunk_ms = [], [], []
-    for _ in range(args.steps):
-        e = [ev() for _ in range(4)]
-        e[0].record(stream)
-        fused_step()
-        e[1].record(stream)
+    fused_ms = [e_beg.elapsed_time(e_end) / args.steps]
+    # the unfused pair for reference: K pairs back to back, events between the calls
+    evs = [ev() for _ in range(2 * args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
         K.kda_gate(A, z, g=g, stream=stream)
-        e[2].record(stream)
+        evs[2 * i + 1].record(stream)
         K.kda_chunk_fwd(q, k, v, beta, g, initial_state=S0, final_state=hT, o=o, workspace=ws,
                         stream=stream)
-        e[3].record(stream)
-        e[3].synchronize()
-        fused_ms.append(e[0].elapsed_time(e[1]))
-        gate_ms.append(e[1].elapsed_time(e[2]))
-        chunk_ms.append(e[2].elapsed_time(e[3]))
+        evs[2 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    gate_ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)]
+    chunk_ms = [evs[2 * i + 1].elapsed_time(evs[2 * i + 2]) for i in range(args.steps)]
     fused_avg = sum(fused_ms) / len(fused_ms)
     chunk_avg = sum(chunk_ms) / len(chunk_ms)
     gate_avg = sum(gate_ms) / len(gate_ms)
