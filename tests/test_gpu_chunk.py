@@ -115,6 +115,18 @@ def test_prefill_gate_extremes(gmode):
     assert torch.isfinite(o).all() and torch.isfinite(hT).all()
 
 
+@pytest.mark.parametrize("div", [20.0, 5.0])
+def test_prefill_mild_decay(div):
+    """Gates scaled down (mean decay about e^-0.125 and e^-0.5 per token): across the 16-token
+    halves of a 32-token state step both the decay factors and the cross terms between the halves
+    are far from 0 and from 1, which neither the standard recipe (cross terms vanish) nor g = 0
+    (every factor is 1) exercises."""
+    d = prefill_case("prefill_bf16", B=2, H=2, T=300)
+    g = oracle_g(d) / div
+    say("chunk mild decay", div)
+    check_full(d, g, TOL["bf16"], label=f"g/{div:g}")
+
+
 @pytest.mark.parametrize("bval", [0.0, 1.0])
 def test_prefill_beta_extremes(bval):
     """beta = 0 (nothing written: pure decay of the initial state) and beta = 1 (full
