@@ -20,26 +20,30 @@
 //   O  = scale * (Qt S + P W),          S <- Diag(e^{G_15}) S + Kb^T W
 // Kt, Qt, Kb lie in [-1, 1] (factors <= 1); Kd's factor is at most e^{16*5} = e^80, inside the
 // bf16 / fp32 range (e^88.7): the bound on g is what makes the diagonal block a plain dense
-// product.  Successive blocks are chained through S, so a 64-token chunk is four blocks and its
-// 64 x 64 triangular system is solved blockwise, the coupling going through the state.
+// product.  For 16-bit inputs one state step covers two such blocks (32 tokens): the same form
+// with G taken from the first block's start, its 32 x 32 A and P assembled from 16 x 16 tiles
+// whose exponents stay within e^{+-80} (the cross tiles use factors <= 1 referenced at the
+// blocks' boundary), and T' block-triangular.  Successive steps are chained through S, so a
+// 64-token chunk's triangular system is solved blockwise, the coupling going through the state.
 //
-// 1. Intra-block kernel (everything that does not depend on S; fully parallel): one wave per
-//    (16-token block, head); writes one record per (head, block) to the workspace -- Kt, Qt,
-//    Kb^T in their MFMA formats, T', P, e^{G_15} - 1 -- in whole 1 KB wave stores.
-//    16-bit inputs (chunk_intra_tok_kernel): each lane owns one token and the channels of its
-//    record unit; inputs arrive by direct-to-LDS loads, the block cumsum is a DPP scan across
-//    the lanes, A and P are fp32 MFMAs fed from registers, T' by substitution.
-//    fp32 inputs (chunk_intra_kernel, split-bf16 records): each lane owns 4 tokens x 4 channels;
-//    quad-lane cumsum, A and P on MFMA from split-bf16 operands staged in LDS.
+// 1. Intra-block kernel (everything that does not depend on S; fully parallel): writes one
+//    record per (head, record slot) to the workspace -- Kt, Qt, Kb^T in their MFMA formats,
+//    T', P, the step's e^{G_last} - 1.
+//    16-bit inputs (chunk_intra_tok_kernel): one wave per (32-token record, head); each lane
+//    owns one token of each 16-token sub-block and the channels of its record unit; inputs
+//    arrive by direct-to-LDS loads, the cumsums are DPP scans across the lanes, A and P are fp32
+//    MFMAs fed from registers, T' by substitution and one block-triangular product.
+//    fp32 inputs (chunk_intra_kernel, split-bf16 records of 16 tokens): each lane owns 4 tokens
+//    x 4 channels; quad-lane cumsum, A and P on MFMA from split-bf16 operands staged in LDS.
 // 2. State-passing kernel (the sequential part): one 256-lane workgroup per (sequence, head,
 //    64 state columns); each wave owns 16 state columns in fp32 accumulators for the whole
-//    sequence.  A chunk's four records and its V rows stream into double-buffered LDS while the
+//    sequence.  A chunk's two records and its V rows stream into double-buffered LDS while the
 //    previous chunk is processed.  Optionally it stores the state every k tokens (checkpoints).
 //    Long sequences with few (sequence, head) units run it as segment passes around a scan of
 //    the segments' affine pairs (see the segment section below).
-// Precision: operands that are range-bounded use fp16 (11-bit significand) in one pass (Kt S,
-// Qt S, T' X, Kb^T W for bf16 inputs); the diagonal products (factors up to e^80) and P W use
-// split bf16 (hi*hi + hi*lo + lo*hi).  For fp32 inputs every product is split bf16.
+// Precision (16-bit inputs): A and P of each 16-token block are fp32 products; every operand of
+// the state pass is range-bounded and runs in fp16 (11-bit significand) with fp32 accumulation.
+// For fp32 inputs every product is split bf16 (hi*hi + hi*lo + lo*hi).
 #include <type_traits>
 
 #include "kda_common.hpp"
