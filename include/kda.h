@@ -84,9 +84,10 @@ int kda_gate(const float *A, const void *z, int z_dtype, void *g, int g_dtype, i
 /*
  * Workspace bytes kda_chunk_fwd needs for a batch of n_seqs sequences holding total_tokens tokens
  * (B*T for fixed-length batches) with inputs in in_dtype.  The prefill runs in two kernels: the
- * first computes, for every (head, 16-token block), everything that does not depend on the state
- * and writes it to the workspace; the second passes the state along each sequence reading it.
- * The size is 14 KiB per (head, block) at d_k = 128 for bf16 inputs (26.5 KiB for fp32).
+ * first computes, for every (head, 32-token record; 16 tokens for fp32 inputs), everything that
+ * does not depend on the state and writes it to the workspace; the second passes the state
+ * along each sequence reading it.  At d_k = 128 a record is 27.5 KiB for bf16 inputs (880 bytes
+ * per token and head) and 26.5 KiB for fp32 inputs (16 tokens).
  * Never fails; returns 0 for invalid sizes (kda_chunk_fwd then reports the error).
  */
 size_t kda_chunk_fwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
