@@ -63,7 +63,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BLK = 16;     // tokens per block (one state step)
-constexpr int STATE_WAVES = 4;   // waves per state-kernel workgroup (16 state columns each)
+// Waves per state-kernel workgroup, 16 state columns each: 2 in the whole-sequence pass (more
+// CUs, each streaming the records once per 32 columns, measured faster than 4), 4 in the segment
+// passes (8 when d_k = d_v = 128).
+constexpr int STATE_WAVES = 2;
+constexpr int SEG_WAVES = 4;
 constexpr int STATE_SLICES = 2;  // slices a chunk's transfers are issued in (at most NB - 1)
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -1459,7 +1463,7 @@ size_t record_bytes(int32_t dk, bool precise) {
 // column blocks -- and sequences are long on average.  A pure function of the sizes, so that
 // the workspace query and the launch agree.
 bool use_segments(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dv) {
-    const int64_t wgs = static_cast<int64_t>(n_seqs) * H * (dv / (16 * STATE_WAVES));
+    const int64_t wgs = static_cast<int64_t>(n_seqs) * H * (dv / 64);   // 64-column units
     return wgs <= 128 && total_tokens >= 2 * SEG_TOK * static_cast<int64_t>(n_seqs);
 }
 int64_t seg_slot_bound(int32_t n_seqs, int64_t total_tokens) {   // packed and fixed batches
@@ -1515,8 +1519,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    constexpr int NW = STATE_WAVES;
-    const int32_t n_vblk = a.dv / (16 * NW);
+    const int32_t n_vblk = a.dv / (16 * STATE_WAVES);
     SegArgs sg{};
     if (!use_segments(a.n_seqs, total, a.H, a.dv)) {
         launch_state_ck<DK, IDT, ODT, PRECISE, 0>(a, nslots, ws, sg, static_cast<int64_t>(a.n_seqs) * a.H,
@@ -1533,6 +1536,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     sg.slots = a.cu ? seg_slot_bound(a.n_seqs, total)
                     : static_cast<int64_t>(a.B) * (a.T <= 0 ? 1 : (a.T + SEG_TOK - 1) / SEG_TOK);
     const int64_t seg_units = sg.slots * a.H;
+    constexpr int NW = SEG_WAVES;
     const bool wide = (DK == 128 && a.dv == 128);
     const int nw = wide ? 2 * NW : NW;
     sg.n_vblk_m = DK / (16 * nw);
@@ -1540,7 +1544,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     if (wide)
         launch_state_ck<DK, IDT, ODT, PRECISE, 1, 2 * NW>(a, nslots, ws, sg, seg_units, sg.n_vblk_m + nvb, stream);
     else
-        launch_state_ck<DK, IDT, ODT, PRECISE, 1>(a, nslots, ws, sg, seg_units, sg.n_vblk_m + nvb, stream);
+        launch_state_ck<DK, IDT, ODT, PRECISE, 1, NW>(a, nslots, ws, sg, seg_units, sg.n_vblk_m + nvb, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((seg_scan_kernel<DK>), dim3(static_cast<unsigned>(static_cast<int64_t>(a.n_seqs) * a.H * (a.dv / 16))),
@@ -1550,7 +1554,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     if (wide)
         launch_state_ck<DK, IDT, ODT, PRECISE, 2, 2 * NW>(a, nslots, ws, sg, seg_units, nvb, stream);
     else
-        launch_state_ck<DK, IDT, ODT, PRECISE, 2>(a, nslots, ws, sg, seg_units, nvb, stream);
+        launch_state_ck<DK, IDT, ODT, PRECISE, 2, NW>(a, nslots, ws, sg, seg_units, nvb, stream);
     return hipGetLastError();
 }
 
