@@ -101,9 +101,8 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
     const float r1 = x1 - __uint_as_float(hi & 0xffff0000u);
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
 }
-// Staged tiles are written as 16-bit (or fp32) elements and read back as whole 16-byte units:
-// the reads go through may_alias types, or type-based alias analysis may take the element stores
-// for dead (nothing of their type reads them before the next group overwrites them).
+// Staged tiles are written as 16-bit (or fp32) elements and read back as whole 16-byte units
+// through may_alias types, which makes these type-punned reads well defined.
 typedef uint4 __attribute__((may_alias)) uint4_ma;
 typedef float4 __attribute__((may_alias)) float4_ma;
 __device__ __forceinline__ uint32_t f16_pair(float x0, float x1) {
@@ -1576,8 +1575,8 @@ hipError_t dispatch(const ChunkArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Workspace: one record per (head, 16-token block slot); for segmented launches, then the
-// segment start states, B and M per (segment slot, head).
+// Workspace: one record per (head, record slot: 32 tokens for 16-bit inputs, 16 for fp32);
+// for segmented launches, then the segment start states, B and M per (segment slot, head).
 size_t chunk_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
                              int32_t dv, int32_t in_dtype) {
     size_t b = record_area(n_seqs, total_tokens, H, dk, in_dtype == KDA_F32);
