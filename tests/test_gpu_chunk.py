@@ -422,6 +422,15 @@ def test_segmented_prefill_batch_and_packed():
     check_full(d, oracle_g(d), TOL["bf16"], label="seg packed")
 
 
+def test_segmented_prefill_mild_decay():
+    """Gates scaled down 20x (mean decay about e^-0.125 per token): every channel carries state
+    across segment boundaries, so each segment's transition M is far from 0 and the pair scan
+    decides the later segments' outputs."""
+    d = prefill_case("prefill_bf16", B=1, H=2, T=3 * 8192 + 5)
+    say("segmented prefill, mild decay")
+    check_full(d, oracle_g(d) / 20.0, TOL["bf16"], label="seg g/20")
+
+
 def test_segmented_prefill_f32_and_fused_gate():
     """fp32 inputs (32-token chunks, tolerance 1e-4) and the fused gate on segmented launches."""
     d = prefill_case("prefill_f32_small", T=20000)
