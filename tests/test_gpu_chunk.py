@@ -127,6 +127,14 @@ def test_prefill_mild_decay(div):
     check_full(d, g, TOL["bf16"], label=f"g/{div:g}")
 
 
+def test_prefill_mild_decay_f32():
+    """fp32 inputs (16-token records, split-bf16 operands) with gates scaled down 20x: the state
+    carries across blocks and chunks at full weight."""
+    d = prefill_case("prefill_f32_small")
+    say("chunk mild decay f32", d["cfg"])
+    check_full(d, oracle_g(d) / 20.0, TOL["f32"], label="f32 g/20")
+
+
 @pytest.mark.parametrize("bval", [0.0, 1.0])
 def test_prefill_beta_extremes(bval):
     """beta = 0 (nothing written: pure decay of the initial state) and beta = 1 (full
