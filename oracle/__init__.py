@@ -6,7 +6,11 @@ shares nothing with the HIP library.  What each function computes, and which pas
 pages it follows, is stated in ``kda_oracle.c``.
 
 Parity status of every function here: pinned by ``tests/test_oracle_pins.py`` (closed forms,
-invariants and brute-force transition products on small inputs).
+invariants and brute-force transition products on small inputs).  ``forward_units`` and
+``forward_checkpoints`` are pinned to the pinned ``forward`` bit for bit (``check_forward_units``,
+``test_checkpoints_equal_prefix_final_states``); ``tests/test_oracle_mutants.py`` shows that
+broken copies of ``forward_units`` (a shifted first token, a short unit, the wrong initial-state
+row or head, no scale) fail that pin.
 
 Inputs may be numpy arrays or CPU torch tensors in float32, bfloat16 or float64; they are
 handed to C in their stored dtype and upcast exactly there.

@@ -310,8 +310,59 @@ def check_decode(lib=None):
     assert np.allclose(o_r, v, rtol=0, atol=1e-12)
 
 
+def check_forward_units(lib=None, forward_units=None):
+    """oracle.forward_units, the reference the sampled parity tests of the long and packed
+    workloads compare against, returns for each chosen (sequence, head) unit exactly the rows of
+    o and the final state that oracle.forward (pinned above) gives for the whole batch: a
+    fixed-length batch with bf16 inputs, fp32 S0 and scale != 1, and a packed batch with empty
+    and unequal sequences, per-sequence S0 and without one.  `forward_units` replaces the
+    function under test (the mutation tests pass deliberately broken copies)."""
+    import torch
+    fu = forward_units or oracle.forward_units
+    rng = np.random.default_rng(13)
+    t = lambda a, dt: torch.tensor(a, dtype=torch.float32).to(dt)  # noqa: E731
+    # fixed-length batch: B = 3 sequences of T tokens, bf16 inputs, fp32 initial states
+    B, T, H, dk, dv, scale = 3, 11, 3, 5, 4, 0.5
+    bf = torch.bfloat16
+    q, k = t(rng.standard_normal((B, T, H, dk)), bf), t(_rand_unit_rows(rng, (B, T, H, dk)), bf)
+    v, beta = t(rng.standard_normal((B, T, H, dv)), bf), t(rng.uniform(0, 1, (B, T, H)), bf)
+    g = t(rng.uniform(-5, 0, (B, T, H, dk)), torch.float32)
+    S0 = t(rng.standard_normal((B, H, dk, dv)), torch.float32)
+    o, S = _fwd(lib, q, k, v, beta, g, S0, scale=scale)
+    units = [(0, 0), (2, 1), (1, 2), (2, 2), (0, 1)]
+    res = fu(q, k, v, beta, g, units, S0=S0, scale=scale, lib_path=lib)
+    assert set(res) == set(units)
+    for (n, h), (o_u, S_u) in res.items():
+        assert o_u.shape == (T, dv) and S_u.shape == (dk, dv)
+        assert np.array_equal(o_u, o[n, :, h]), f"o of unit {(n, h)}"
+        assert np.array_equal(S_u, S[n, h]), f"final state of unit {(n, h)}"
+    # packed batch with an empty first sequence and unequal lengths
+    lens = [0, 7, 13, 1, 9]
+    N, tot = len(lens), sum(lens)
+    cu = np.cumsum([0] + lens).astype(np.int32)
+    q = rng.standard_normal((1, tot, H, dk))
+    k = _rand_unit_rows(rng, (1, tot, H, dk))
+    v = rng.standard_normal((1, tot, H, dv))
+    beta = rng.uniform(0, 1, (1, tot, H))
+    g = rng.uniform(-5, 0, (1, tot, H, dk))
+    S0 = rng.standard_normal((N, H, dk, dv))
+    everything = [(n, h) for n in range(N) for h in range(H)]
+    for s0 in (S0, None):
+        o, S = _fwd(lib, q, k, v, beta, g, s0, cu, scale=scale)
+        res = fu(q, k, v, beta, g, everything, S0=s0, cu_seqlens=cu, scale=scale, lib_path=lib)
+        assert set(res) == set(everything)
+        for (n, h), (o_u, S_u) in res.items():
+            a, b = int(cu[n]), int(cu[n + 1])
+            assert o_u.shape == (b - a, dv), f"rows of unit {(n, h)}"
+            assert np.array_equal(o_u, o[0, a:b, h]), f"o of unit {(n, h)}"
+            assert np.array_equal(S_u, S[n, h]), f"final state of unit {(n, h)}"
+        if s0 is not None:   # an empty sequence passes its initial state through
+            assert np.array_equal(res[(0, 1)][1], S0[0, 1])
+
+
 ALL_CHECKS = [
     check_gate_closed_forms, check_gate_dtypes, check_worked_example, check_retrieval,
     check_pure_decay, check_deltanet_limit, check_unrolled_product, check_pair_scan,
     check_linearity, check_nonexpansive, check_batch_layouts, check_dtype_upcast, check_decode,
+    check_forward_units,
 ]

@@ -81,3 +81,44 @@ def test_pins_catch_mutant(name, mutant_dir):
         except AssertionError:
             caught.append(check.__name__)
     assert caught, f"no pin caught mutant {name}"
+
+
+# ---- oracle.forward_units: deliberately broken copies of the Python wrapper, each of which the
+# forward_units pin must reject (the C loop is the real one, so only the unit bookkeeping changes)
+UNIT_MUTANTS = {
+    "packed_tok0_off_by_one": ("tok0 = int(cu[n]) if", "tok0 = max(int(cu[n]) - 1, 0) if"),
+    "fixed_tok0_off_by_one": ("else n * T\n        length", "else max(n * T - 1, 0)\n        length"),
+    "short_length": ("length = int(cu[n + 1] - cu[n]) if cu is not None else T",
+                     "length = max(int(cu[n + 1] - cu[n]) - 1, 0) if cu is not None else T - 1"),
+    "wrong_S0_sequence": ("np.array(s0[n, h], dtype", "np.array(s0[(n + 1) % s0.shape[0], h], dtype"),
+    "wrong_S0_head": ("np.array(s0[n, h], dtype", "np.array(s0[n, (h + 1) % H], dtype"),
+    "S0_ignored": ("S = np.array(s0[n, h], dtype=np.float64) if sdt != _BF16 else None",
+                   "S = np.zeros((dk, dv)) if sdt != _BF16 else None"),
+    "wrong_head": ("tok0, length, H, h,", "tok0, length, H, (h + 1) % H,"),
+    "no_scale": ("dk, dv, float(scale), _p(S), _p(o_u)", "dk, dv, 1.0, _p(S), _p(o_u)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(UNIT_MUTANTS))
+def test_forward_units_pin_catches_mutant(name):
+    import inspect
+
+    import oracle
+    src = inspect.getsource(oracle.forward_units)
+    old, new = UNIT_MUTANTS[name]
+    assert src.count(old) == 1, f"mutation {name} did not apply"
+    ns = dict(vars(oracle))
+    exec(compile(src.replace(old, new), f"<forward_units mutant {name}>", "exec"), ns)
+    with pytest.raises(AssertionError):
+        oracle_pins.check_forward_units(None, forward_units=ns["forward_units"])
+
+
+def test_forward_units_pin_passes_unmodified_copy():
+    """The same recompilation without a mutation passes, so the rejections above come from the
+    mutations themselves."""
+    import inspect
+
+    import oracle
+    ns = dict(vars(oracle))
+    exec(compile(inspect.getsource(oracle.forward_units), "<forward_units copy>", "exec"), ns)
+    oracle_pins.check_forward_units(None, forward_units=ns["forward_units"])
