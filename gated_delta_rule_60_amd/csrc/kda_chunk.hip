@@ -248,10 +248,25 @@ __device__ __forceinline__ void store_words(void* dst, const uint32_t (&w)[NP]) 
     else *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
 }
 
+// Token range [bos, end) of sequence n of a packed batch (B = 1, T tokens in all).  The offsets
+// are clamped so that 0 <= bos <= end <= T whatever cu_seqlens holds: with malformed offsets
+// (negative, past T, decreasing) results are unspecified, but every slot base and buffer range
+// derived from bos and end stays inside the buffers sized for T tokens.
+__device__ __forceinline__ int64_t seq_start(const ChunkArgs& p, int n) {
+    const int64_t a = p.cu[n];
+    return a < 0 ? 0 : a > p.T ? p.T : a;
+}
+__device__ __forceinline__ void seq_bounds(const ChunkArgs& p, int n, int64_t& bos, int64_t& end) {
+    bos = seq_start(p, n);
+    const int64_t b = p.cu[n + 1];
+    end = b < bos ? bos : b > p.T ? p.T : b;
+}
+
 // Locate the record slot of a workgroup: sequence n, record j inside it (TOK tokens each), or
 // false when the slot is past its sequence's end.  Slot bases: n * ceil(T/TOK) for fixed-length
-// batches, floor(cu[n]/TOK) + n for packed ones (ceil(len/TOK) <= floor(len/TOK) + 1 keeps them
-// disjoint).
+// batches, floor(bos_n/TOK) + n for packed ones (ceil(len/TOK) <= floor(len/TOK) + 1 keeps them
+// disjoint, and floor(bos/TOK) + ceil(len/TOK) <= ceil(T/TOK) keeps them below the
+// T/TOK + N + 1 slots of the workspace).
 template <int TOK>
 __device__ __forceinline__ bool locate_slot(const ChunkArgs& p, int64_t slot, int& n,
                                             int64_t& j, int64_t& bos, int64_t& len) {
@@ -259,13 +274,14 @@ __device__ __forceinline__ bool locate_slot(const ChunkArgs& p, int64_t slot, in
         int lo = 0, hi = p.n_seqs - 1;
         while (lo < hi) {                 // largest n with base(n) <= slot
             const int mid = (lo + hi + 1) >> 1;
-            const int64_t base = static_cast<int64_t>(p.cu[mid] / TOK) + mid;
+            const int64_t base = seq_start(p, mid) / TOK + mid;
             if (base <= slot) lo = mid; else hi = mid - 1;
         }
         n = lo;
-        bos = p.cu[n];
-        len = static_cast<int64_t>(p.cu[n + 1]) - bos;
-        j = slot - (static_cast<int64_t>(p.cu[n] / TOK) + n);
+        int64_t end;
+        seq_bounds(p, n, bos, end);
+        len = end - bos;
+        j = slot - (bos / TOK + n);
     } else {
         const int64_t nrec = (p.T + TOK - 1) / TOK;
         if (nrec == 0) return false;
@@ -581,8 +597,11 @@ __device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_S
 //   * the record's Kt_1 and Qt_1 are scaled by sub-block 0's e^{G_15} (from the record's first
 //     token) and its Kb_0 by sub-block 1's (to the record's last token).
 // Kt and Qt leave as whole 1 KB wave stores from registers; Kb^T (channel-major) goes through LDS.
+// Occupancy hint: three waves per SIMD fit the register budget with a 16-bit g or z; an fp32 g
+// or z tile holds twice the registers and two fit.
 template <int DK, int GDT, bool GATE>
-__global__ void __launch_bounds__(64, 3) chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
+__global__ void __launch_bounds__(64, GDT == KDA_BF16 ? 3 : 2)
+chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     using R = Rec<DK, false>;
     constexpr int TOKR = R::TOK;          // tokens per record: two sub-blocks
     constexpr int KS = DK / 32;           // 32-channel groups
@@ -956,12 +975,14 @@ __device__ __forceinline__ bool locate_seg(const ChunkArgs& p, int64_t slot, int
         int lo = 0, hi = p.n_seqs - 1;
         while (lo < hi) {                 // largest n with base(n) <= slot
             const int mid = (lo + hi + 1) >> 1;
-            const int64_t base = static_cast<int64_t>(p.cu[mid]) / SEG_TOK + mid;
+            const int64_t base = seq_start(p, mid) / SEG_TOK + mid;
             if (base <= slot) lo = mid; else hi = mid - 1;
         }
         n = lo;
-        s = slot - (static_cast<int64_t>(p.cu[n]) / SEG_TOK + n);
-        return s >= 0 && s < seg_count(static_cast<int64_t>(p.cu[n + 1]) - p.cu[n]);
+        int64_t bos, end;
+        seq_bounds(p, n, bos, end);
+        s = slot - (bos / SEG_TOK + n);
+        return s >= 0 && s < seg_count(end - bos);
     }
     const int64_t per = seg_count(p.T);
     n = static_cast<int>(slot / per);
@@ -1025,9 +1046,10 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
 
     int64_t bos, len, base;
     if (p.cu) {
-        bos = p.cu[n];
-        len = static_cast<int64_t>(p.cu[n + 1]) - bos;
-        base = static_cast<int64_t>(p.cu[n] / R::TOK) + n;
+        int64_t end;
+        seq_bounds(p, n, bos, end);
+        len = end - bos;
+        base = bos / R::TOK + n;
     } else {
         bos = static_cast<int64_t>(n) * p.T;
         len = p.T;
@@ -1085,7 +1107,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     // floor(cu[n] / every) + n for packed ones (disjoint for the same reason as the block slots).
     const int64_t ck_every = CKPT ? p.ckpt_every : 1;
     const int64_t ck_base = !CKPT ? 0
-                            : p.cu ? static_cast<int64_t>(p.cu[n]) / ck_every + n
+                            : p.cu ? bos / ck_every + n
                                    : static_cast<int64_t>(n) * (p.T / ck_every);
     auto checkpoint = [&](int64_t done) {          // `done` tokens of the sequence processed
         if constexpr (!CKPT) return;
@@ -1371,8 +1393,10 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
     const int n = static_cast<int>(useq / H), h = static_cast<int>(useq % H);
     int64_t len, slot0;
     if (p.cu) {
-        len = static_cast<int64_t>(p.cu[n + 1]) - p.cu[n];
-        slot0 = static_cast<int64_t>(p.cu[n]) / SEG_TOK + n;
+        int64_t bos, end;
+        seq_bounds(p, n, bos, end);
+        len = end - bos;
+        slot0 = bos / SEG_TOK + n;
     } else {
         len = p.T;
         slot0 = static_cast<int64_t>(n) * seg_count(p.T);

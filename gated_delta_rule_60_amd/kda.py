@@ -93,10 +93,62 @@ def _dt(t: torch.Tensor) -> int:
         raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)") from None
 
 
-def _stream(stream) -> ctypes.c_void_p:
+_FLOATS = (torch.float32, torch.bfloat16)
+
+
+def _expect(fn: str, name: str, t, shape, dtypes=None):
+    """Host-side argument check: t (None = absent) must be a contiguous tensor of the given
+    shape (None entries match any size) and, when given, one of `dtypes`."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{fn}: {name} must be a torch.Tensor")
+    if len(t.shape) != len(shape) or any(w is not None and int(a) != int(w)
+                                         for a, w in zip(t.shape, shape)):
+        want = tuple("*" if w is None else int(w) for w in shape)
+        raise ValueError(f"{fn}: {name} must have shape {want}, got {tuple(t.shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{fn}: {name} must be one of {[str(d) for d in dtypes]}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{fn}: {name} must be contiguous")
+
+
+def _same_dtype(fn: str, **named):
+    dts = {n: t.dtype for n, t in named.items() if t is not None}
+    if len(set(dts.values())) > 1:
+        raise ValueError(f"{fn}: {', '.join(dts)} must share one dtype, got {dts}")
+
+
+def _one_device(fn: str, **named) -> torch.device:
+    """Every tensor handed to the library must live on the same GPU: a host pointer reaching a
+    kernel would fault the device."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{fn}: {name} must be a GPU tensor, got one on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{fn}: {name} is on {t.device}, the other tensors on {dev}")
+    return dev
+
+
+def _torch_stream(stream, device):
+    """The torch stream the work goes to: None = the current stream of `device`; a raw
+    hipStream_t (int) is wrapped.  Outputs and workspaces the binding allocates are allocated on
+    this stream, so the caching allocator never hands their memory to other work while the
+    library's kernels may still use it."""
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream, device=device)
+    return stream
+
+
+def _sptr(ts) -> ctypes.c_void_p:
+    return ctypes.c_void_p(ts.cuda_stream)
 
 
 def _check(fn: str, status: int):
@@ -115,14 +167,21 @@ def kda_version() -> int:
 def kda_gate(A: torch.Tensor, z: torch.Tensor, g: Optional[torch.Tensor] = None,
              g_dtype: torch.dtype = torch.float32, g_min: float = -5.0, stream=None) -> torch.Tensor:
     """g = g_min * sigmoid(exp(A) * z); A [H, dk] fp32, z [..., H, dk] -> g like z (g_dtype)."""
+    fn = "kda_gate"
+    _expect(fn, "A", A, (None, None), (torch.float32,))
     H, dk = A.shape
-    if z.shape[-2:] != (H, dk):
-        raise ValueError("z must end in [H, dk]")
+    if z.dim() < 2:
+        raise ValueError(f"{fn}: z must end in [H, dk]")
+    _expect(fn, "z", z, tuple(z.shape[:-2]) + (H, dk), _FLOATS)
+    _expect(fn, "g", g, tuple(z.shape), _FLOATS)
+    dev = _one_device(fn, A=A, z=z, g=g)
+    ts = _torch_stream(stream, dev)
     if g is None:
-        g = torch.empty(z.shape, dtype=g_dtype, device=z.device)
+        with torch.cuda.stream(ts):
+            g = torch.empty(z.shape, dtype=g_dtype, device=dev)
     n_tokens = z.numel() // (H * dk)
-    _check("kda_gate", load_library().kda_gate(_ptr(A), _ptr(z), _dt(z), _ptr(g), _dt(g),
-                                               n_tokens, H, dk, float(g_min), _stream(stream)))
+    _check(fn, load_library().kda_gate(_ptr(A), _ptr(z), _dt(z), _ptr(g), _dt(g), n_tokens, H,
+                                       dk, float(g_min), _sptr(ts)))
     return g
 
 
@@ -132,36 +191,74 @@ def kda_chunk_fwd_workspace_size(n_seqs: int, total_tokens: int, H: int, dk: int
                                                             chunk, _DT[in_dtype]))
 
 
+def _check_prefill(fn, q, k, v, beta, gz, initial_state, final_state, cu_seqlens, o, workspace,
+                   A=None, checkpoints=None):
+    """Shapes, dtypes and devices of a prefill call, checked on the host before the library is
+    called.  Returns (B, T, N, H, dk, dv, device)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError(f"{fn}: q must be a [B, T, H, dk] tensor")
+    B, T, H, dk = (int(x) for x in q.shape)
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError(f"{fn}: v must be a [B, T, H, dv] tensor")
+    dv = int(v.shape[-1])
+    _expect(fn, "q", q, (B, T, H, dk), _FLOATS)
+    _expect(fn, "k", k, (B, T, H, dk), _FLOATS)
+    _expect(fn, "v", v, (B, T, H, dv), _FLOATS)
+    _expect(fn, "beta", beta, (B, T, H), _FLOATS)
+    _same_dtype(fn, q=q, k=k, v=v, beta=beta)
+    _expect(fn, "g" if A is None else "z", gz, (B, T, H, dk), _FLOATS)
+    _expect(fn, "A", A, (H, dk), (torch.float32,))
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError(f"{fn}: cu_seqlens needs B == 1 (a packed batch)")
+        _expect(fn, "cu_seqlens", cu_seqlens, (None,), (torch.int32,))
+        if cu_seqlens.numel() < 2:
+            raise ValueError(f"{fn}: cu_seqlens needs at least two offsets")
+    N = B if cu_seqlens is None else int(cu_seqlens.numel()) - 1
+    _expect(fn, "initial_state", initial_state, (N, H, dk, dv), (torch.float32,))
+    _expect(fn, "final_state", final_state, (N, H, dk, dv), (torch.float32,))
+    _expect(fn, "o", o, (B, T, H, dv), _FLOATS)
+    _expect(fn, "checkpoints", checkpoints, (None, H, dk, dv), (torch.float32,))
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError(f"{fn}: workspace must be contiguous")
+    dev = _one_device(fn, q=q, k=k, v=v, beta=beta, gz=gz, A=A, initial_state=initial_state,
+                      final_state=final_state, cu_seqlens=cu_seqlens, o=o, workspace=workspace,
+                      checkpoints=checkpoints)
+    return B, T, N, H, dk, dv, dev
+
+
+def _chunk_outputs(q, B, T, N, H, dk, dv, o, o_dtype, final_state, output_final_state,
+                   workspace, ts):
+    """Allocate (on the launch stream) what the caller did not pass."""
+    with torch.cuda.stream(ts):
+        if o is None:
+            o = torch.empty((B, T, H, dv), dtype=o_dtype or q.dtype, device=q.device)
+        if final_state is None and output_final_state:
+            final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+        need = kda_chunk_fwd_workspace_size(N, B * T, H, dk, dv, in_dtype=q.dtype)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return o, final_state, workspace, ws_bytes
+
+
 def kda_chunk_fwd(q, k, v, beta, g, initial_state=None, final_state=None, cu_seqlens=None,
                   o=None, o_dtype=None, scale: float = 1.0, output_final_state: bool = True,
                   workspace=None, stream=None):
     """Chunked prefill.  q, k, g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H];
     initial_state [N, H, dk, dv] fp32 or None; cu_seqlens device int32 [N+1] or None (B == 1).
     Returns (o, final_state); final_state is allocated when output_final_state and not given."""
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    N, o, final_state, workspace, ws_bytes = _chunk_outputs(
-        q, v, cu_seqlens, o, o_dtype, final_state, output_final_state, workspace)
-    _check("kda_chunk_fwd", load_library().kda_chunk_fwd(
+    fn = "kda_chunk_fwd"
+    B, T, N, H, dk, dv, dev = _check_prefill(fn, q, k, v, beta, g, initial_state, final_state,
+                                             cu_seqlens, o, workspace)
+    ts = _torch_stream(stream, dev)
+    o, final_state, workspace, ws_bytes = _chunk_outputs(
+        q, B, T, N, H, dk, dv, o, o_dtype, final_state, output_final_state, workspace, ts)
+    _check(fn, load_library().kda_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(g), _dt(g), _ptr(initial_state),
         _ptr(final_state), _ptr(cu_seqlens), _ptr(o), _dt(o), B, T, N, H, dk, dv, 64,
-        float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
+        float(scale), _ptr(workspace), ws_bytes, _sptr(ts)))
     return o, final_state
-
-
-def _chunk_outputs(q, v, cu_seqlens, o, o_dtype, final_state, output_final_state, workspace):
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
-    if o is None:
-        o = torch.empty((B, T, H, dv), dtype=o_dtype or q.dtype, device=q.device)
-    if final_state is None and output_final_state:
-        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
-    need = kda_chunk_fwd_workspace_size(N, B * T, H, dk, dv, in_dtype=q.dtype)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    return N, o, final_state, workspace, ws_bytes
 
 
 def kda_chunk_fwd_gated(q, k, v, beta, A, z, g_min: float = -5.0, initial_state=None,
@@ -170,14 +267,16 @@ def kda_chunk_fwd_gated(q, k, v, beta, A, z, g_min: float = -5.0, initial_state=
                         stream=None):
     """Chunked prefill with the gate fused: A [H, dk] fp32 and z [B, T, H, dk] replace g.
     Same outputs as kda_gate followed by kda_chunk_fwd (fp32 g)."""
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    N, o, final_state, workspace, ws_bytes = _chunk_outputs(
-        q, v, cu_seqlens, o, o_dtype, final_state, output_final_state, workspace)
-    _check("kda_chunk_fwd_gated", load_library().kda_chunk_fwd_gated(
+    fn = "kda_chunk_fwd_gated"
+    B, T, N, H, dk, dv, dev = _check_prefill(fn, q, k, v, beta, z, initial_state, final_state,
+                                             cu_seqlens, o, workspace, A=A)
+    ts = _torch_stream(stream, dev)
+    o, final_state, workspace, ws_bytes = _chunk_outputs(
+        q, B, T, N, H, dk, dv, o, o_dtype, final_state, output_final_state, workspace, ts)
+    _check(fn, load_library().kda_chunk_fwd_gated(
         _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(A), _ptr(z), _dt(z), float(g_min),
         _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(o), _dt(o), B, T, N, H,
-        dk, dv, 64, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
+        dk, dv, 64, float(scale), _ptr(workspace), ws_bytes, _sptr(ts)))
     return o, final_state
 
 
@@ -204,35 +303,65 @@ def kda_chunk_fwd_checkpointed(q, k, v, beta, every: int, g=None, A=None, z=None
     64) of each sequence.  Give g (as kda_chunk_fwd) or A and z (as kda_chunk_fwd_gated).
     Returns (o, final_state, checkpoints [slots, H, dk, dv] fp32); slot layout as
     checkpoint_layout; a new checkpoints buffer starts zeroed."""
+    fn = "kda_chunk_fwd_checkpointed"
     if (g is None) == (A is None or z is None):
         raise ValueError("give either g, or A and z")
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    N, o, final_state, workspace, ws_bytes = _chunk_outputs(
-        q, v, cu_seqlens, o, o_dtype, final_state, output_final_state, workspace)
+    gz = g if g is not None else z
+    B, T, N, H, dk, dv, dev = _check_prefill(fn, q, k, v, beta, gz, initial_state, final_state,
+                                             cu_seqlens, o, workspace, A=A,
+                                             checkpoints=checkpoints)
+    ts = _torch_stream(stream, dev)
+    o, final_state, workspace, ws_bytes = _chunk_outputs(
+        q, B, T, N, H, dk, dv, o, o_dtype, final_state, output_final_state, workspace, ts)
     need = (B * (T // every)) if cu_seqlens is None else (T // every + N)
     if checkpoints is None:
-        checkpoints = torch.zeros((need, H, dk, dv), dtype=torch.float32, device=q.device)
-    gz = g if g is not None else z
-    _check("kda_chunk_fwd_checkpointed", load_library().kda_chunk_fwd_checkpointed(
+        with torch.cuda.stream(ts):
+            checkpoints = torch.zeros((need, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(fn, load_library().kda_chunk_fwd_checkpointed(
         _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(A), _ptr(gz), _dt(gz), float(g_min),
         _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(o), _dt(o), B, T, N, H,
         dk, dv, 64, float(scale), _ptr(checkpoints), int(every), checkpoints.shape[0],
-        _ptr(workspace), ws_bytes, _stream(stream)))
+        _ptr(workspace), ws_bytes, _sptr(ts)))
     return o, final_state, checkpoints
+
+
+def _check_decode(fn, q, k, v, beta, g, state, o, draft: bool, accepted=None):
+    """Shapes, dtypes and devices of the decode calls: [N, H, d] per token, or [N, K, H, d]
+    for a draft of K tokens.  Returns (N, K, H, dk, dv, device)."""
+    nd = 4 if draft else 3
+    if not isinstance(q, torch.Tensor) or q.dim() != nd:
+        raise ValueError(f"{fn}: q must be a {'[N, K, H, dk]' if draft else '[N, H, dk]'} tensor")
+    if not isinstance(v, torch.Tensor) or v.dim() != nd:
+        raise ValueError(f"{fn}: v must have {nd} dimensions")
+    lead = tuple(int(x) for x in q.shape[:-1])
+    N, H, dk, dv = lead[0], lead[-1], int(q.shape[-1]), int(v.shape[-1])
+    K = lead[1] if draft else 1
+    _expect(fn, "q", q, lead + (dk,), _FLOATS)
+    _expect(fn, "k", k, lead + (dk,), _FLOATS)
+    _expect(fn, "v", v, lead + (dv,), _FLOATS)
+    _expect(fn, "beta", beta, lead, _FLOATS)
+    _same_dtype(fn, q=q, k=k, v=v, beta=beta)
+    _expect(fn, "g", g, lead + (dk,), _FLOATS)
+    _expect(fn, "state", state, (N, H, dk, dv), (torch.float32,))
+    _expect(fn, "o", o, lead + (dv,), _FLOATS)
+    _expect(fn, "accepted", accepted, (N,), (torch.int32,))
+    dev = _one_device(fn, q=q, k=k, v=v, beta=beta, g=g, state=state, o=o, accepted=accepted)
+    return N, K, H, dk, dv, dev
 
 
 def kda_decode_step(q, k, v, beta, g, state, o=None, o_dtype=None, scale: float = 1.0,
                     stream=None):
     """One token per sequence: q, k, g [N, H, dk]; v [N, H, dv]; beta [N, H]; state
     [N, H, dk, dv] fp32 updated in place.  Returns o [N, H, dv]."""
-    N, H, dk = q.shape
-    dv = v.shape[-1]
+    fn = "kda_decode_step"
+    N, _, H, dk, dv, dev = _check_decode(fn, q, k, v, beta, g, state, o, draft=False)
+    ts = _torch_stream(stream, dev)
     if o is None:
-        o = torch.empty((N, H, dv), dtype=o_dtype or q.dtype, device=q.device)
-    _check("kda_decode_step", load_library().kda_decode_step(
+        with torch.cuda.stream(ts):
+            o = torch.empty((N, H, dv), dtype=o_dtype or q.dtype, device=dev)
+    _check(fn, load_library().kda_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(g), _dt(g), _ptr(state), _ptr(o),
-        _dt(o), N, H, dk, dv, float(scale), _stream(stream)))
+        _dt(o), N, H, dk, dv, float(scale), _sptr(ts)))
     return o
 
 
@@ -240,24 +369,28 @@ def kda_decode_verify(q, k, v, beta, g, state, o=None, o_dtype=None, scale: floa
                       stream=None):
     """K draft tokens per sequence from a read-only state: q, k, g [N, K, H, dk]; v [N, K, H, dv];
     beta [N, K, H]; state [N, H, dk, dv] fp32 (not modified).  Returns o [N, K, H, dv]."""
-    N, Kd, H, dk = q.shape
-    dv = v.shape[-1]
+    fn = "kda_decode_verify"
+    N, Kd, H, dk, dv, dev = _check_decode(fn, q, k, v, beta, g, state, o, draft=True)
+    ts = _torch_stream(stream, dev)
     if o is None:
-        o = torch.empty((N, Kd, H, dv), dtype=o_dtype or q.dtype, device=q.device)
-    _check("kda_decode_verify", load_library().kda_decode_verify(
+        with torch.cuda.stream(ts):
+            o = torch.empty((N, Kd, H, dv), dtype=o_dtype or q.dtype, device=dev)
+    _check(fn, load_library().kda_decode_verify(
         _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(g), _dt(g), _ptr(state), _ptr(o),
-        _dt(o), N, Kd, H, dk, dv, float(scale), _stream(stream)))
+        _dt(o), N, Kd, H, dk, dv, float(scale), _sptr(ts)))
     return o
 
 
 def kda_decode_commit(q, k, v, beta, g, state, accepted, stream=None):
     """Advance each state in place by its first accepted[n] draft tokens (device int32 [N]);
     inputs as kda_decode_verify.  Returns state."""
-    N, Kd, H, dk = q.shape
-    dv = v.shape[-1]
-    if accepted.dtype != torch.int32:
-        raise TypeError("accepted must be int32")
-    _check("kda_decode_commit", load_library().kda_decode_commit(
+    fn = "kda_decode_commit"
+    if not isinstance(accepted, torch.Tensor) or accepted.dtype != torch.int32:
+        raise TypeError(f"{fn}: accepted must be an int32 tensor")
+    N, Kd, H, dk, dv, dev = _check_decode(fn, q, k, v, beta, g, state, None, draft=True,
+                                          accepted=accepted)
+    ts = _torch_stream(stream, dev)
+    _check(fn, load_library().kda_decode_commit(
         _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(g), _dt(g), _ptr(state),
-        _ptr(accepted), N, Kd, H, dk, dv, _stream(stream)))
+        _ptr(accepted), N, Kd, H, dk, dv, _sptr(ts)))
     return state

@@ -24,6 +24,27 @@ def rel_err(x, ref) -> float:
     return float(np.abs(x - ref).max() / (denom if denom > 0 else 1.0))
 
 
+def _np64(x):
+    return np.asarray(x.detach().double().cpu().numpy() if isinstance(x, torch.Tensor) else x,
+                      dtype=np.float64)
+
+
+def worst_unit_errs(o, o_ref, S, S_ref, cu=None):
+    """The parity metric per (sequence, head) unit -- each unit's o rows and final state
+    normalised by that unit's own max|ref| -- and the worst over units: (o err, state err)."""
+    o, o_ref, S, S_ref = _np64(o), _np64(o_ref), _np64(S), _np64(S_ref)
+    N, H = S_ref.shape[:2]
+    eo = es = 0.0
+    for n in range(N):
+        b, rows = (0, slice(int(cu[n]), int(cu[n + 1]))) if cu is not None else (n, slice(None))
+        for h in range(H):
+            ref = o_ref[b, rows, h]
+            if ref.size:
+                eo = max(eo, rel_err(o[b, rows, h], ref))
+            es = max(es, rel_err(S[n, h], S_ref[n, h]))
+    return eo, es
+
+
 def oracle_g(d, g_dtype=torch.float32):
     """Gate values from the fp64 oracle, rounded to the dtype both sides consume."""
     g64 = oracle.gate(d["A"], d["z"])
