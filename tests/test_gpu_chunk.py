@@ -162,13 +162,8 @@ def test_prefill_scale():
     check_full(d, oracle_g(d), TOL["bf16"], scale=0.125, label="scale")
 
 
-def test_split_invariance_and_inplace_state():
-    """[0, T) in one call equals [0, T1) then [T1, T) through the emitted state (the second call
-    updating the state in place); the state carries the whole history."""
-    d = prefill_case("prefill_bf16", B=2, H=3, T=320)
-    g = oracle_g(d)
-    o_full, h_full = run_gpu(d, g)
-    T1 = 100
+def _split_run(d, g, T1):
+    """[0, T1) then [T1, T) through the emitted state, the second call updating it in place."""
     first = {k: (v[:, :T1] if isinstance(v, torch.Tensor) and v.dim() >= 3 and k != "S0" else v)
              for k, v in d.items()}
     o1, h1 = run_gpu(first, g[:, :T1])
@@ -176,12 +171,25 @@ def test_split_invariance_and_inplace_state():
     o2, h2 = K.kda_chunk_fwd(*qs, g[:, T1:].contiguous().to(DEV), initial_state=h1,
                              final_state=h1, o_dtype=torch.float32)
     torch.cuda.synchronize()
-    # a split at a token that is not a block boundary changes the blocking, so the two runs agree
-    # to the kernel's rounding, not bit for bit
-    eo = rel_err(torch.cat([o1, o2], 1), o_full.double().cpu().numpy())
-    es = rel_err(h2, h_full.double().cpu().numpy())
-    say(f"  split vs whole: o {eo:.2e}  S {es:.2e}")
-    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    return torch.cat([o1, o2], 1), h2
+
+
+def test_split_invariance_and_inplace_state():
+    """[0, T) in one call equals [0, T1) then [T1, T) through the emitted state (the second call
+    updating the state in place): the state carries the whole history.  A split on a chunk
+    boundary keeps every record's tokens, so the two runs agree bit for bit; a split inside a
+    record changes the blocking, and they agree to the kernels' rounding (the state much more
+    closely than o, whose error the fp16-staged products dominate)."""
+    d = prefill_case("prefill_bf16", B=2, H=3, T=320)
+    g = oracle_g(d)
+    o_full, h_full = run_gpu(d, g)
+    o_s, h_s = _split_run(d, g, 128)
+    assert torch.equal(o_s, o_full) and torch.equal(h_s, h_full)
+    o_s, h_s = _split_run(d, g, 100)
+    eo = rel_err(o_s, o_full.double().cpu().numpy())
+    es = rel_err(h_s, h_full.double().cpu().numpy())
+    say(f"  split at 100 vs whole: o {eo:.2e}  S {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= 1e-4
 
 
 def test_decode_steps_equal_prefill():

@@ -113,16 +113,18 @@ def test_binding_on_a_side_stream():
     args = [d[x].to(DEV) for x in ("q", "k", "v", "beta")]
     h0 = d["S0"].to(DEV)
     o_ref, h_ref = K.kda_chunk_fwd(*args, g, initial_state=h0, o_dtype=torch.float32)
+    A, z = d["A"].to(DEV), d["z"].to(DEV)
+    og_ref, hg_ref = K.kda_chunk_fwd_gated(*args, A, z, initial_state=h0, o_dtype=torch.float32)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     for _ in range(3):   # allocations and frees on the side stream between calls
         o, h = K.kda_chunk_fwd(*args, g, initial_state=h0, o_dtype=torch.float32, stream=side)
-        o2, h2 = K.kda_chunk_fwd_gated(*args, d["A"].to(DEV), d["z"].to(DEV), initial_state=h0,
-                                       o_dtype=torch.float32, stream=side.cuda_stream)
+        o2, h2 = K.kda_chunk_fwd_gated(*args, A, z, initial_state=h0, o_dtype=torch.float32,
+                                       stream=side.cuda_stream)
     side.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(h, h_ref)
-    assert rel_err(o2, o_ref.double().cpu().numpy()) <= 1e-5
+    assert torch.equal(o2, og_ref) and torch.equal(h2, hg_ref)
 
 
 def test_decode_outside_usual_range():
