@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/kda.h"
 #include "kda_internal.hpp"
@@ -29,6 +30,45 @@ bool overlap(Range a, Range b) {
 }
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+// ---- the prefill workspace of kda_chunk_fwd_gated_noalloc: a static device array ------------
+// Each GPU the library runs on holds its own copy from the first use on that device until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device memory: the
+// device address comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is ever handed to kernels.
+__device__ __align__(256) uint8_t scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device `stream` belongs to.
+hipError_t scratch_address(hipStream_t stream, void** out) {
+    int dev = 0, cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (stream != nullptr) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 }  // namespace
 
@@ -164,6 +204,29 @@ int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void*
     return chunk_fwd_impl(q, k, v, beta, in_dtype, z, z_dtype, A, g_min, initial_state,
                           final_state, cu_seqlens, o, o_dtype, B, T, n_seqs, H, dk, dv, chunk,
                           scale, workspace, workspace_bytes, stream, true);
+}
+
+int kda_chunk_fwd_gated_noalloc(const void* q, const void* k, const void* v, const void* beta,
+                                int in_dtype, const float* A, const void* z, int z_dtype,
+                                float g_min, const float* initial_state, float* final_state,
+                                const int32_t* cu_seqlens, void* o, int o_dtype, int32_t B,
+                                int64_t T, int32_t n_seqs, int32_t H, int32_t dk, int32_t dv,
+                                int32_t chunk, float scale, void* stream) {
+    // sizes first: a call whose workspace would not fit is refused before any device work
+    if (B < 1 || T < 0 || n_seqs < 1 || H < 1 || !valid_dtype(in_dtype))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_d(dk) || !supported_d(dv) || chunk != 64) return KDA_ERR_UNSUPPORTED;
+    const size_t need = kda::chunk_workspace_bytes(n_seqs, int64_t(B) * T, H, dk, dv, in_dtype);
+    if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = scratch_address(static_cast<hipStream_t>(stream), &ws);
+        if (e != hipSuccess) return KDA_ERR_HIP;
+    }
+    return chunk_fwd_impl(q, k, v, beta, in_dtype, z, z_dtype, A, g_min, initial_state,
+                          final_state, cu_seqlens, o, o_dtype, B, T, n_seqs, H, dk, dv, chunk,
+                          scale, ws, need > 0 ? size_t(KDA_NOALLOC_SCRATCH_BYTES) : 0, stream,
+                          true);
 }
 
 int kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* v, const void* beta,

@@ -55,6 +55,10 @@ def load_library(path: Optional[str] = None):
                                         vp, vp, vp, vp, ctypes.c_int, i32, i64, i32, i32, i32,
                                         i32, i32, f32, vp, sz, vp]
     lib.kda_chunk_fwd_gated.restype = ctypes.c_int
+    lib.kda_chunk_fwd_gated_noalloc.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp,
+                                                ctypes.c_int, f32, vp, vp, vp, vp, ctypes.c_int,
+                                                i32, i64, i32, i32, i32, i32, i32, f32, vp]
+    lib.kda_chunk_fwd_gated_noalloc.restype = ctypes.c_int
     lib.kda_chunk_fwd_checkpointed.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int,
                                                f32, vp, vp, vp, vp, ctypes.c_int, i32, i64, i32,
                                                i32, i32, i32, i32, f32, vp, i32, i64, vp, sz, vp]
@@ -74,8 +78,12 @@ def load_library(path: Optional[str] = None):
 
 
 EXPORTED = ["kda_status_string", "kda_version", "kda_gate", "kda_chunk_fwd_workspace_size",
-            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_checkpointed", "kda_decode_step",
-            "kda_decode_verify", "kda_decode_commit"]
+            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_noalloc",
+            "kda_chunk_fwd_checkpointed", "kda_decode_step", "kda_decode_verify",
+            "kda_decode_commit"]
+
+# Size of the library's static prefill workspace used by kda_chunk_fwd_gated_noalloc.
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -277,6 +285,26 @@ def kda_chunk_fwd_gated(q, k, v, beta, A, z, g_min: float = -5.0, initial_state=
         _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(A), _ptr(z), _dt(z), float(g_min),
         _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(o), _dt(o), B, T, N, H,
         dk, dv, 64, float(scale), _ptr(workspace), ws_bytes, _sptr(ts)))
+    return o, final_state
+
+
+def kda_chunk_fwd_gated_noalloc(q, k, v, beta, A, z, o, final_state=None, g_min: float = -5.0,
+                                initial_state=None, cu_seqlens=None, scale: float = 1.0,
+                                stream=None):
+    """kda_chunk_fwd_gated with the workspace taken from the library's static device array
+    (NOALLOC_SCRATCH_BYTES per GPU): nothing is allocated, here or in the library, so o (and
+    final_state, if wanted) must be passed in.  Calls that overlap on one GPU race on the array.
+    Returns (o, final_state)."""
+    fn = "kda_chunk_fwd_gated_noalloc"
+    if o is None:
+        raise ValueError(f"{fn}: o must be given (nothing is allocated)")
+    B, T, N, H, dk, dv, dev = _check_prefill(fn, q, k, v, beta, z, initial_state, final_state,
+                                             cu_seqlens, o, None, A=A)
+    ts = _torch_stream(stream, dev)
+    _check(fn, load_library().kda_chunk_fwd_gated_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dt(q), _ptr(A), _ptr(z), _dt(z), float(g_min),
+        _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(o), _dt(o), B, T, N, H,
+        dk, dv, 64, float(scale), _sptr(ts)))
     return o, final_state
 
 

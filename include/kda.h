@@ -146,6 +146,31 @@ int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const void 
                         size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_fwd_gated_noalloc -- kda_chunk_fwd_gated for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * It takes no workspace argument; the prefill's workspace is a static device array of
+ * KDA_NOALLOC_SCRATCH_BYTES inside the library, which each GPU holds from the first call on it
+ * until the process ends.  The call itself allocates nothing.
+ *   Sizes: the call is refused with KDA_ERR_WORKSPACE, before any device work, when
+ *   kda_chunk_fwd_workspace_size(n_seqs, B*T, H, dk, dv, 64, in_dtype) exceeds
+ *   KDA_NOALLOC_SCRATCH_BYTES (256 MiB: e.g. 16-bit inputs with d_k = 128 up to about 290 K
+ *   token-heads, such as 4 x 4096 tokens x 16 heads).
+ *   Sharing: every call on one GPU uses that GPU's array.  Nothing in it has to start at zero and
+ *   it keeps the last call's contents; calls that overlap in time on one GPU (another stream,
+ *   another thread) race on it and must be serialised by the caller.
+ *   Device: the array of the device `stream` belongs to (the current device for NULL) is used.
+ * Every other argument, the results (equal to kda_chunk_fwd_gated's bit for bit) and the error
+ * behaviour are those of kda_chunk_fwd_gated.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int kda_chunk_fwd_gated_noalloc(const void *q, const void *k, const void *v, const void *beta,
+                                int in_dtype, const float *A, const void *z, int z_dtype,
+                                float g_min, const float *initial_state, float *final_state,
+                                const int32_t *cu_seqlens, void *o, int o_dtype, int32_t B,
+                                int64_t T, int32_t n_seqs, int32_t H, int32_t dk, int32_t dv,
+                                int32_t chunk, float scale, void *stream);
+
+/*
  * kda_chunk_fwd_checkpointed -- the chunked prefill that also stores the state at fixed token
  * boundaries, for prefix caching: a later request that shares a prefix resumes from the stored
  * state (copy it, then continue) instead of recomputing the prefix ([habr, § Как обслуживать
