@@ -30,7 +30,8 @@
  *   - Every call returns a kda_status; nothing is printed and nothing aborts.  Host-checkable
  *     argument errors are reported before any device work is enqueued.  Device-resident
  *     preconditions (g in [-5, 0], well-formed cu_seqlens) are the caller's contract and are not
- *     checked; violating them gives undefined (but memory-safe) results.
+ *     checked; violating them gives unspecified results but no out-of-bounds access: the
+ *     kernels clamp every offset to 0 <= cu_seqlens[n] <= cu_seqlens[n+1] <= T before using it.
  *   - Debug check: with the environment variable KDA_DEBUG_VALIDATE set (to anything but "" or
  *     "0"), kda_chunk_fwd, kda_chunk_fwd_checkpointed and the three decode calls first test those
  *     preconditions on the device (kda_chunk_fwd_gated tests cu_seqlens only: its g is in range
@@ -118,10 +119,16 @@ size_t kda_chunk_fwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_
  *                   unspecified.  It must not overlap any other argument.  Calls that share
  *                   a workspace must not overlap in time.
  * Results match the token-by-token definition up to rounding: the kernels evaluate the chunked
- * form with fp32 accumulation and split-precision matrix products.  For bf16 inputs some
- * range-bounded operands are staged in fp16; this assumes the usual KDA inputs -- q and k
- * L2-normalised per head, beta in [0, 1], |v| and |scale * q| well below 65504 -- outside which
- * intermediate values can leave the fp16 range.  fp32 inputs use bf16 hi/lo splits throughout.
+ * form with fp32 accumulation and split-precision matrix products.  Any finite input values are
+ * accepted (beta included: the pages give it no range).  For bf16 inputs the state-pass operands
+ * are staged in fp16, whose largest value is 65504: the results hold their tolerance while the
+ * state, initial_state, v, scale * |q| * |k| and the entries of each 16-token block's UT
+ * transform stay well inside that range.  The usual KDA inputs (q, k L2-normalised, beta in
+ * [0, 1], the gate's decay) keep them below 10; the tests also cover beta in [-0.5, 1.5],
+ * |q| = |k| = 3 with scale 4 and |v| about 30 (states to about 1000).  Keys with
+ * beta * |k|^2 > 2 make the recurrence itself expansive along k (the transition scales that
+ * direction by 1 - beta |k|^2 alpha), so long sequences of such inputs overflow any precision.
+ * fp32 inputs use bf16 hi/lo splits throughout and have the fp32 range.
  */
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *beta, int in_dtype,
                   const void *g, int g_dtype, const float *initial_state, float *final_state,
