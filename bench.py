@@ -1,23 +1,25 @@
 """Benchmark of the KDA forward pass on one MI355X.
 
-One step = one pass of the prefill hot path over the bf16 prefill workload (B=4, H=16, T=4096,
-d_k=d_v=128, chunk 64, random fp32 initial state): kda_chunk_fwd_gated, i.e. the forget gate,
-the intra-block work and the state pass, from A and z (bf16) to o (bf16) and the final state
-(fp32).  The same step through the separate kda_gate + kda_chunk_fwd entry points is timed too
-and reported under "unfused".  Inputs are synthetic (seeded generators, the workload's shapes
-and distributions) and resident in HBM before the timed region starts.  The decode workload
-(256 sequences x 32 heads, 64 in-place steps, plus speculative-decode verify and commit) is
-timed in the same run and reported under "decode", the long workload (1 x 65536 tokens, 32
-heads, run in 8192-token segments) under "long_prefill", and the packed workload (8 sequences of
-seeded log-uniform lengths summing to 2^20 tokens, 8 heads, cu_seqlens) under "packed_prefill".
+One step = one pass of the prefill hot path over the largest single-GPU workload: 8 packed
+sequences whose seeded log-uniform lengths in [1K, 256K] sum to 2^20 tokens, 8 heads,
+d_k = d_v = 128, chunk 64, per-sequence fp32 initial states, cu_seqlens offsets.  The step is
+kda_chunk_fwd_gated -- the forget gate, the intra-block work and the state pass (in segments
+for these long sequences), from A and z (bf16) to o (bf16) and the final states (fp32).  Inputs
+are synthetic (seeded generators, the workload's shapes and distributions) and resident in HBM
+before the timed region starts.
 
-Prints ONE JSON line.  ``value`` is prefill tokens/s (B*T tokens per step / step time).
-``roofline`` describes the step's one operation, kda_chunk_fwd_gated (its two kernels: the
-intra-block kernel with the gate fused, and the state-passing kernel, launched back to back on
-one stream), with its algorithmic bytes per call divided by its mean call time: HIP events on
-the launch stream around the timed region's K steps.
-``cpu_baseline`` is the fp64 oracle (test infrastructure) timed on this host's cores on the same
-workload.
+The other workloads are timed in the same run, each with its own roofline: the bf16 prefill
+workload (B=4, H=16, T=4096) under "prefill_bf16" (with the separate kda_gate + kda_chunk_fwd
+pair under "unfused"), the long workload (1 x 65536 tokens, 32 heads) under "long_prefill", the
+decode workload (256 sequences x 32 heads, 64 in-place steps, plus speculative-decode verify and
+commit) under "decode".
+
+Prints ONE JSON line.  ``value`` is prefill tokens/s (tokens per step / wall-clock step time
+over exactly K steps).  ``roofline`` describes the step's one operation, kda_chunk_fwd_gated
+(its kernels launched back to back on one stream), with its algorithmic bytes per call divided
+by its mean call time: HIP events on the launch stream around the timed region's K steps.
+``cpu_baseline`` is the fp64 oracle (test infrastructure) timed on this host's cores on the
+whole headline workload.
 """
 from __future__ import annotations
 
@@ -54,16 +56,16 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the long-sequence prefill leg")
-    ap.add_argument("--no-packed", action="store_true", help="skip the packed-batch prefill leg")
     ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--mode", choices=("all", "prefill", "decode", "packed"), default="all",
-                    help="prefill / decode: run only that workload and print no JSON line "
-                         "(for profiler counter passes)")
+    ap.add_argument("--mode", choices=("all", "packed", "prefill", "long", "decode"),
+                    default="all",
+                    help="packed (the headline workload) / prefill / long / decode: run only that "
+                         "workload and print no JSON line (for profiler passes)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first copy this many MiB device-to-device (a plain copy kernel of known "
                          "size, the calibration for HBM byte counters)")
@@ -93,6 +95,27 @@ def measured_traffic(summary: str, digest: str):
     if rec.get("source_sha256") != digest:
         return None
     return int(rec["hbm_bytes_per_launch"])
+
+
+def mfma_executed(summary: str, call_ms: float):
+    """Executed MFMA work per call from a committed counter summary (SQ_INSTS_VALU_MFMA_MOPS_*
+    counters, 512 FLOP per unit), over the call time measured now; None when the summary is
+    missing or was taken with other kernel sources."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"<!-- mfma (\{.*?\}) -->", open(path).read())
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256") != source_digest("kda_chunk.hip", "kda_common.hpp",
+                                                 "kda_internal.hpp"):
+        return None
+    flop = float(rec["flop_per_call"])
+    return {"flop_per_call": flop, "tflops": round(flop / (call_ms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(flop / (call_ms * 1e-3) / BF16_PEAK, 4),
+            "by_type": rec.get("by_type"),
+            "note": "counter-measured MFMA work (fp32 and fp16 MFMAs together) over the call time"}
 
 
 def log(*a):
@@ -195,83 +218,125 @@ def run_decode(args, dev, inputs, K, stream):
                       "bf16 q/k/v/beta/g, 64 steps"}
 
 
-def run_long(args, dev, inputs, K, stream):
-    """The long workload: 1 sequence x 65536 tokens, 32 heads, z ~ N(0, 2^2).  With few
-    (sequence, head) units the library cuts the sequence into 8192-token segments (pass 1, the
-    scan of segment pairs, pass 2).  kda_chunk_fwd_gated, timed with HIP events over 5 calls."""
-    cfg = inputs.config("prefill_long")
+def _median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def load_prefill(name, inputs, dev, keep_host=False):
+    """Device copies of a prefill workload's inputs (and, when asked, the host tensors)."""
+    cfg = inputs.config(name)
     log("generating", cfg)
     d = inputs.make_prefill(cfg)
-    q, k, v, beta, z = (d[x].to(dev) for x in ("q", "k", "v", "beta", "z"))
-    A, S0 = d["A"].to(dev), d["S0"].to(dev)
-    del d
-    B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
-    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
-    hT = torch.empty_like(S0)
-    ws = torch.empty(K.kda_chunk_fwd_workspace_size(B, B * T, H, dk, dv), dtype=torch.uint8,
-                     device=dev)
+    w = {x: d[x].to(dev) for x in ("q", "k", "v", "beta", "z", "A", "S0")}
+    w["cu"] = d["cu_seqlens"].to(dev) if d["cu_seqlens"] is not None else None
+    w["lens"] = d["cu_seqlens"].diff().tolist() if d["cu_seqlens"] is not None else [d["T"]] * d["B"]
+    w["cfg"], w["B"], w["T"], w["N"] = cfg, d["B"], d["T"], d["N"]
+    return w, (d if keep_host else None)
 
+
+def gated_call(K, w, stream, o, hT, ws):
     def call():
-        K.kda_chunk_fwd_gated(q, k, v, beta, A, z, initial_state=S0, final_state=hT, o=o,
+        K.kda_chunk_fwd_gated(w["q"], w["k"], w["v"], w["beta"], w["A"], w["z"],
+                              initial_state=w["S0"], final_state=hT, cu_seqlens=w["cu"], o=o,
                               workspace=ws, stream=stream)
-
-    call()
-    torch.cuda.synchronize()
-    reps = 5
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        call()
-    e1.record(stream)
-    e1.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    alg = B * T * H * FUSED_BYTES_PER_TH + H * dk * 4 + 2 * B * H * dk * dv * 4
-    return {"config": "1 x 65536 tokens, 32 heads, d_k=d_v=128, bf16, gate fused; "
-                      "split into 8192-token segments",
-            "ms_per_call": round(ms, 4),
-            "tokens_per_s": round(B * T / (ms * 1e-3), 1),
-            "algorithmic_gbs": round(alg / (ms * 1e-3) / 1e9, 1),
-            "frac_hbm": round(alg / (ms * 1e-3) / HBM_PEAK, 4)}
+    return call
 
 
-def run_packed(args, dev, inputs, K, stream, reps=5):
-    """The packed workload: 8 sequences of seeded log-uniform lengths summing to 2^20 tokens, 8
-    heads, per-sequence initial states, packed with cu_seqlens (every sequence runs in 8192-token
-    segments).  kda_chunk_fwd_gated, timed with HIP events over `reps` calls."""
-    cfg = inputs.config("prefill_varlen")
-    log("generating", cfg)
-    d = inputs.make_prefill(cfg)
-    q, k, v, beta, z = (d[x].to(dev) for x in ("q", "k", "v", "beta", "z"))
-    A, S0, cu = d["A"].to(dev), d["S0"].to(dev), d["cu_seqlens"].to(dev)
-    lens = d["cu_seqlens"].diff().tolist()
-    del d
-    T, H, dk, dv = q.shape[1], cfg.H, cfg.dk, cfg.dv
-    N = len(lens)
-    o = torch.empty((1, T, H, dv), dtype=torch.bfloat16, device=dev)
-    hT = torch.empty_like(S0)
-    ws = torch.empty(K.kda_chunk_fwd_workspace_size(N, T, H, dk, dv), dtype=torch.uint8,
+def prefill_buffers(K, w, dev):
+    cfg = w["cfg"]
+    B, T, H, dk, dv = w["B"], w["T"], cfg.H, cfg.dk, cfg.dv
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty_like(w["S0"])
+    ws = torch.empty(K.kda_chunk_fwd_workspace_size(w["N"], B * T, H, dk, dv), dtype=torch.uint8,
                      device=dev)
+    return o, hT, ws
 
-    def call():
-        K.kda_chunk_fwd_gated(q, k, v, beta, A, z, initial_state=S0, final_state=hT,
-                              cu_seqlens=cu, o=o, workspace=ws, stream=stream)
 
+def time_calls(call, stream, reps):
+    """`reps` calls back to back with an event between consecutive calls (HIP events on the
+    launch stream): (mean, median) ms per call."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record(stream)
+    for i in range(reps):
+        call()
+        evs[i + 1].record(stream)
+    evs[-1].synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
+    return evs[0].elapsed_time(evs[-1]) / reps, _median(per)
+
+
+def prefill_alg_bytes(w):
+    cfg = w["cfg"]
+    th = w["B"] * w["T"] * cfg.H
+    return th * FUSED_BYTES_PER_TH + cfg.H * cfg.dk * 4 + 2 * w["N"] * cfg.H * STATE_BYTES
+
+
+def prefill_leg(name, K, inputs, dev, stream, reps, traffic_summary=None, label=""):
+    """A prefill workload other than the headline one: kda_chunk_fwd_gated timed with HIP events
+    over `reps` calls after one untimed call; its own HBM roofline."""
+    w, _ = load_prefill(name, inputs, dev)
+    o, hT, ws = prefill_buffers(K, w, dev)
+    call = gated_call(K, w, stream, o, hT, ws)
     call()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        call()
-    e1.record(stream)
-    e1.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    alg = T * H * FUSED_BYTES_PER_TH + H * dk * 4 + 2 * N * H * dk * dv * 4
-    return {"config": f"{N} packed sequences (lengths {', '.join(str(x) for x in lens)}), "
-                      f"{T} tokens, {H} heads, d_k=d_v={dk}, bf16, gate fused",
-            "ms_per_call": round(ms, 4),
-            "tokens_per_s": round(T / (ms * 1e-3), 1),
-            "algorithmic_gbs": round(alg / (ms * 1e-3) / 1e9, 1),
-            "frac_hbm": round(alg / (ms * 1e-3) / HBM_PEAK, 4)}
+    mean, med = time_calls(call, stream, reps)
+    alg = prefill_alg_bytes(w)
+    cfg = w["cfg"]
+    tokens = w["B"] * w["T"]
+    th = tokens * cfg.H
+    out = {"config": label,
+           "ms_per_call": round(mean, 4), "ms_per_call_median": round(med, 4),
+           "tokens_per_s": round(tokens / (mean * 1e-3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(alg / (mean * 1e-3) / 1e9, 1),
+                        "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                        "frac": round(alg / (mean * 1e-3) / HBM_PEAK, 4),
+                        "traffic": measured_traffic(traffic_summary, chunk_digest())
+                        if traffic_summary else None,
+                        "bytes_per_launch": alg},
+           "mfma": {"canonical_tflops": round(th * PREFILL_FLOP_PER_TH / (mean * 1e-3) / 1e12, 2),
+                    "frac_bf16_peak": round(th * PREFILL_FLOP_PER_TH / (mean * 1e-3) / BF16_PEAK, 4)}}
+    return out, (w, o, hT, ws)
+
+
+def chunk_digest():
+    return source_digest("kda_chunk.hip", "kda_common.hpp", "kda_internal.hpp")
+
+
+def cpu_baseline(args, d, lens):
+    """The fp64 oracle (gate + token loop) on the whole headline workload on this host's cores,
+    plus one thread on two (sequence, head) units of the bf16 prefill workload."""
+    import oracle
+    from gated_delta_rule_60_amd import inputs
+    log("oracle baseline on host cores (whole headline workload)")
+    t1 = time.perf_counter()
+    g64 = oracle.gate(d["A"], d["z"])
+    _, _, used = oracle.forward(d["q"], d["k"], d["v"], d["beta"], g64, S0=d["S0"],
+                                cu_seqlens=d["cu_seqlens"].numpy(), nthreads=args.cpu_threads,
+                                want_o=True)
+    cpu_s = time.perf_counter() - t1
+    del g64
+    tokens = int(sum(lens))
+    # one thread, one unit at a time: the per-token rate that bounds the longest sequence
+    c1 = inputs.config("prefill_bf16")
+    s = inputs.make_prefill(inputs.config("prefill_bf16", B=1, H=2))
+    g1 = oracle.gate(s["A"], s["z"])
+    t2 = time.perf_counter()
+    oracle.forward(s["q"], s["k"], s["v"], s["beta"], g1, S0=s["S0"], nthreads=1)
+    one_s = time.perf_counter() - t2
+    per_th = one_s / (c1.T * 2)                  # seconds per token-head on one thread
+    return {"value": round(tokens / cpu_s, 1), "unit": "tokens/s", "cores": int(used),
+            "nproc": os.cpu_count(), "kind": "oracle",
+            "sample": f"the whole headline workload ({tokens} tokens x 8 heads: gate + fp64 token "
+                      f"loop, OpenMP over the 64 (sequence, head) units), {cpu_s:.1f} s",
+            "seconds": round(cpu_s, 2),
+            "single_thread": {"tokens_per_s_per_head": round(1.0 / per_th, 1),
+                              "sample": "one thread, 2 units of 4096 tokens of the bf16 "
+                                        f"prefill workload, {one_s:.2f} s"},
+            "critical_path_s": round(max(lens) * per_th, 2),
+            "critical_path_note": "the longest sequence's one unit at the single-thread rate: "
+                                  "no thread count makes the oracle faster than this"}
 
 
 def main():
@@ -288,6 +353,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     K.load_library()
+    stream = torch.cuda.current_stream()
 
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
@@ -298,103 +364,94 @@ def main():
         del src, dst
 
     if args.mode == "decode":
-        r = run_decode(args, dev, inputs, K, torch.cuda.current_stream())
+        r = run_decode(args, dev, inputs, K, stream)
         log(f"decode: {r['ms_per_step']:.4f} ms/step; spec decode {r['spec_decode']}")
         return
-    if args.mode == "packed":
-        r = run_packed(args, dev, inputs, K, torch.cuda.current_stream(), reps=args.steps)
-        log(f"packed prefill: {r['ms_per_call']:.4f} ms/call, {r['tokens_per_s']:.0f} tokens/s")
+    if args.mode in ("prefill", "long"):
+        name = "prefill_bf16" if args.mode == "prefill" else "prefill_long"
+        r, _ = prefill_leg(name, K, inputs, dev, stream, args.steps)
+        log(f"{name}: {r['ms_per_call']:.4f} ms/call (median {r['ms_per_call_median']:.4f})")
         return
 
-    # ------------------------------------------------------------------ prefill workload
-    cfg = inputs.config("prefill_bf16")
-    log("generating", cfg)
-    d = inputs.make_prefill(cfg)
-    B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
-    q, k, v, beta, z = (d[x].to(dev) for x in ("q", "k", "v", "beta", "z"))
-    A, S0 = d["A"].to(dev), d["S0"].to(dev)
-    g = torch.empty(z.shape, dtype=torch.float32, device=dev)
-    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
-    hT = torch.empty_like(S0)
-    ws = torch.empty(K.kda_chunk_fwd_workspace_size(B, B * T, H, dk, dv, in_dtype=q.dtype),
-                     dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def ev():
-        return torch.cuda.Event(enable_timing=True)
-
-    def fused_step():
-        K.kda_chunk_fwd_gated(q, k, v, beta, A, z, initial_state=S0, final_state=hT, o=o,
-                              workspace=ws, stream=stream)
-
-    def unfused_step():
-        K.kda_gate(A, z, g=g, stream=stream)
-        K.kda_chunk_fwd(q, k, v, beta, g, initial_state=S0, final_state=hT, o=o, workspace=ws,
-                        stream=stream)
-
+    # ------------------------------------------------------------------ headline: packed workload
+    w, host = load_prefill("prefill_varlen", inputs, dev,
+                           keep_host=(args.mode == "all" and not args.no_cpu_baseline))
+    cfg = w["cfg"]
+    o, hT, ws = prefill_buffers(K, w, dev)
+    step = gated_call(K, w, stream, o, hT, ws)
     for _ in range(args.warmup):
-        fused_step()
-        unfused_step()
+        step()
     torch.cuda.synchronize()
     # exactly K steps: wall clock, and HIP events on the launch stream around the same region
-    e_beg, e_end = ev(), ev()
+    e_beg, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e_beg.record(stream)
     for _ in range(args.steps):
-        fused_step()
+        step()
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    fused_ms = [e_beg.elapsed_time(e_end) / args.steps]
-    # the unfused pair for reference: K pairs back to back, events between the calls
-    evs = [ev() for _ in range(2 * args.steps + 1)]
-    evs[0].record(stream)
-    for i in range(args.steps):
-        K.kda_gate(A, z, g=g, stream=stream)
-        evs[2 * i + 1].record(stream)
-        K.kda_chunk_fwd(q, k, v, beta, g, initial_state=S0, final_state=hT, o=o, workspace=ws,
-                        stream=stream)
-        evs[2 * i + 2].record(stream)
-    torch.cuda.synchronize()
-    gate_ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)]
-    chunk_ms = [evs[2 * i + 1].elapsed_time(evs[2 * i + 2]) for i in range(args.steps)]
-    fused_avg = sum(fused_ms) / len(fused_ms)
-    chunk_avg = sum(chunk_ms) / len(chunk_ms)
-    gate_avg = sum(gate_ms) / len(gate_ms)
-    if args.mode == "prefill":
-        log(f"prefill: {ms_per_step:.4f} ms/step, kda_chunk_fwd_gated {fused_avg:.4f} ms, "
-            f"kda_gate {gate_avg:.4f} ms + kda_chunk_fwd {chunk_avg:.4f} ms")
+    call_ms = e_beg.elapsed_time(e_end) / args.steps
+    # per-call spread: the same K calls again with an event between consecutive calls
+    _, call_med = time_calls(step, stream, max(args.steps, 20))
+    if args.mode == "packed":
+        log(f"packed prefill: {ms_per_step:.4f} ms/step, events {call_ms:.4f} ms/call "
+            f"(median {call_med:.4f})")
         return
 
-    tokens = B * T
+    lens = w["lens"]
+    T, H, dk = w["T"], cfg.H, cfg.dk
+    tokens = T
     th = tokens * H
-    state_io = 2 * B * H * STATE_BYTES
-    fused_bytes = th * FUSED_BYTES_PER_TH + H * dk * 4 + state_io
-    chunk_bytes = th * PREFILL_BYTES_PER_TH + state_io
-    chunk_flop = th * PREFILL_FLOP_PER_TH
-    achieved = fused_bytes / (fused_avg * 1e-3)
+    alg = prefill_alg_bytes(w)
+    achieved = alg / (call_ms * 1e-3)
+    flop = th * PREFILL_FLOP_PER_TH
     value = tokens / (ms_per_step * 1e-3)
+    del o, hT, ws, w, step
+    torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------------ other workloads
+    leg1, (w1, o1, h1, ws1) = prefill_leg(
+        "prefill_bf16", K, inputs, dev, stream, max(args.steps, 20),
+        traffic_summary="chunk_fwd_gated_prefill_bf16_B4_H16_T4096.md",
+        label="B=4 H=16 T=4096 d_k=d_v=128, bf16, random initial states, gate fused")
+    g1 = torch.empty(w1["z"].shape, dtype=torch.float32, device=dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    K.kda_gate(w1["A"], w1["z"], g=g1, stream=stream)
+    torch.cuda.synchronize()
+    reps = max(args.steps, 20)
+    evs[0].record(stream)
+    for _ in range(reps):
+        K.kda_gate(w1["A"], w1["z"], g=g1, stream=stream)
+    evs[1].record(stream)
+    for _ in range(reps):
+        K.kda_chunk_fwd(w1["q"], w1["k"], w1["v"], w1["beta"], g1, initial_state=w1["S0"],
+                        final_state=h1, o=o1, workspace=ws1, stream=stream)
+    evs[2].record(stream)
+    evs[2].synchronize()
+    gate_ms, chunk_ms = evs[0].elapsed_time(evs[1]) / reps, evs[1].elapsed_time(evs[2]) / reps
+    th1 = w1["B"] * w1["T"] * w1["cfg"].H
+    chunk_bytes = th1 * PREFILL_BYTES_PER_TH + 2 * w1["N"] * w1["cfg"].H * STATE_BYTES
+    leg1["unfused"] = {"kda_gate_ms": round(gate_ms, 4), "kda_chunk_fwd_ms": round(chunk_ms, 4),
+                       "kda_chunk_fwd_bytes": chunk_bytes,
+                       "kda_chunk_fwd_frac_hbm": round(chunk_bytes / (chunk_ms * 1e-3) / HBM_PEAK, 4),
+                       "tokens_per_s": round(w1["B"] * w1["T"] / ((gate_ms + chunk_ms) * 1e-3), 1)}
+    del w1, o1, h1, ws1, g1
+    torch.cuda.empty_cache()
+    long_ = None
+    if not args.no_long:
+        long_, bufs = prefill_leg("prefill_long", K, inputs, dev, stream, max(args.steps, 20),
+                                  traffic_summary="chunk_fwd_gated_long_B1_H32_T65536.md",
+                                  label="1 x 65536 tokens, 32 heads, d_k=d_v=128, bf16, "
+                                        "z ~ N(0, 2^2), gate fused")
+        del bufs
+        torch.cuda.empty_cache()
     dec = run_decode(args, dev, inputs, K, stream)
-    long_ = None if args.no_long else run_long(args, dev, inputs, K, stream)
-    packed = None if args.no_packed else run_packed(args, dev, inputs, K, stream)
     copy_bps = copy_ceiling(dev, stream)
     dec["roofline"]["frac_of_copy"] = round(dec["roofline"]["achieved"] * 1e9 / copy_bps, 4)
 
-    # ------------------------------------------------------------------ CPU baseline (oracle)
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        log("oracle baseline on host cores")
-        t1 = time.perf_counter()
-        g64 = oracle.gate(d["A"], d["z"])
-        _, _, used = oracle.forward(d["q"], d["k"], d["v"], d["beta"], g64, S0=d["S0"],
-                                    nthreads=args.cpu_threads, want_o=True)
-        cpu_s = time.perf_counter() - t1
-        cpu = {"value": round(tokens / cpu_s, 1), "unit": "tokens/s", "cores": int(used),
-               "kind": "oracle",
-               "sample": f"the whole prefill workload (gate + token loop, fp64), {cpu_s:.1f} s"}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, host, lens)
 
     out = {
         "metric": "KDA prefill tokens/s (% bf16 MFMA peak) + decode state GB/s (% HBM peak)",
@@ -409,29 +466,26 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "KDA chunked prefill, bf16 inputs / fp32 state, B=4 H=16 T=4096 "
-                               "d_k=d_v=128 chunk=64, gate fused (A, z in)",
-                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": dk,
-                   "parallelism": "single GPU"},
+        "config": {"workload": "KDA variable-length packed prefill, bf16 inputs / fp32 state: "
+                               f"{len(lens)} sequences (lengths {', '.join(str(x) for x in lens)}), "
+                               f"{tokens} tokens, H={H}, d_k=d_v={dk}, chunk=64, per-sequence "
+                               "initial states, cu_seqlens, gate fused (A, z in)",
+                   "global_batch": len(lens), "seq_len": max(lens), "total_tokens": tokens,
+                   "heads": H, "head_dim": dk, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4),
-                     "traffic": measured_traffic(
-                         "chunk_fwd_gated_prefill_bf16_B4_H16_T4096.md",
-                         source_digest("kda_chunk.hip", "kda_common.hpp", "kda_internal.hpp")),
-                     "kernel": "kda_chunk_fwd_gated = chunk_intra_tok_kernel (gate fused) + "
-                               "chunk_state_kernel",
-                     "kernel_ms": round(fused_avg, 4), "bytes_per_launch": fused_bytes,
-                     "workspace_bytes": ws.numel()},
-        "mfma": {"canonical_tflops": round(chunk_flop / (fused_avg * 1e-3) / 1e12, 2),
-                 "frac_bf16_peak": round(chunk_flop / (fused_avg * 1e-3) / BF16_PEAK, 4)},
-        "unfused": {"kda_gate_ms": round(gate_avg, 4), "kda_chunk_fwd_ms": round(chunk_avg, 4),
-                    "kda_chunk_fwd_bytes": chunk_bytes,
-                    "kda_chunk_fwd_frac_hbm": round(chunk_bytes / (chunk_avg * 1e-3) / HBM_PEAK, 4),
-                    "tokens_per_s": round(tokens / ((gate_avg + chunk_avg) * 1e-3), 1)},
-        "decode": dec,
+                     "traffic": measured_traffic("chunk_fwd_gated_varlen_8seq_1M_H8.md",
+                                                 chunk_digest()),
+                     "kernel": "kda_chunk_fwd_gated (the call's kernels back to back)",
+                     "kernel_ms": round(call_ms, 4), "kernel_ms_median": round(call_med, 4),
+                     "bytes_per_launch": alg},
+        "mfma": {"canonical_tflops": round(flop / (call_ms * 1e-3) / 1e12, 2),
+                 "frac_bf16_peak": round(flop / (call_ms * 1e-3) / BF16_PEAK, 4),
+                 "executed": mfma_executed("chunk_fwd_gated_varlen_8seq_1M_H8.md", call_ms)},
+        "prefill_bf16": leg1,
         "long_prefill": long_,
-        "packed_prefill": packed,
+        "decode": dec,
         "copy_ceiling_gbs": round(copy_bps / 1e9, 1),
         "cpu_baseline": cpu,
     }
