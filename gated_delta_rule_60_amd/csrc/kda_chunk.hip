@@ -46,21 +46,10 @@
 // For fp32 inputs every product is split bf16 (hi*hi + hi*lo + lo*hi).
 #include <type_traits>
 
-#include "kda_common.hpp"
-#include "kda_internal.hpp"
+#include "kda_chunk_util.hpp"
 
 namespace kda {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BLK = 16;     // tokens per block (one state step)
 // Waves per state-kernel workgroup, 16 state columns each: 2 in the whole-sequence pass (more
@@ -69,61 +58,6 @@ constexpr int BLK = 16;     // tokens per block (one state step)
 constexpr int STATE_WAVES = 2;
 constexpr int SEG_WAVES = 4;
 constexpr int STATE_SLICES = 2;  // slices a chunk's transfers are issued in (at most NB - 1)
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// s_waitcnt immediate for "vmcnt <= n", other counters unconstrained.
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-
-// Buffer resource over [base, base + bytes): raw (unswizzled, stride 0) accesses whose byte offset
-// lies outside the range read 0 and write nothing, so loads and stores need no branches and the
-// compiler can count outstanding memory operations exactly.  Word 3 selects 32-bit data format.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr int CP_NT = 2;   // buffer cache policy: non-temporal (data used once)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                             static_cast<int>(bytes), 0x00020000);
-}
-
-// 2^x with one v_exp_f32.  Every factor formed here lies in [2^-116, 2^116] (a 16-token span
-// decays by at most e^-80), so the instruction's denormal flush never applies.
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ uint16_t bf16_bits(float x) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
-__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
-
-// Two fp32 values -> packed bf16 hi word and packed bf16 lo word (x = hi + lo to ~16 bits).
-__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
-    const float r0 = x0 - __uint_as_float(hi << 16);
-    const float r1 = x1 - __uint_as_float(hi & 0xffff0000u);
-    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
-}
-// Staged tiles are written as 16-bit (or fp32) elements and read back as whole 16-byte units
-// through may_alias types, which makes these type-punned reads well defined.
-typedef uint4 __attribute__((may_alias)) uint4_ma;
-typedef float4 __attribute__((may_alias)) float4_ma;
-__device__ __forceinline__ uint32_t f16_pair(float x0, float x1) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, f16x2));
-}
-__device__ __forceinline__ void split4(const f32x4& x, s16x4& hi, s16x4& lo) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint16_t h = bf16_bits(x[i]);
-        hi[i] = static_cast<short>(h);
-        lo[i] = static_cast<short>(bf16_bits(x[i] - bf16_val(h)));
-    }
-}
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const __bf16 hb = static_cast<__bf16>(x[i]);
-        hi[i] = hb;
-        lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(hb));
-    }
-}
 
 // ---- MFMA wrappers (operands already in their 16-bit format) --------------------------------
 __device__ __forceinline__ f32x4 mfma32_bf16_x3(const bf16x8& ah, const bf16x8& al,
@@ -149,32 +83,11 @@ constexpr int QP_PREV1 = 0 | (0 << 2) | (1 << 4) | (2 << 6);   // [0,0,1,2]
 constexpr int QP_PREV2 = 0 | (0 << 2) | (0 << 4) | (1 << 6);   // [0,0,0,1]
 constexpr int QP_LAST = 3 | (3 << 2) | (3 << 4) | (3 << 6);    // [3,3,3,3]
 
-// ---- layouts ---------------------------------------------------------------------------------
-// [16][DK] 16-bit arrays (token-major): 16-byte units of 8 channels, unit index XOR (row & 7)
-// so that the 16 rows of an MFMA fragment read fall in different banks.
-template <int DK>
-__device__ __forceinline__ int tok_major(int r, int c) {
-    return r * DK + ((((c >> 3) ^ (r & 7))) << 3) + (c & 7);
-}
-// Record arrays are stored in MFMA fragment order, so that the state pass reads each operand
-// with one contiguous 16- or 8-byte load per lane (1 KB / 512 B per wave, no bank conflicts):
-//   frag32: [16][DK] operand of a 16x16x32 product (row = token, K = channel): fragment kk,
-//           lane (m, q) holds channels 32kk + 4q + {0..3} in slots 0..3 and 32kk + 16 + 4q + {0..3}
-//           in slots 4..7 -- the K order in which the state tiles are packed as the B operand.
-//   frag16: [DK][16] operand of a 16x16x16 product (row = channel, K = token): tile i, lane
-//           (m, q) holds channel 16i + m, tokens 4q .. 4q + 3.
-//   fragT : [16][16] operand of a 16x16x16 product: lane (m, q) holds row m, columns 4q .. 4q + 3.
-__device__ __forceinline__ int frag32(int r, int c) {
-    return ((c >> 5) * 64 + r + 16 * ((c & 15) >> 2)) * 8 + ((c & 16) >> 2) + (c & 3);
-}
-__device__ __forceinline__ int frag16(int c, int t) { return ((c >> 4) * 64 + (c & 15) + 16 * (t >> 2)) * 4 + (t & 3); }
-__device__ __forceinline__ int fragT(int r, int s) { return (r + 16 * (s >> 2)) * 4 + (s & 3); }
-
 // Record of one (head, block slot) in the workspace (byte offsets).  E = 16 * DK elements per
 // array.  A fast record covers 32 tokens: two 16-token sub-blocks, one 32-token state step; a
 // precise record covers one 16-token block.
 //   fast   : per sub-block s = 0, 1: [Kt fp16 frag32][Qt fp16 frag32][Kb^T fp16 frag16]; then
-//            T'_00, T'_10, T'_11 and P_00, P_10, P_11 (fp16 fragT, [row sub-block][column
+//            T'_00, -C, T'_11 and P_00, P_10, P_11 (fp16 fragT, [row sub-block][column
 //            sub-block]); then e^{G_31} - 1 (DK fp32).  Kt, Qt are scaled from the record's first
 //            token, Kb from its last, so every exponent is <= 0.
 //   precise: [Kt hi][Kt lo][Qt hi][Qt lo] (bf16 frag32) [Kb^T hi][Kb^T lo] (bf16 frag16), then T'
@@ -246,20 +159,6 @@ template <int NP>
 __device__ __forceinline__ void store_words(void* dst, const uint32_t (&w)[NP]) {
     if constexpr (NP == 4) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     else *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-}
-
-// Token range [bos, end) of sequence n of a packed batch (B = 1, T tokens in all).  The offsets
-// are clamped so that 0 <= bos <= end <= T whatever cu_seqlens holds: with malformed offsets
-// (negative, past T, decreasing) results are unspecified, but every slot base and buffer range
-// derived from bos and end stays inside the buffers sized for T tokens.
-__device__ __forceinline__ int64_t seq_start(const ChunkArgs& p, int n) {
-    const int64_t a = p.cu[n];
-    return a < 0 ? 0 : a > p.T ? p.T : a;
-}
-__device__ __forceinline__ void seq_bounds(const ChunkArgs& p, int n, int64_t& bos, int64_t& end) {
-    bos = seq_start(p, n);
-    const int64_t b = p.cu[n + 1];
-    end = b < bos ? bos : b > p.T ? p.T : b;
 }
 
 // Locate the record slot of a workgroup: sequence n, record j inside it (TOK tokens each), or
@@ -574,11 +473,6 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
         *reinterpret_cast<uint4*>(rec + R::OFF_T + 16 * j) = *reinterpret_cast<const uint4_ma*>(stg + 16 * j);
 }
 
-// LDS ordering inside a one-wave workgroup: a wave's LDS operations execute in order, so only the
-// compiler must keep them in place.  A wavefront-scope fence does that and emits no wait (a
-// workgroup barrier's fence would also wait for every transfer in flight).
-__device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
-
 // ============================================================================================
 // 1b. intra-block kernel for 16-bit inputs: one wave per (32-token record slot, head)
 // ============================================================================================
@@ -592,8 +486,9 @@ __device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_S
 //   * the cross-sub-block terms use factors <= 1 only: with Kb_0 = e^{G_15 - G} K of sub-block 0,
 //     C = Kt_1 Kb_0^T gives A_10 = Diag(beta_1) C and P_10 = Qt_1 Kb_0^T, on fp16 16x16x32
 //     MFMAs (fp16 operands, as the state pass uses them);
-//   * T' of the record is block lower-triangular: T'_00 and T'_11 by forward substitution, and
-//     T'_10 = -T'_11 C T'_00, the lower-left block of the inverse;
+//   * T' of the record is block lower-triangular: T'_00 and T'_11 by forward substitution; its
+//     lower-left block T'_10 = -T'_11 C T'_00 is never formed -- the record keeps -C and the state
+//     pass applies it as W_1 = T'_11 (X_1 - C W_0);
 //   * the record's Kt_1 and Qt_1 are scaled by sub-block 0's e^{G_15} (from the record's first
 //     token) and its Kb_0 by sub-block 1's (to the record's last token).
 // Kt and Qt leave as whole 1 KB wave stores from registers; Kb^T (channel-major) goes through LDS.
@@ -623,14 +518,11 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     __shared__ __attribute__((aligned(16))) uint16_t sKb[2][BLK * 32];  // Kb^T of one group, frag16
     __shared__ __attribute__((aligned(16))) float sRate[GATE ? DK : 4];
     __shared__ float sBeta[TOKR];
-    // After the last group the input tiles are dead and hold: A_00, A_11, C, T'_00 and T'_11 in
-    // fp32 (for the cross product), the product C T'_00, then the staged T' and P tiles (fp16).
-    constexpr int O_C = 2048, O_TF = 3072, O_U = 5120, O_TAIL = 6144;
+    // After the last group the input tiles are dead and hold A_00, A_11 in fp32 (for the
+    // substitutions), then the staged T' / -C and P tiles (fp16).
+    constexpr int O_TAIL = 2048;
     static_assert(O_TAIL + TAIL <= PB, "staging fits the input tiles");
     float (*const sA)[16][16] = reinterpret_cast<float (*)[16][16]>(sIn);
-    float (*const sC)[16] = reinterpret_cast<float (*)[16]>(sIn + O_C);
-    float (*const sTf)[16][16] = reinterpret_cast<float (*)[16][16]>(sIn + O_TF);
-    float (*const sU)[16] = reinterpret_cast<float (*)[16]>(sIn + O_U);
     uint8_t* const sTail = sIn + O_TAIL;
 
     const int lane = threadIdx.x;
@@ -864,9 +756,8 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
         }
     }
 
-    // ---- A_00, A_11 and C to LDS (for the substitutions and the cross product); P staged in
-    // fp16.  Lane (m, q) holds rows 4q + i of column m.  Staged tiles: T'_00, T'_10, T'_11, then
-    // P_00, P_10, P_11.
+    // ---- A_00, A_11 to LDS (for the substitutions); -C and P staged in fp16.  Lane (m, q) holds
+    // rows 4q + i of column m.  Staged tiles: T'_00, -C, T'_11, then P_00, P_10, P_11.
     uint16_t* const tT = reinterpret_cast<uint16_t*>(sTail);
     uint16_t* const tP = reinterpret_cast<uint16_t*>(sTail + (R::OFF_P - R::OFF_T));
 #pragma unroll
@@ -874,7 +765,7 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
         const int r = 4 * q + i, sc = m;
         sA[0][r][sc] = (sc < r) ? accA[0][i] * sBeta[r] : 0.f;
         sA[1][r][sc] = (sc < r) ? accA[1][i] * sBeta[16 + r] : 0.f;
-        sC[r][sc] = accC[i];
+        tT[256 + fragT(r, sc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(-accC[i]));
         tP[fragT(r, sc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>((sc <= r) ? accP[0][i] : 0.f));
         tP[256 + fragT(r, sc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(accQ[i]));
         tP[512 + fragT(r, sc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>((sc <= r) ? accP[1][i] : 0.f));
@@ -911,31 +802,10 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
         }
         const float bj = sBeta[16 * sb + jc];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float v = t[r] * bj;
-            sTf[sb][r][jc] = v;
-            tT[512 * sb + fragT(r, jc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
-        }
+        for (int r = 0; r < 16; ++r)
+            tT[512 * sb + fragT(r, jc)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(t[r] * bj));
     }
-    wave_fence();   // T'_00 and T'_11 are read across lanes below
-
-    // ---- T'_10 = -T'_11 (C T'_00): fp32 16x16x4 MFMAs, lane (i, k) supplying row i, column
-    // 4 st + k of the left operand and lane (j, k) row 4 st + k, column j of the right one
-    f32x4 U = zero4();
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-        U = __builtin_amdgcn_mfma_f32_16x16x4f32(sC[m][4 * st + q], sTf[0][4 * st + q][m], U, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sU[4 * q + i][m] = U[i];
-    wave_fence();
-    f32x4 T10 = zero4();
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-        T10 = __builtin_amdgcn_mfma_f32_16x16x4f32(sTf[1][m][4 * st + q], sU[4 * st + q][m], T10, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        tT[256 + fragT(4 * q + i, m)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(-T10[i]));
-    wave_fence();   // T' and P staged
+    wave_fence();   // T', -C and P staged
     for (int u = lane; u < TAIL / 16; u += 64)
         *reinterpret_cast<uint4*>(rec + R::OFF_T + 16 * u) = *reinterpret_cast<const uint4_ma*>(sTail + 16 * u);
 }
@@ -944,51 +814,9 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
 // 2. state-passing kernel: one workgroup of NW waves per (sequence, head, 16 NW state columns)
 // ============================================================================================
 
-// ---- segments of long sequences ---------------------------------------------------------------
-// A sequence longer than SEG_TOK tokens is cut into segments of SEG_TOK tokens [bagrov § Уровень
-// графического ускорителя: the long-context scheduler].  The state after a segment is an affine
-// map of the state before it, S_out = M S_in + B (M: d_k x d_k, B: d_k x d_v), so:
-//   pass 1: segment 0 runs from the initial state (output included) and every middle segment
-//           computes its pair (M, B) -- the same state recurrence on columns started at the
-//           identity with V = 0, and on columns started at zero -- all segments in parallel;
-//   scan  : S_start(s + 1) = M_s S_start(s) + B_s along each sequence (column blocks apart);
-//   pass 2: every later segment runs from its start state, output included.
-// Segment slots: n * max(1, ceil(T / SEG_TOK)) for fixed-length batches, floor(cu[n] / SEG_TOK) + n
-// for packed ones; per (slot, head) the workspace holds S_start, M and B in fp32.
-constexpr int64_t SEG_TOK = 8192;
-
-struct SegArgs {
-    float* S;            // [slots, H, d_k, d_v] segment start states
-    float* M;            // [slots, H, d_k, d_k]
-    float* B;            // [slots, H, d_k, d_v]
-    int64_t slots;
-    int32_t n_vblk_m;    // column blocks of M (d_k columns)
-};
-
-__device__ __forceinline__ int64_t seg_count(int64_t len) {
-    return len <= 0 ? 1 : (len + SEG_TOK - 1) / SEG_TOK;   // an empty sequence still has one
-}
-
-// Segment slot -> sequence n and segment s within it; false for slots no segment maps to.
-__device__ __forceinline__ bool locate_seg(const ChunkArgs& p, int64_t slot, int& n, int64_t& s) {
-    if (p.cu) {
-        int lo = 0, hi = p.n_seqs - 1;
-        while (lo < hi) {                 // largest n with base(n) <= slot
-            const int mid = (lo + hi + 1) >> 1;
-            const int64_t base = seq_start(p, mid) / SEG_TOK + mid;
-            if (base <= slot) lo = mid; else hi = mid - 1;
-        }
-        n = lo;
-        int64_t bos, end;
-        seq_bounds(p, n, bos, end);
-        s = slot - (bos / SEG_TOK + n);
-        return s >= 0 && s < seg_count(end - bos);
-    }
-    const int64_t per = seg_count(p.T);
-    n = static_cast<int>(slot / per);
-    s = slot % per;
-    return n < p.n_seqs;
-}
+// Long sequences in the two-kernel path: segments of 2^SEG_SHIFT tokens (kda_chunk_util.hpp).
+constexpr int SEG_SHIFT = 13;
+constexpr int64_t SEG_TOK = int64_t(1) << SEG_SHIFT;
 
 // MODE 0: whole sequences.  MODE 1: segment pass 1.  MODE 2: segment pass 2.
 template <int DK, int IDT, int ODT, bool PRECISE, int NW, bool CKPT, int MODE>
@@ -1039,7 +867,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     int n = static_cast<int>(unit / H);
     int64_t seg = 0;
     if constexpr (MODE != 0) {
-        if (!locate_seg(p, unit / H, n, seg)) return;
+        if (!locate_seg(p, sg, unit / H, n, seg)) return;
     }
     const int DV = p.dv;
     const int32_t vstride = static_cast<int32_t>(H) * DV;
@@ -1067,8 +895,8 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     int ldst = DV;                                                     // row stride of init / fin
     bool ident = false, use_v = true, emit_o = true;
     if constexpr (MODE != 0) {
-        constexpr int64_t SEGC = SEG_TOK / CHT;
-        const int64_t nseg = seg_count(len), slot = unit / H;
+        const int64_t SEGC = (int64_t(1) << sg.seg_shift) / CHT;
+        const int64_t nseg = seg_count(len, sg.seg_shift), slot = unit / H;
         const int64_t us = slot * H + h;                                // (segment slot, head)
         c_begin = seg * SEGC;
         c_end = c_begin + SEGC < nchunks_all ? c_begin + SEGC : nchunks_all;
@@ -1234,11 +1062,11 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
             for (int i = 0; i < CT; ++i) gm[i] = *reinterpret_cast<const float4*>(gam + 16 * i + 4 * lq);
             if constexpr (!PRECISE) {
                 // ---- one 32-token step: sub-blocks 0 and 1, S taken at the record's first token
-                const uint8_t* tb = rb + R::OFF_T + 8 * lane;   // T'_00, T'_10, T'_11 (fragT)
+                const uint8_t* tb = rb + R::OFF_T + 8 * lane;   // T'_00, -C, T'_11 (fragT)
                 const uint8_t* pb = rb + R::OFF_P + 8 * lane;   // P_00, P_10, P_11
                 const f16x4 t00 = *reinterpret_cast<const f16x4*>(tb);
-                const f16x8 t1x = __builtin_shufflevector(*reinterpret_cast<const f16x4*>(tb + 512),
-                                                          *reinterpret_cast<const f16x4*>(tb + 1024), 0, 1, 2, 3, 4, 5, 6, 7);
+                const f16x4 ncm = *reinterpret_cast<const f16x4*>(tb + 512);
+                const f16x4 t11 = *reinterpret_cast<const f16x4*>(tb + 1024);
                 const f16x4 p00 = *reinterpret_cast<const f16x4*>(pb);
                 const f16x8 p1x = __builtin_shufflevector(*reinterpret_cast<const f16x4*>(pb + 512),
                                                           *reinterpret_cast<const f16x4*>(pb + 1024), 0, 1, 2, 3, 4, 5, 6, 7);
@@ -1257,19 +1085,21 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                     O0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[1][kk], sb, O0, 0, 0, 0);
                     O1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[3][kk], sb, O1, 0, 0, 0);
                 }
-                // X = V - Y (the beta scaling sits in T'); W_0 = T'_00 X_0, W_1 = T'_10 X_0 +
-                // T'_11 X_1 as one K = 32 product: K slots 8k .. 8k + 3 pair with sub-block 0's
-                // tokens 4k .. 4k + 3, slots 8k + 4 .. 8k + 7 with sub-block 1's
+                // X = V - Y (the beta scaling sits in T'); W_0 = T'_00 X_0, X_1' = X_1 - C W_0,
+                // W_1 = T'_11 X_1'
                 const f32x4 X0 = v_minus(Y0, 32 * b), X1 = v_minus(Y1, 32 * b + 16);
-                f16x4 x0, x1;
+                f16x4 x0, x1, w0, w1;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { x0[i] = static_cast<_Float16>(X0[i]); x1[i] = static_cast<_Float16>(X1[i]); }
+                for (int i = 0; i < 4; ++i) x0[i] = static_cast<_Float16>(X0[i]);
                 const f32x4 W0 = __builtin_amdgcn_mfma_f32_16x16x16f16(t00, x0, zero4(), 0, 0, 0);
-                const f32x4 W1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    t1x, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7), zero4(), 0, 0, 0);
-                f16x4 w0, w1;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { w0[i] = static_cast<_Float16>(W0[i]); w1[i] = static_cast<_Float16>(W1[i]); }
+                for (int i = 0; i < 4; ++i) w0[i] = static_cast<_Float16>(W0[i]);
+                const f32x4 X1p = __builtin_amdgcn_mfma_f32_16x16x16f16(ncm, w0, X1, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x1[i] = static_cast<_Float16>(X1p[i]);
+                const f32x4 W1 = __builtin_amdgcn_mfma_f32_16x16x16f16(t11, x1, zero4(), 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w1[i] = static_cast<_Float16>(W1[i]);
                 const f16x8 wx = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
                 // O += P W (P and Qt carry the output scale)
                 O0 = __builtin_amdgcn_mfma_f32_16x16x16f16(p00, w0, O0, 0, 0, 0);
@@ -1396,12 +1226,12 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
         int64_t bos, end;
         seq_bounds(p, n, bos, end);
         len = end - bos;
-        slot0 = bos / SEG_TOK + n;
+        slot0 = (bos >> sg.seg_shift) + n;
     } else {
         len = p.T;
-        slot0 = static_cast<int64_t>(n) * seg_count(p.T);
+        slot0 = static_cast<int64_t>(n) * seg_count(p.T, sg.seg_shift);
     }
-    const int64_t nseg = seg_count(len);
+    const int64_t nseg = seg_count(len, sg.seg_shift);
     if (nseg < 3) return;                             // no middle segment: nothing to combine
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -1522,6 +1352,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     const int64_t nslots = slot_count(a.n_seqs, total, a.cu != nullptr, a.B, a.T, Rec<DK, PRECISE>::TOK);
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
     const int64_t intra_wgs = nslots * a.H;
+    const bool segmented = use_segments(a.n_seqs, total, a.H, a.dv);
     if (intra_wgs > 0) {
         // 16-bit inputs: the token-per-lane kernel; fp32 inputs (split-bf16 records): the
         // split-operand kernel
@@ -1544,7 +1375,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     }
     const int32_t n_vblk = a.dv / (16 * STATE_WAVES);
     SegArgs sg{};
-    if (!use_segments(a.n_seqs, total, a.H, a.dv)) {
+    if (!segmented) {
         launch_state_ck<DK, IDT, ODT, PRECISE, 0>(a, nslots, ws, sg, static_cast<int64_t>(a.n_seqs) * a.H,
                                                   n_vblk, stream);
         return hipGetLastError();
@@ -1556,6 +1387,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     sg.S = reinterpret_cast<float*>(ws + record_area(a.n_seqs, total, a.H, DK, PRECISE));
     sg.B = sg.S + st * a.dv;
     sg.M = sg.B + st * a.dv;
+    sg.seg_shift = SEG_SHIFT;
     sg.slots = a.cu ? seg_slot_bound(a.n_seqs, total)
                     : static_cast<int64_t>(a.B) * (a.T <= 0 ? 1 : (a.T + SEG_TOK - 1) / SEG_TOK);
     const int64_t seg_units = sg.slots * a.H;
@@ -1603,6 +1435,7 @@ hipError_t dispatch(const ChunkArgs& a, hipStream_t s) {
 // for segmented launches, then the segment start states, B and M per (segment slot, head).
 size_t chunk_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
                              int32_t dv, int32_t in_dtype) {
+    if (fused_eligible(in_dtype, dk, dv, n_seqs, H)) return 0;
     size_t b = record_area(n_seqs, total_tokens, H, dk, in_dtype == KDA_F32);
     if (use_segments(n_seqs, total_tokens, H, dv))
         b += static_cast<size_t>(seg_slot_bound(n_seqs, total_tokens)) * H * dk *
@@ -1611,6 +1444,7 @@ size_t chunk_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32_t H, in
 }
 
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream) {
+    if (fused_eligible(a.in_dtype, a.dk, a.dv, a.n_seqs, a.H)) return launch_fused(a, stream);
     if (a.dk == 128) return dispatch<128>(a, stream);
     return dispatch<64>(a, stream);
 }

@@ -56,10 +56,27 @@ struct ChunkArgs {
     int64_t ckpt_slots;    // capacity of ckpt in [H, dk, dv] states
 };
 
-// Workspace bytes of a chunked prefill: one record per (head, 16-token block).
+// Segment buffers of a prefill that runs long sequences in segments (see kda_chunk_util.hpp):
+// per (segment slot, head) the segment's start state S, its transition M and its zero-start
+// state B, fp32.
+struct SegArgs {
+    float* S;            // [slots, H, d_k, d_v] segment start states
+    float* M;            // [slots, H, d_k, d_k]
+    float* B;            // [slots, H, d_k, d_v]
+    int64_t slots;
+    int32_t n_vblk_m;    // column blocks of M (d_k columns; two-kernel path)
+    int32_t seg_shift;   // log2 of the segment length in tokens
+};
+
+// Workspace bytes of a chunked prefill (records and/or segment buffers, by path).
 size_t chunk_workspace_bytes(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
                              int32_t dv, int32_t in_dtype);
 
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream);
+
+// The fused kernel (kda_fused.hip): 16-bit inputs at d_k = d_v = 128 with at least 256
+// (sequence, head) units -- whole sequences, records built and consumed in LDS, no workspace.
+bool fused_eligible(int32_t in_dtype, int32_t dk, int32_t dv, int32_t n_seqs, int32_t H);
+hipError_t launch_fused(const ChunkArgs& a, hipStream_t stream);
 
 }  // namespace kda

@@ -57,9 +57,13 @@ def chunk(lib, q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, beta=FAKE + 0x3
 
 
 def test_chunk_fwd_rejects(lib):
-    ws_need = K.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128)
-    assert chunk(lib, ws=FAKE + 0x80000000, ws_bytes=ws_need - 1) == WS   # undersized workspace
-    assert chunk(lib, ws=0, ws_bytes=0) == WS                             # missing workspace
+    # 4096 tokens and 2 heads run in segments, whose buffers live in the workspace
+    ws_need = K.kda_chunk_fwd_workspace_size(1, 4096, 2, 128, 128)
+    assert ws_need > 0
+    assert chunk(lib, T=4096, ws=FAKE + 0x80000000, ws_bytes=ws_need - 1) == WS   # undersized
+    assert chunk(lib, T=4096, ws=0, ws_bytes=0) == WS                             # missing
+    f32_need = K.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, in_dtype=__import__("torch").float32)
+    assert chunk(lib, in_dt=0, ws=FAKE + 0x80000000, ws_bytes=f32_need - 1) == WS   # fp32 records
     assert chunk(lib, ws=FAKE + 0x20000000 + 64) == INV                   # workspace overlaps v
     assert chunk(lib, in_dt=7) == INV
     assert chunk(lib, g_dt=-1) == INV
@@ -99,37 +103,51 @@ def test_chunk_fwd_gated_rejects(lib):
     assert gated(lib, o=FAKE + 0x48000000 + 64) == INV  # o overlaps A
     assert gated(lib, ws=FAKE + 0x40000000 + 64) == INV  # workspace overlaps z
     assert gated(lib, dk=96) == UNS
-    assert gated(lib, ws_bytes=16) == WS
+    assert gated(lib, T=4096, ws_bytes=16) == WS
+
+
+def two_kernel_workspace(n, tok, H, dk, dv, tpr, rec):
+    """One fixed-size record per (head, slot) -- 32 tokens for 16-bit inputs (two 16-token
+    sub-blocks), 16 for fp32 -- with slots <= tokens / tpr + sequences + 1 and the area rounded up
+    to 256 bytes.  Launches that cut long sequences into 8192-token segments (when n * H * dv / 64
+    <= 128 and sequences average at least 16384 tokens) add, per (segment slot, head), a start
+    state, B (d_k x d_v) and M (d_k x d_k) in fp32, with segment slots <= tokens / 8192 +
+    sequences + 1."""
+    area = (tok // tpr + n + 1) * H * rec
+    area = (area + 255) // 256 * 256
+    if n * H * (dv // 64) <= 128 and tok >= 2 * 8192 * n:
+        area += (tok // 8192 + n + 1) * H * dk * (2 * dv + dk) * 4
+    return area
 
 
 def test_workspace_size(lib):
     import torch
-    # one fixed-size record per (head, slot): 32 tokens for 16-bit inputs (two 16-token
-    # sub-blocks), 16 tokens for fp32 inputs; slots <= tokens/tok + sequences + 1; the record area
-    # is rounded up to 256 bytes.  Launches that split long sequences into 8192-token segments
-    # add, per (segment slot, head), a start state, B (d_k x d_v) and M (d_k x d_k) in fp32, with
-    # segment slots <= tokens/8192 + sequences + 1.
-    for dt, tpr in ((torch.bfloat16, 32), (torch.float32, 16)):
-        rec = K.kda_chunk_fwd_workspace_size(1, 0, 1, 128, 128, in_dtype=dt) // 2
+    # 16-bit records at d_k = 128: 6 fp16 [16][128] arrays, 3 + 3 fp16 16 x 16 tiles, 128 fp32 decays
+    rec128 = 6 * 16 * 128 * 2 + 3072 + 512
+    # 16-bit inputs at d_k = d_v = 128: no workspace when the (sequence, head) units fill 256
+    # workgroups (the fused kernel runs whole sequences); otherwise the two-kernel layout (its
+    # segment pass 1 is the fused kernel, which writes the same records)
+    for n, tok, H in [(4, 4 * 4096, 16), (8, 1 << 20, 8), (1, 1 << 16, 32), (3, 17, 5), (1, 15, 1),
+                      (16, 16 * 4096, 16), (1, 4096, 2), (2, 32768, 2), (64, 64 * 1024, 16), (256, 256, 1)]:
+        want = 0 if n * H >= 256 else two_kernel_workspace(n, tok, H, 128, 128, 32, rec128)
+        assert K.kda_chunk_fwd_workspace_size(n, tok, H, 128, 128) == want, (n, tok, H)
+    # the bf16 prefill workload runs whole sequences; the long and packed ones in 8192-token segments
+    assert K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128) == (512 + 5) * 16 * rec128
+    assert K.kda_chunk_fwd_workspace_size(8, 1 << 20, 8, 128, 128) == \
+        (32768 + 9) * 8 * rec128 + (128 + 9) * 8 * 128 * 384 * 4
+    assert K.kda_chunk_fwd_workspace_size(1, 1 << 16, 32, 128, 128) == \
+        (2048 + 2) * 32 * rec128 + (8 + 2) * 32 * 128 * 384 * 4
+    # fp32 inputs, or 16-bit inputs with a head size of 64
+    for dt, tpr, dk in ((torch.bfloat16, 32, 64), (torch.float32, 16, 128), (torch.float32, 16, 64)):
+        rec = K.kda_chunk_fwd_workspace_size(1, 0, 1, dk, dk, in_dtype=dt) // 2
         assert rec > 0 and rec % 16 == 0
         for n, tok, H in [(4, 4 * 4096, 16), (8, 1 << 20, 8), (1, 1 << 16, 32), (3, 17, 5), (1, 15, 1)]:
-            area = (tok // tpr + n + 1) * H * rec
-            area = (area + 255) // 256 * 256
-            got = K.kda_chunk_fwd_workspace_size(n, tok, H, 128, 128, in_dtype=dt)
-            seg = (tok // 8192 + n + 1) * H * 128 * (2 * 128 + 128) * 4
-            assert got in (area, area + seg), (n, tok, H, got, area)
-    # 16-bit records: 6 fp16 [16][128] arrays, 3 + 3 fp16 16 x 16 tiles and 128 fp32 decays
-    assert K.kda_chunk_fwd_workspace_size(1, 0, 1, 128, 128) == 2 * 28160
-    # the bf16 prefill workload runs unsegmented; the long one (1 x 65536 tokens, 32 heads) and
-    # the packed one (8 sequences, 2^20 tokens, 8 heads) are segmented
-    bf = K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128)
-    assert bf == ((512 + 5) * 16 * 28160 + 255) // 256 * 256
-    for n, tok, H in [(1, 1 << 16, 32), (8, 1 << 20, 8)]:
-        area = ((tok // 32 + n + 1) * H * 28160 + 255) // 256 * 256
-        assert K.kda_chunk_fwd_workspace_size(n, tok, H, 128, 128) == \
-            area + (tok // 8192 + n + 1) * H * 128 * 384 * 4
+            got = K.kda_chunk_fwd_workspace_size(n, tok, H, dk, dk, in_dtype=dt)
+            assert got == two_kernel_workspace(n, tok, H, dk, dk, tpr, rec), (n, tok, H, got)
+    # 16-bit records at d_k = 64: 6 fp16 [16][64] arrays, 3 + 3 fp16 16 x 16 tiles, 64 fp32 decays
+    assert K.kda_chunk_fwd_workspace_size(1, 0, 1, 64, 64) == 2 * (6 * 16 * 64 * 2 + 3072 + 256)
     f32 = K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128, in_dtype=torch.float32)
-    assert f32 > bf
+    assert f32 > K.kda_chunk_fwd_workspace_size(4, 4 * 4096, 16, 128, 128)
     assert K.kda_chunk_fwd_workspace_size(1, 4096, 16, 96, 128) == 0
     assert K.kda_chunk_fwd_workspace_size(0, 4096, 16, 128, 128) == 0
     assert lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 64, 7) == 0
@@ -188,8 +206,9 @@ def test_chunk_fwd_checkpointed_rejects(lib):
     assert ckpt(lib, ck=FAKE + 0x40000000 - 64) == INV   # checkpoints run into g
     assert ckpt(lib, A=FAKE + 0x48000000, gmin=1.0) == UNS   # fused gate: g_min checked as usual
     assert ckpt(lib, dk=96) == UNS
-    assert ckpt(lib, ws_bytes=16) == WS                  # otherwise kda_chunk_fwd's checks
-    assert ckpt(lib, cu=FAKE + 0x60000000, N=3, slots=5, ws_bytes=16) == WS
+    # otherwise kda_chunk_fwd's checks (4096 tokens in two or three sequences need segment buffers)
+    assert ckpt(lib, T=4096, slots=64, ws_bytes=16) == WS
+    assert ckpt(lib, T=4096, cu=FAKE + 0x60000000, N=3, slots=67, ws_bytes=16) == WS
 
 
 def test_checkpoint_layout_helper():

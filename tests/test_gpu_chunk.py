@@ -106,6 +106,35 @@ def test_prefill_varlen_small_all_units():
     check_full(d, oracle_g(d), TOL["bf16"], label="varlen small")
 
 
+# ---- whole sequences in the fused kernel: 16-bit inputs at d_k = d_v = 128 when the (sequence,
+# head) units fill 256 workgroups --------------------------------------------------------------
+@pytest.mark.parametrize("T", [1, 47, 300])
+def test_fused_whole_sequences(T):
+    """256 (sequence, head) units of one, 47 (a ragged second sub-block) and 300 tokens, random
+    initial states; every unit."""
+    d = prefill_case("prefill_bf16", B=64, H=4, T=T)
+    assert K.kda_chunk_fwd_workspace_size(64, 64 * T, 4, 128, 128) == 0
+    say("fused whole", T)
+    check_full(d, oracle_g(d), TOL["bf16"], label=f"fused whole T={T}")
+
+
+def test_fused_whole_packed_and_gated():
+    """A packed batch of 130 sequences x 2 heads (empty, single-token, chunk-exact and ragged
+    lengths) through kda_chunk_fwd and through the fused gate; every unit."""
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.choice([0, 1, 16, 32, 33, 64, 150, 257], size=130)]
+    d = prefill_case("prefill_varlen", seqlens=lens, H=2)
+    say("fused whole packed", sum(lens))
+    check_full(d, oracle_g(d), TOL["bf16"], label="fused whole packed")
+    o, hT = _gated(d)
+    cu = d["cu_seqlens"].numpy()
+    o_ref, S_ref, _ = oracle.forward(d["q"], d["k"], d["v"], d["beta"], oracle.gate(d["A"], d["z"]),
+                                     S0=d["S0"], cu_seqlens=cu)
+    eo, es = rel_err(o, o_ref), rel_err(hT, S_ref)
+    say(f"  fused whole gated: o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("gmode", ["floor", "one"])
 def test_prefill_gate_extremes(gmode):
     """g = -5 in every channel (the decay floor: diagonal-block factors reach e^80) and g = 0
@@ -392,7 +421,7 @@ def _check_checkpoints(d, every, tol, gated=False, units=None, label=""):
             assert torch.isnan(ck_host[s]).all(), s
 
 
-@pytest.mark.parametrize("case", ["fixed", "varlen", "f32", "gated"])
+@pytest.mark.parametrize("case", ["fixed", "varlen", "f32", "gated", "fused_whole"])
 def test_checkpoints_parity(case):
     """States stored every k tokens equal the oracle's states at those boundaries; o and the
     final state equal the plain entry points' bit for bit; slots between packed sequences keep
@@ -403,10 +432,12 @@ def test_checkpoints_parity(case):
         d, every, tol = prefill_case("prefill_varlen", seqlens=[0, 5, 64, 130, 200, 17, 256], H=3), 64, TOL["bf16"]
     elif case == "f32":
         d, every, tol = prefill_case("prefill_f32_small"), 64, TOL["f32"]
-    else:
+    elif case == "gated":
         d, every, tol = prefill_case("prefill_bf16", B=2, H=2, T=257), 128, TOL["bf16"]
+    else:   # 256 (sequence, head) units: whole sequences in the fused kernel, checkpoints from LDS
+        d, every, tol = prefill_case("prefill_bf16", B=64, H=4, T=200), 64, TOL["bf16"]
     say("checkpoints", case, every)
-    _check_checkpoints(d, every, tol, gated=(case == "gated"), label=case)
+    _check_checkpoints(d, every, tol, gated=(case in ("gated", "fused_whole")), label=case)
 
 
 def test_checkpoints_full_size_sampled():

@@ -1,11 +1,15 @@
-"""GPU, white box: the workspace records of the intra-block kernel (16-bit inputs) against their
-definitions, evaluated in fp64 from the same inputs.
+"""GPU, white box: the workspace records of the intra-block kernel (16-bit inputs, head sizes 64
+and 128) against their definitions, evaluated in fp64 from the same inputs.  The fused kernel
+(whole sequences at d_k = d_v = 128 when the (sequence, head) units fill the chip) builds the same
+records in LDS, where they are checked only through its outputs.
 
 A record covers 32 tokens, two 16-token sub-blocks, with G the per-channel cumsum of g from the
 record's first token [habr § Последовательность: the bounded gate keeps every factor in range]:
   Kt = e^G k,  Qt = e^G q (times the output scale),  Kb = e^{G_31 - G} k      (per sub-block)
   A[i, j] = beta_i sum_c k_ic k_jc e^{G_ic - G_jc} (j < i),  P[i, j] = the same with q_i, j <= i
-  T' = (I + A)^{-1} Diag(beta),  and e^{G_31} - 1 per channel.
+  T' = (I + A)^{-1} Diag(beta) (its diagonal blocks T'_00, T'_11),  C[i, j] = sum_c k_{16+i,c}
+  k_jc e^{G_{16+i,c} - G_jc} (the cross block of A without beta, stored negated),
+  and e^{G_31} - 1 per channel.
 The record stores them in fp16 MFMA fragment order (Kt, Qt: 16x16x32 A operands; Kb^T: 16x16x16
 A operand, channel-major; T', P: [16][16] tiles), so each field is checked to fp16 precision.
 The gates are scaled down 20x so that every field, the cross-sub-block tiles included, is O(1).
@@ -19,13 +23,17 @@ from kda_testutil import DEV, oracle_g, prefill_case, say
 
 pytestmark = pytest.mark.gpu
 
-DK = 128
-E2 = 16 * DK * 2                     # bytes of one fp16 [16][DK] array
-OFF_T = 6 * E2                       # T'_00, T'_10, T'_11
-OFF_P = OFF_T + 3 * 512              # P_00, P_10, P_11
-OFF_G = OFF_P + 3 * 512              # e^{G_31} - 1, DK fp32
-REC = OFF_G + 4 * DK
 TOL = 2e-3                           # fp16 storage is 2^-11 relative
+
+
+def layout(dk):
+    """Byte offsets of a record at head size dk: six fp16 [16][dk] arrays, then T'_00, -C, T'_11,
+    then P_00, P_10, P_11 (fp16 16 x 16 tiles), then e^{G_31} - 1 (dk fp32)."""
+    e2 = 16 * dk * 2
+    off_t = 6 * e2
+    off_p = off_t + 3 * 512
+    off_g = off_p + 3 * 512
+    return e2, off_t, off_p, off_g, off_g + 4 * dk
 
 
 def frag32(r, c):
@@ -44,15 +52,16 @@ def fragT(r, s):
     return (r + 16 * (s >> 2)) * 4 + (s & 3)
 
 
-def decode(rec):
+def decode(rec, dk):
+    E2, OFF_T, OFF_P, OFF_G, _ = layout(dk)
     h = lambda off, n: rec[off:off + 2 * n].view(np.float16).astype(np.float64)
-    r16, c16 = np.meshgrid(np.arange(16), np.arange(DK), indexing="ij")
+    r16, c16 = np.meshgrid(np.arange(16), np.arange(dk), indexing="ij")
 
     def tok_major(off):
-        return h(off, 16 * DK)[frag32(r16, c16)]
+        return h(off, 16 * dk)[frag32(r16, c16)]
 
     def chan_major(off):
-        return h(off, 16 * DK)[frag16(c16, r16)]
+        return h(off, 16 * dk)[frag16(c16, r16)]
 
     rr, ss = np.meshgrid(np.arange(16), np.arange(16), indexing="ij")
     tile = lambda off: h(off, 256)[fragT(rr, ss)]
@@ -61,16 +70,16 @@ def decode(rec):
         base = 3 * s * E2
         out[f"Kt{s}"], out[f"Qt{s}"], out[f"Kb{s}"] = (tok_major(base), tok_major(base + E2),
                                                        chan_major(base + 2 * E2))
-    for name, off in (("T", OFF_T), ("P", OFF_P)):
-        out[name + "00"], out[name + "10"], out[name + "11"] = (tile(off), tile(off + 512),
-                                                                tile(off + 1024))
-    out["gamma"] = rec[OFF_G:OFF_G + 4 * DK].view(np.float32).astype(np.float64)
+    out["T00"], out["negC"], out["T11"] = tile(OFF_T), tile(OFF_T + 512), tile(OFF_T + 1024)
+    out["P00"], out["P10"], out["P11"] = tile(OFF_P), tile(OFF_P + 512), tile(OFF_P + 1024)
+    out["gamma"] = rec[OFF_G:OFF_G + 4 * dk].view(np.float32).astype(np.float64)
     return out
 
 
 def expected(g, k, q, beta, t0, n):
     """The record's fields in fp64 for tokens t0 .. t0 + n - 1 (zero past the sequence)."""
-    gx, kx, qx, bx = (np.zeros((32, DK)), np.zeros((32, DK)), np.zeros((32, DK)), np.zeros(32))
+    dk = k.shape[1]
+    gx, kx, qx, bx = (np.zeros((32, dk)), np.zeros((32, dk)), np.zeros((32, dk)), np.zeros(32))
     gx[:n], kx[:n], qx[:n], bx[:n] = g[t0:t0 + n], k[t0:t0 + n], q[t0:t0 + n], beta[t0:t0 + n]
     G = np.cumsum(gx, axis=0)
     A = np.zeros((32, 32))
@@ -87,30 +96,37 @@ def expected(g, k, q, beta, t0, n):
     for s in range(2):
         sl = slice(16 * s, 16 * s + 16)
         out[f"Kt{s}"], out[f"Qt{s}"], out[f"Kb{s}"] = Kt[sl], Qt[sl], Kb[sl]
-    for name, M in (("T", T), ("P", P)):
-        out[name + "00"], out[name + "10"], out[name + "11"] = M[:16, :16], M[16:, :16], M[16:, 16:]
+    C = np.zeros((16, 16))
+    for i in range(16):
+        for j in range(16):
+            C[i, j] = np.sum(kx[16 + i] * np.exp(G[16 + i] - G[j]) * kx[j])
+    out["T00"], out["negC"], out["T11"] = T[:16, :16], -C, T[16:, 16:]
+    out["P00"], out["P10"], out["P11"] = P[:16, :16], P[16:, :16], P[16:, 16:]
     return out
 
 
-@pytest.mark.parametrize("T", [63, 96])
-def test_intra_records_match_definitions(T):
+def _check_records(W, base, slots, T, d, g, dk):
+    rec_bytes = layout(dk)[4]
+    f64 = lambda x: x.double().numpy().reshape(T, -1)
+    g64, k64, q64, b64 = f64(g), f64(d["k"]), f64(d["q"]), d["beta"].double().numpy().reshape(T)
+    assert W.size >= (base + max(slots) + 1) * rec_bytes
+    for j in slots:
+        got = decode(W[(base + j) * rec_bytes:(base + j + 1) * rec_bytes], dk)
+        ref = expected(g64, k64, q64, b64, 32 * j, min(T - 32 * j, 32))
+        for name, r in ref.items():
+            err = np.abs(got[name] - r).max() / max(np.abs(r).max(), 1e-30)
+            say(f"  record {j} {name}: max|ref| {np.abs(r).max():.3e}  rel err {err:.2e}")
+            assert err <= TOL, (j, name, err)
+
+
+@pytest.mark.parametrize("T,DK", [(63, 64), (96, 64), (63, 128), (96, 128)])
+def test_intra_records_match_definitions(T, DK):
     """T = 63: a full record and one with 31 tokens (the tail reads zeros); T = 96: three."""
-    d = prefill_case("prefill_bf16", B=1, H=1, T=T)
+    d = prefill_case("prefill_bf16", B=1, H=1, T=T, dk=DK, dv=DK)
     g = oracle_g(d) / 20.0
-    say("records", T)
+    say("records", T, DK)
     ws = torch.zeros(K.kda_chunk_fwd_workspace_size(1, T, 1, DK, DK), dtype=torch.uint8, device=DEV)
     K.kda_chunk_fwd(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV), d["beta"].to(DEV), g.to(DEV),
                     initial_state=d["S0"].to(DEV), workspace=ws)
     torch.cuda.synchronize()
-    W = ws.cpu().numpy()
-    f64 = lambda x: x.double().numpy().reshape(T, -1)
-    g64, k64, q64, b64 = f64(g), f64(d["k"]), f64(d["q"]), d["beta"].double().numpy().reshape(T)
-    nrec = (T + 31) // 32
-    assert W.size >= nrec * REC
-    for slot in range(nrec):
-        got = decode(W[slot * REC:(slot + 1) * REC])
-        ref = expected(g64, k64, q64, b64, 32 * slot, min(T - 32 * slot, 32))
-        for name, r in ref.items():
-            err = np.abs(got[name] - r).max() / max(np.abs(r).max(), 1e-30)
-            say(f"  record {slot} {name}: max|ref| {np.abs(r).max():.3e}  rel err {err:.2e}")
-            assert err <= TOL, (slot, name, err)
+    _check_records(ws.cpu().numpy(), 0, range((T + 31) // 32), T, d, g, DK)
