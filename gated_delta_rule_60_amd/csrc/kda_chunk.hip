@@ -865,9 +865,13 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     if (unit >= units) return;
     const int h = static_cast<int>(unit % H);
     int n = static_cast<int>(unit / H);
-    int64_t seg = 0;
-    if constexpr (MODE != 0) {
+    int64_t seg = 0, seg_slot = 0;
+    if constexpr (MODE == 1) {
         if (!locate_seg(p, sg, unit / H, n, seg)) return;
+        seg_slot = unit / H;
+    } else if constexpr (MODE == 2) {
+        // every segment of the batch runs here, longest first
+        if (!locate_seg_lpt(p, sg, unit / H, n, seg, seg_slot)) return;
     }
     const int DV = p.dv;
     const int32_t vstride = static_cast<int32_t>(H) * DV;
@@ -896,8 +900,8 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     bool ident = false, use_v = true, emit_o = true;
     if constexpr (MODE != 0) {
         const int64_t SEGC = (int64_t(1) << sg.seg_shift) / CHT;
-        const int64_t nseg = seg_count(len, sg.seg_shift), slot = unit / H;
-        const int64_t us = slot * H + h;                                // (segment slot, head)
+        const int64_t nseg = seg_count(len, sg.seg_shift);
+        const int64_t us = seg_slot * H + h;                            // (segment slot, head)
         c_begin = seg * SEGC;
         c_end = c_begin + SEGC < nchunks_all ? c_begin + SEGC : nchunks_all;
         if (MODE == 1) {
@@ -920,8 +924,8 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                 return;                                                // the last segment: pass 2
             }
         } else {
-            if (seg == 0) return;                                      // ran in pass 1
-            init = sg.S + us * DK * DV;
+            if (seg == 0 && !sg.from0) return;                         // ran in pass 1
+            if (seg > 0) init = sg.S + us * DK * DV;                   // else the initial state
             if (seg + 1 < nseg) fin = nullptr;                         // its end state is known
         }
     }
@@ -1200,6 +1204,220 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     }
 }
 
+// Segment pass 1 at d_k = d_v = 128 with 16-bit inputs: one workgroup of eight waves per
+// (segment, head) for every segment but a sequence's last, running the segment's pair at once --
+// wave w holds state columns 16 w .. 16 w + 15 of both M (from the identity, V = 0) and B (from
+// zero, with V).  The records stream through LDS once, their Qt and P parts skipped (no o here);
+// the two tiles' dependent chains interleave in each wave.
+constexpr uint64_t pair_skip_mask() {     // 1 KB units of a two-record chunk that hold only Qt / P
+    using R = Rec<128, false>;
+    uint64_t m = 0;
+    for (int u = 0; u < 64; ++u) {
+        const int lo = 1024 * u, hi = lo + 1024;
+        for (int b = 0; b < 2; ++b) {
+            const int o = b * R::BYTES;
+            const int rng[3][2] = {{o + R::E * 2, o + 2 * R::E * 2}, {o + 4 * R::E * 2, o + 5 * R::E * 2},
+                                   {o + R::OFF_P, o + R::OFF_G}};
+            for (int k = 0; k < 3; ++k)
+                if (lo >= rng[k][0] && hi <= rng[k][1]) m |= uint64_t(1) << u;
+        }
+    }
+    return m;
+}
+
+template <int IDT>
+__global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t nslots, const uint8_t* ws,
+                                                            SegArgs sg) {
+    constexpr int DK = 128, NW = 8;
+    using R = Rec<DK, false>;
+    constexpr int KS = DK / 32, CT = DK / 16;
+    constexpr int NB = 2, CHT = NB * R::TOK;           // two 32-token records per chunk
+    constexpr int WKB = 64 * 16;
+    constexpr int ROUNDS = (NB * R::BYTES + NW * WKB - 1) / (NW * WKB);
+    constexpr int RBYTES = ROUNDS * NW * WKB;
+    constexpr int BVW = 16 * NW;                       // 128 columns: all of M, all of B
+    constexpr int VROW = BVW * 2;
+    constexpr int VROUNDS = (CHT * VROW + NW * WKB - 1) / (NW * WKB);
+    constexpr int LBYTES = RBYTES + VROUNDS * NW * WKB;
+    constexpr int E2 = 2 * R::E;
+    constexpr uint64_t SKIP = pair_skip_mask();
+    static_assert(ROUNDS * NW <= 64, "skip mask covers the chunk");
+    static_assert(IDT == KDA_BF16, "16-bit inputs");
+    __shared__ __attribute__((aligned(16))) uint8_t bufA[LBYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t bufB[LBYTES];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int ln = lane & 15, lq = lane >> 4;
+    const int64_t H = p.H;
+    const int64_t unit = blockIdx.x;                   // (segment slot, head)
+    const int h = static_cast<int>(unit % H);
+    int n;
+    int64_t seg;
+    if (!locate_seg(p, sg, unit / H, n, seg)) return;
+    const int32_t vstride = static_cast<int32_t>(H) * DK;
+    int64_t bos, len, base;
+    if (p.cu) {
+        int64_t end;
+        seq_bounds(p, n, bos, end);
+        len = end - bos;
+        base = bos / R::TOK + n;
+    } else {
+        bos = static_cast<int64_t>(n) * p.T;
+        len = p.T;
+        base = static_cast<int64_t>(n) * ((p.T + R::TOK - 1) / R::TOK);
+    }
+    const int64_t nseg = seg_count(len, sg.seg_shift);
+    if (seg + 1 >= nseg) return;                       // a sequence's last segment has no pair
+    const uint8_t* recs = ws + (static_cast<int64_t>(h) * nslots + base) * R::BYTES;
+    const int64_t SEGC = (int64_t(1) << sg.seg_shift) / CHT;
+    const int64_t nchunks_all = (len + CHT - 1) / CHT;
+    const int64_t c_begin = seg * SEGC;
+    const int64_t c_end = c_begin + SEGC < nchunks_all ? c_begin + SEGC : nchunks_all;
+    const int n0 = wave * 16;                          // this wave's first column of M and of B
+
+    // tile 0: M (lane (ln, lq) holds M[16 i + 4 lq + r][n0 + ln]); tile 1: B, the same layout
+    f32x4 S[2][CT];
+#pragma unroll
+    for (int i = 0; i < CT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            S[0][i][r] = (16 * i + 4 * lq + r == n0 + ln) ? 1.f : 0.f;
+            S[1][i][r] = 0.f;
+        }
+    auto tokens_in = [&](int64_t c) -> int {
+        const int64_t rem = len - c * CHT;
+        return static_cast<int>(rem < 0 ? 0 : rem < CHT ? rem : CHT);
+    };
+    // chunk c's records (their Kt, Kb, T' and decay units) and its V rows into an LDS buffer
+    auto prefetch = [&](uint8_t* buf, int64_t c) {
+        const int nt = tokens_in(c);
+        const int nbk = (nt + R::TOK - 1) / R::TOK;
+        const __amdgpu_buffer_rsrc_t rr =
+            make_rsrc(nt > 0 ? recs + c * NB * R::BYTES : ws, static_cast<uint32_t>(nbk * R::BYTES));
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(
+            nt > 0 ? static_cast<const uint8_t*>(p.v) + ((bos + c * CHT) * H + h) * DK * 2 : p.v,
+            static_cast<uint32_t>(nt * vstride * 2));
+#pragma unroll
+        for (int it = 0; it < ROUNDS; ++it) {
+            const int u = it * NW + wave;
+            if ((SKIP >> u) & 1) continue;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void*)(buf + u * WKB), 16,
+                                                     u * WKB + 16 * lane, 0, 0, 0);
+        }
+#pragma unroll
+        for (int it = 0; it < VROUNDS; ++it) {
+            const int u = it * NW + wave;
+            const int byte = u * WKB + 16 * lane;
+            const int row = byte / VROW, col = byte % VROW;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(buf + RBYTES + u * WKB),
+                                                     16, row * vstride * 2 + col, 0, 0, CP_NT);
+        }
+    };
+    // one chunk: two 32-token steps of both tiles
+    auto run = [&](const uint8_t* buf, int64_t c, uint8_t* nbuf) {
+        if (c + 1 < c_end) prefetch(nbuf, c + 1);
+        __builtin_amdgcn_sched_barrier(0x78F);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint8_t* rb = buf + b * R::BYTES;
+            const float* gam = reinterpret_cast<const float*>(rb + R::OFF_G);   // e^{G_last} - 1
+            const uint8_t* tb = rb + R::OFF_T + 8 * lane;                        // T'_00, -C, T'_11
+            const f16x4 t00 = *reinterpret_cast<const f16x4*>(tb);
+            const f16x4 ncm = *reinterpret_cast<const f16x4*>(tb + 512);
+            const f16x4 t11 = *reinterpret_cast<const f16x4*>(tb + 1024);
+            // Y_s = Kt_s S for both tiles (contraction over d_k; S packed as the B operand)
+            f32x4 Y[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const f16x8 k0 = *reinterpret_cast<const f16x8*>(rb + 1024 * kk + 16 * lane);
+                const f16x8 k1 = *reinterpret_cast<const f16x8*>(rb + 3 * E2 + 1024 * kk + 16 * lane);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f16x8 sb;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sb[i] = static_cast<_Float16>(S[t][2 * kk][i]);
+                        sb[4 + i] = static_cast<_Float16>(S[t][2 * kk + 1][i]);
+                    }
+                    Y[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, sb, Y[t][0], 0, 0, 0);
+                    Y[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, sb, Y[t][1], 0, 0, 0);
+                }
+            }
+            // X = V - Y (V = 0 for M); W_0 = T'_00 X_0, X_1' = X_1 - C W_0, W_1 = T'_11 X_1'
+            f16x8 wx[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                f32x4 X0, X1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ve0 = (32 * b + 4 * lq + i) * BVW + n0 + ln, ve1 = ve0 + 16 * BVW;
+                    const uint16_t* vb = reinterpret_cast<const uint16_t*>(buf + RBYTES);
+                    X0[i] = (t == 1 ? bf16_val(vb[ve0]) : 0.f) - Y[t][0][i];
+                    X1[i] = (t == 1 ? bf16_val(vb[ve1]) : 0.f) - Y[t][1][i];
+                }
+                f16x4 x0, x1, w0, w1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x0[i] = static_cast<_Float16>(X0[i]);
+                const f32x4 W0 = __builtin_amdgcn_mfma_f32_16x16x16f16(t00, x0, zero4(), 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w0[i] = static_cast<_Float16>(W0[i]);
+                const f32x4 X1p = __builtin_amdgcn_mfma_f32_16x16x16f16(ncm, w0, X1, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x1[i] = static_cast<_Float16>(X1p[i]);
+                const f32x4 W1 = __builtin_amdgcn_mfma_f32_16x16x16f16(t11, x1, zero4(), 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w1[i] = static_cast<_Float16>(W1[i]);
+                wx[t] = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            // S <- Diag(e^{G_31}) S + Kb^T W for both tiles
+            const uint8_t* kb0 = rb + 2 * E2 + 8 * lane;
+            const uint8_t* kb1 = rb + 5 * E2 + 8 * lane;
+#pragma unroll
+            for (int i = 0; i < CT; ++i) {
+                const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * i + 4 * lq);
+                const f16x8 ka = __builtin_shufflevector(*reinterpret_cast<const f16x4*>(kb0 + 512 * i),
+                                                         *reinterpret_cast<const f16x4*>(kb1 + 512 * i), 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f32x4 acc;
+                    acc[0] = fmaf(S[t][i][0], gm.x, S[t][i][0]); acc[1] = fmaf(S[t][i][1], gm.y, S[t][i][1]);
+                    acc[2] = fmaf(S[t][i][2], gm.z, S[t][i][2]); acc[3] = fmaf(S[t][i][3], gm.w, S[t][i][3]);
+                    S[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, wx[t], acc, 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    prefetch(bufA, c_begin);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    for (int64_t ci = c_begin; ci < c_end; ci += 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        run(bufA, ci, bufB);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        if (ci + 1 >= c_end) break;
+        __builtin_amdgcn_sched_barrier(0);
+        run(bufB, ci + 1, bufA);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+    }
+    const int64_t us = unit;                           // (segment slot, head)
+    float* Mo = sg.M + us * DK * DK;
+    float* Bo = sg.B + us * DK * DK;
+#pragma unroll
+    for (int i = 0; i < CT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t e = static_cast<int64_t>(16 * i + 4 * lq + r) * DK + n0 + ln;
+            Mo[e] = S[0][i][r];
+            Bo[e] = S[1][i][r];
+        }
+}
+
 // Segment scan: one workgroup per (sequence, head, 16 state columns) walks the sequence's
 // segments, S_start(s + 1) = M_s S_start(s) + B_s for s = 1 .. nseg - 2, in fp32.  The column
 // blocks are independent (M acts on the rows), so they run apart.  Each step is a d_k x d_k by
@@ -1232,7 +1450,8 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
         slot0 = static_cast<int64_t>(n) * seg_count(p.T, sg.seg_shift);
     }
     const int64_t nseg = seg_count(len, sg.seg_shift);
-    if (nseg < 3) return;                             // no middle segment: nothing to combine
+    const int64_t s_first = sg.from0 ? 0 : 1;         // first segment with a pair
+    if (nseg < s_first + 2) return;                   // no pair before the last segment
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int li = lane & 15, lc = lane >> 4;         // row / column within a tile; K group
@@ -1255,13 +1474,15 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
         }
     };
     {
-        const float* S1 = sg.S + ((slot0 + 1) * H + h) * DK * DV + cb * 16;
-        for (int e = t; e < DK * 16; e += 256) sS[0][(e >> 4) * SP + (e & 15)] = S1[(e >> 4) * DV + (e & 15)];
+        // S_start(s_first): the initial state (zeros when absent) or segment 1's start from pass 1
+        const float* S1 = sg.from0 ? (p.h0 ? p.h0 + useq * DK * DV + cb * 16 : nullptr)
+                                   : sg.S + ((slot0 + 1) * H + h) * DK * DV + cb * 16;
+        for (int e = t; e < DK * 16; e += 256) sS[0][(e >> 4) * SP + (e & 15)] = S1 ? S1[(e >> 4) * DV + (e & 15)] : 0.f;
     }
-    load_step(1);
+    load_step(s_first);
     __syncthreads();
     int cur = 0;
-    for (int64_t s = 1; s + 1 < nseg; ++s) {
+    for (int64_t s = s_first; s + 1 < nseg; ++s) {
         f32x4 acc[TPW];
         float4 mc[TPW][NM];
 #pragma unroll
@@ -1396,10 +1617,24 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     const int nw = wide ? 2 * NW : NW;
     sg.n_vblk_m = DK / (16 * nw);
     const int nvb = a.dv / (16 * nw);
-    if (wide)
-        launch_state_ck<DK, IDT, ODT, PRECISE, 1, 2 * NW>(a, nslots, ws, sg, seg_units, sg.n_vblk_m + nvb, stream);
-    else
-        launch_state_ck<DK, IDT, ODT, PRECISE, 1, NW>(a, nslots, ws, sg, seg_units, sg.n_vblk_m + nvb, stream);
+    // 16-bit inputs at d_k = d_v = 128: pass 1 runs the pairs of every segment but the last, M
+    // and B together (chunk_pair_kernel); the scan then starts from the initial state and pass 2
+    // runs every segment.  Otherwise pass 1 runs segment 0 whole and the column blocks of the
+    // middle segments' M and B apart.
+    if constexpr (DK == 128 && !PRECISE) {
+        if (wide) {
+            sg.from0 = 1;
+            if (seg_units > 0)
+                hipLaunchKernelGGL((chunk_pair_kernel<IDT>), dim3(static_cast<unsigned>(seg_units)), dim3(512), 0,
+                                   stream, a, nslots, ws, sg);
+        }
+    }
+    if (!sg.from0) {
+        if (wide)
+            launch_state_ck<DK, IDT, ODT, PRECISE, 1, 2 * NW>(a, nslots, ws, sg, seg_units, sg.n_vblk_m + nvb, stream);
+        else
+            launch_state_ck<DK, IDT, ODT, PRECISE, 1, NW>(a, nslots, ws, sg, seg_units, sg.n_vblk_m + nvb, stream);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((seg_scan_kernel<DK>), dim3(static_cast<unsigned>(static_cast<int64_t>(a.n_seqs) * a.H * (a.dv / 16))),

@@ -160,5 +160,47 @@ __device__ __forceinline__ bool locate_seg(const ChunkArgs& p, const SegArgs& sg
     return n < p.n_seqs;
 }
 
+// Work index k -> sequence n, segment s and its slot, ordered longest first: every sequence's
+// segments but its last (all 2^seg_shift tokens), then the last segments (the partial ones), so
+// that a launch with more workgroups than CUs ends on its shortest ones.  Linear in the number of
+// sequences for packed batches (a segmented launch has at most 64 (sequence, head) units).
+__device__ __forceinline__ bool locate_seg_lpt(const ChunkArgs& p, const SegArgs& sg, int64_t k,
+                                               int& n, int64_t& s, int64_t& slot) {
+    const int sh = sg.seg_shift;
+    if (!p.cu) {
+        const int64_t per = seg_count(p.T, sh), full = static_cast<int64_t>(p.n_seqs) * (per - 1);
+        if (k < full) {
+            n = static_cast<int>(k / (per - 1));
+            s = k % (per - 1);
+        } else {
+            if (k - full >= p.n_seqs) return false;
+            n = static_cast<int>(k - full);
+            s = per - 1;
+        }
+        slot = static_cast<int64_t>(n) * per + s;
+        return true;
+    }
+    int64_t acc = 0;
+    for (int m = 0; m < p.n_seqs; ++m) {
+        int64_t bos, end;
+        seq_bounds(p, m, bos, end);
+        const int64_t cnt = seg_count(end - bos, sh) - 1;
+        if (k < acc + cnt) {
+            n = m;
+            s = k - acc;
+            slot = (bos >> sh) + m + s;
+            return true;
+        }
+        acc += cnt;
+    }
+    if (k - acc >= p.n_seqs) return false;
+    n = static_cast<int>(k - acc);
+    int64_t bos, end;
+    seq_bounds(p, n, bos, end);
+    s = seg_count(end - bos, sh) - 1;
+    slot = (bos >> sh) + n + s;
+    return true;
+}
+
 }  // namespace
 }  // namespace kda

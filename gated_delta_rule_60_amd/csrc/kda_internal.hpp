@@ -64,8 +64,11 @@ struct SegArgs {
     float* M;            // [slots, H, d_k, d_k]
     float* B;            // [slots, H, d_k, d_v]
     int64_t slots;
-    int32_t n_vblk_m;    // column blocks of M (d_k columns; two-kernel path)
+    int32_t n_vblk_m;    // column blocks of M (d_k columns) in segment pass 1
     int32_t seg_shift;   // log2 of the segment length in tokens
+    int32_t from0;       // pairs start at segment 0 (pass 1 runs pairs only; the scan starts from
+                         // the initial state and pass 2 runs every segment); else segment 0 runs
+                         // whole in pass 1 and the pairs start at segment 1
 };
 
 // Workspace bytes of a chunked prefill (records and/or segment buffers, by path).
