@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
 
         // ---- fused gate: g = g_min * sigmoid(exp(A) z) from z, the same arithmetic as kda_gate;
         // rows past the block's tokens get g = 0 like the zero-filled g of the unfused path
-        float ea[4];
+        GateRate ea[4];
         if constexpr (GATE) {
             const float* a = p.gate_A + static_cast<int64_t>(h) * DK + c0;
 #pragma unroll
@@ -516,7 +516,7 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     // Each lane then reads its own channels without bank conflicts.
     __shared__ __attribute__((aligned(16))) uint8_t sIn[PB];          // one phase's tiles
     __shared__ __attribute__((aligned(16))) uint16_t sKb[2][BLK * 32];  // Kb^T of one group, frag16
-    __shared__ __attribute__((aligned(16))) float sRate[GATE ? DK : 4];
+    __shared__ __attribute__((aligned(16))) float sRate[2][GATE ? DK : 4];   // gate rates: hi, lo
     __shared__ float sBeta[TOKR];
     // After the last group the input tiles are dead and hold A_00, A_11 in fp32 (for the
     // substitutions), then the staged T' / -C and P tiles (fp16).
@@ -583,7 +583,11 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     if (lane < TOKR) sBeta[lane] = bval;
     if constexpr (GATE) {   // one rate per (head, channel), shared through LDS
 #pragma unroll
-        for (int i = 0; i < DK / 64; ++i) sRate[64 * i + lane] = gate_rate(av[i]);
+        for (int i = 0; i < DK / 64; ++i) {
+            const GateRate gr = gate_rate(av[i]);
+            sRate[0][64 * i + lane] = gr.hi;
+            sRate[1][64 * i + lane] = gr.lo;
+        }
     }
     // token m of sub-block s: its four channels 32 lk + 16 hf + 4 q .. + 3 of phase tile `tile`
     // (bf16: 8 bytes)
@@ -635,10 +639,13 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
             load_phase(ph + 1);
         }
         float x[2][8], e1[2][8], gm[2][8];
-        float4 rate[2];
+        float4 rate[2][2];   // [hi, lo][channel half]
         if constexpr (GATE) {
-            rate[0] = *reinterpret_cast<const float4_ma*>(&sRate[32 * kk + 4 * q]);
-            rate[1] = *reinterpret_cast<const float4_ma*>(&sRate[32 * kk + 16 + 4 * q]);
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                rate[w][0] = *reinterpret_cast<const float4_ma*>(&sRate[w][32 * kk + 4 * q]);
+                rate[w][1] = *reinterpret_cast<const float4_ma*>(&sRate[w][32 * kk + 16 + 4 * q]);
+            }
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -648,9 +655,10 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
                 float gv;
                 if constexpr (GATE) {
                     const float z = (GDT == KDA_F32) ? __uint_as_float(rg[s][j]) : raw16(rg[s], j);
-                    const float4& r4 = rate[j >> 2];
-                    const float rt = (j & 3) == 0 ? r4.x : (j & 3) == 1 ? r4.y : (j & 3) == 2 ? r4.z : r4.w;
-                    gv = gate_log_decay(rt, z, p.g_min) * keep[s];
+                    auto pick = [&](const float4& r4) {
+                        return (j & 3) == 0 ? r4.x : (j & 3) == 1 ? r4.y : (j & 3) == 2 ? r4.z : r4.w;
+                    };
+                    gv = gate_log_decay(pick(rate[0][j >> 2]), pick(rate[1][j >> 2]), z, p.g_min) * keep[s];
                 } else if constexpr (GDT == KDA_F32) {
                     gv = __uint_as_float(rg[s][j]);
                 } else {

@@ -10,18 +10,39 @@ namespace kda {
 
 // ---------------------------------------------------------------- forget gate
 // g = g_min * sigmoid(exp(A) * z) = g_min / (1 + 2^(-rate * z)) with rate = exp(A) * log2(e),
-// one per (head, key channel).  Hardware exp2 and reciprocal (about 1 ulp each) keep g within
-// 1e-6 of the exact value over g in [-5, 0]; saturation gives g_min and -0.  The separate gate
-// kernel and the chunk kernel's fused gate both call these, with contraction off, so the two
-// paths produce the same bits of g.
-__device__ __forceinline__ float gate_rate(float A) {
-#pragma clang fp contract(off)
-    return expf(A) * 1.4426950408889634f;
+// one per (head, key channel), held as an unevaluated pair hi + lo of floats formed from its fp64
+// value.  The argument rate * z is carried the same way: the rounded product p, and the rest (the
+// product's rounding error and lo * z, at most 2^-23 |p|) by fma.  e = 2^-p comes from the hardware
+// exp2 (exact argument, 1 ulp), and 1 + 2^-(p + rest) = d + de exactly up to second order in rest:
+// d = 1 + e rounded, de its rounding error (Fast2Sum) less e * rest * ln 2.  g_min / (d + de) is
+// the rounded quotient corrected once by its residual.  Error budget: e 1 ulp, the quotient 0.5
+// ulp, so g lands within 1.5 ulp of the exact value while |rate * z| <= 126; beyond that p is
+// clamped and g is g_min on one side and below 2^-123 in magnitude on the other.  The separate
+// gate kernel and the prefill kernels' fused gate call these alike, so the two paths produce the
+// same bits.
+struct GateRate {
+    float hi, lo;
+};
+__device__ __forceinline__ GateRate gate_rate(float A) {
+    const double r = exp(static_cast<double>(A)) * 1.4426950408889634074;
+    const float hi = static_cast<float>(r);
+    return {hi, static_cast<float>(r - static_cast<double>(hi))};
 }
-__device__ __forceinline__ float gate_log_decay(float rate, float z, float g_min) {
+__device__ __forceinline__ float gate_log_decay(float rate_hi, float rate_lo, float z, float g_min) {
 #pragma clang fp contract(off)
-    const float e = __builtin_amdgcn_exp2f(-(rate * z));
-    return g_min * __builtin_amdgcn_rcpf(1.0f + e);
+    const float p = rate_hi * z;
+    const float rest = __builtin_fmaf(rate_lo, z, __builtin_fmaf(rate_hi, z, -p));   // rate * z - p
+    const float e = __builtin_amdgcn_exp2f(-__builtin_amdgcn_fmed3f(p, -126.0f, 126.0f));
+    const float d = 1.0f + e;
+    const float big = __builtin_fmaxf(e, 1.0f), small = __builtin_fminf(e, 1.0f);
+    const float de = __builtin_fmaf(-e, rest * 0.69314718055994531f, (big - d) + small);
+    const float r0 = __builtin_amdgcn_rcpf(d);
+    const float q0 = g_min * r0;
+    const float res = __builtin_fmaf(-q0, de, __builtin_fmaf(-q0, d, g_min));
+    return __builtin_fmaf(res, r0, q0);
+}
+__device__ __forceinline__ float gate_log_decay(GateRate rate, float z, float g_min) {
+    return gate_log_decay(rate.hi, rate.lo, z, g_min);
 }
 
 // ---------------------------------------------------------------- bf16 <-> fp32 (bit level)

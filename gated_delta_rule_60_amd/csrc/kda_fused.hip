@@ -52,7 +52,7 @@ constexpr int F_TILE = RT * FDK * 2;     // a bf16 [32][128] tile, 8 KiB
 struct __attribute__((aligned(16))) FusedLds {
     uint8_t rec[3][F_REC];
     f32x4 part[2][NPROD][6][64];         // A_0, A_1, P_0, P_1, C, Q in accumulator order
-    float rate[FDK];
+    float rate[2][FDK];                  // gate rates: hi, lo
     float beta[3][RT];
     float sA[2][16][16];                 // A_00, A_11 of the record being finished (fp32)
 };
@@ -135,7 +135,7 @@ __device__ __forceinline__ void load_inputs(const FCtx& c, const FUnit& u, int64
 template <int GDT, bool GATE>
 __device__ __forceinline__ void produce(const ChunkArgs& p, const PIn<(GDT == KDA_F32) ? 4 : 2>& in,
                                         uint8_t* rec, f32x4 (*part)[64], float* beta,
-                                        const float* rate, int nt, int kk, int lane) {
+                                        const float (*rate)[FDK], int nt, int kk, int lane) {
     constexpr float LOG2E = 1.4426950408889634f;
     asm volatile("" : "+v"(lane));       // as in finish(): no lane-derived values held across records
     const int m = lane & 15, q = lane >> 4;
@@ -143,10 +143,13 @@ __device__ __forceinline__ void produce(const ChunkArgs& p, const PIn<(GDT == KD
     auto raw16 = [](const uint32_t* w, int j) -> float {      // element j of packed bf16 words
         return (j & 1) ? __uint_as_float(w[j >> 1] & 0xffff0000u) : __uint_as_float(w[j >> 1] << 16);
     };
-    float4 rt4[2];
+    float4 rt4[2][2];                    // [hi, lo][channel half]
     if constexpr (GATE) {
-        rt4[0] = *reinterpret_cast<const float4_ma*>(&rate[32 * kk + 4 * q]);
-        rt4[1] = *reinterpret_cast<const float4_ma*>(&rate[32 * kk + 16 + 4 * q]);
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            rt4[w][0] = *reinterpret_cast<const float4_ma*>(&rate[w][32 * kk + 4 * q]);
+            rt4[w][1] = *reinterpret_cast<const float4_ma*>(&rate[w][32 * kk + 16 + 4 * q]);
+        }
     }
     const bool full = (nt == RT);
     const float keep[2] = {m < nt ? 1.f : 0.f, 16 + m < nt ? 1.f : 0.f};
@@ -158,9 +161,10 @@ __device__ __forceinline__ void produce(const ChunkArgs& p, const PIn<(GDT == KD
             float gv;
             if constexpr (GATE) {
                 const float z = (GDT == KDA_F32) ? __uint_as_float(in.g[s][j]) : raw16(in.g[s], j);
-                const float4& r4 = rt4[j >> 2];
-                const float rt = (j & 3) == 0 ? r4.x : (j & 3) == 1 ? r4.y : (j & 3) == 2 ? r4.z : r4.w;
-                gv = gate_log_decay(rt, z, p.g_min);
+                auto pick = [&](const float4& r4) {
+                    return (j & 3) == 0 ? r4.x : (j & 3) == 1 ? r4.y : (j & 3) == 2 ? r4.z : r4.w;
+                };
+                gv = gate_log_decay(pick(rt4[0][j >> 2]), pick(rt4[1][j >> 2]), z, p.g_min);
                 if (!full) gv *= keep[s];                        // 0 past the record's tokens
             } else if constexpr (GDT == KDA_F32) {
                 gv = __uint_as_float(in.g[s][j]);
@@ -379,7 +383,11 @@ __device__ __forceinline__ void producer_loop(const FCtx& c, const FUnit& u, Fus
     const int nrec = static_cast<int>(c.nrec);
     PIn<GSZ> in;
     if constexpr (GATE) {
-        if (wave < 2) L.rate[64 * wave + lane] = gate_rate(p.gate_A[static_cast<int64_t>(c.h) * FDK + 64 * wave + lane]);
+        if (wave < 2) {
+            const GateRate gr = gate_rate(p.gate_A[static_cast<int64_t>(c.h) * FDK + 64 * wave + lane]);
+            L.rate[0][64 * wave + lane] = gr.hi;
+            L.rate[1][64 * wave + lane] = gr.lo;
+        }
     }
     if (nrec > 0) load_inputs<GSZ>(c, u, 0, in);
     __syncthreads();

@@ -78,6 +78,10 @@ int kda_version(void);
  *             must not overlap z or A.
  *   n_tokens: >= 0 (0 is a no-op); H, d_k >= 1.
  *   g_min   : must lie in [-5, 0); other values return KDA_ERR_UNSUPPORTED.
+ * Precision (fp32 g): within 1.5 ulp of the exact value wherever |exp(A) z| <= 126 ln 2 (the
+ * hardware exp2 of the rounded argument, 1 ulp, and a corrected quotient, 0.5 ulp; the argument's
+ * rounding error is carried separately); beyond that g is g_min or below 2^-123 in magnitude.
+ * z = 0 gives g_min / 2 exactly.  bf16 g is the fp32 value rounded.
  */
 int kda_gate(const float *A, const void *z, int z_dtype, void *g, int g_dtype, int64_t n_tokens,
              int32_t H, int32_t dk, float g_min, void *stream);

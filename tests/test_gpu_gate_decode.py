@@ -11,6 +11,16 @@ from kda_testutil import DEV, rel_err, say
 pytestmark = pytest.mark.gpu
 
 
+def ulp_err(got, ref):
+    """|got - ref| in units of the fp32 spacing at |ref| (ref: the fp64 value)."""
+    return np.abs(got - ref) / np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+
+
+# fp32 gate: within 2 ulp of the fp64 value wherever |exp(A) z| / ln 2 <= 126; the kernel's own
+# error budget is 1.5 ulp (1 ulp from the hardware exp2, 0.5 from the corrected quotient)
+GATE_ULP = 2.0
+
+
 @pytest.mark.parametrize("zdt,gdt,shape", [
     (torch.bfloat16, torch.float32, (3, 77, 4, 128)),
     (torch.float32, torch.float32, (1, 256, 2, 64)),
@@ -29,11 +39,35 @@ def test_gate_parity(zdt, gdt, shape):
     torch.cuda.synchronize()
     got = g.double().cpu().numpy()
     if gdt == torch.float32:
-        assert np.abs(got - ref).max() <= 2e-6, np.abs(got - ref).max()
+        assert ulp_err(got, ref).max() <= GATE_ULP, ulp_err(got, ref).max()
         assert np.all(got[..., 0] == -2.5)
     else:  # bf16: within one bf16 ulp of the exact value
         assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
     assert got.max() <= 0.0 and got.min() >= -5.0
+
+
+def test_gate_wide_arguments():
+    """fp32 z over a wide range: the ulp bound inside |exp(A) z| / ln 2 <= 126, and past it the
+    saturated values (g_min exactly on one side, |g| < 2^-123 on the other)."""
+    gen = torch.Generator("cpu").manual_seed(8)
+    H, dk = 4, 128
+    A = torch.randn((H, dk), generator=gen) * 0.5
+    A[0] = 0.0
+    z = torch.randn((2, 300, H, dk), generator=gen) * 30
+    z[0, 0, 0] = float(np.log(3.0))                     # A = 0: g = -5 * 3/4 = -3.75
+    ref = oracle.gate(A, z)
+    g = K.kda_gate(A.to(DEV), z.to(DEV), g_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = g.double().cpu().numpy()
+    arg2 = np.exp(A.double().numpy()) * z.double().numpy() / np.log(2.0)
+    inr = np.abs(arg2) <= 126
+    assert inr.mean() > 0.9 and (~inr).sum() > 1000
+    e = ulp_err(got, ref)
+    assert e[inr].max() <= GATE_ULP, e[inr].max()
+    assert abs(got[0, 0, 0, 0] + 3.75) <= 4e-7
+    hi, lo = arg2 > 126, arg2 < -126
+    assert np.all(got[hi] == -5.0)
+    assert np.all((got[lo] <= 0.0) & (got[lo] > -(2.0 ** -123)))
 
 
 def test_gate_full_size_sampled():
@@ -48,7 +82,7 @@ def test_gate_full_size_sampled():
     rows = torch.randint(0, cfg.T, (512,), generator=gen)
     ref = oracle.gate(A, z[0, rows])
     got = g[0, rows.to(DEV)].double().cpu().numpy()
-    assert np.abs(got - ref).max() <= 2e-6
+    assert ulp_err(got, ref).max() <= GATE_ULP
 
 
 def _decode_run(cfg, steps, o_dtype=torch.float32, n_check=None):
