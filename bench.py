@@ -108,8 +108,7 @@ def mfma_executed(summary: str, call_ms: float):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("source_sha256") != source_digest("kda_chunk.hip", "kda_common.hpp",
-                                                 "kda_internal.hpp"):
+    if rec.get("source_sha256") != chunk_digest():
         return None
     flop = float(rec["flop_per_call"])
     return {"flop_per_call": flop, "tflops": round(flop / (call_ms * 1e-3) / 1e12, 2),
@@ -301,7 +300,9 @@ def prefill_leg(name, K, inputs, dev, stream, reps, traffic_summary=None, label=
 
 
 def chunk_digest():
-    return source_digest("kda_chunk.hip", "kda_common.hpp", "kda_internal.hpp")
+    """The prefill kernels' sources: both prefill paths, their shared helpers and the gate."""
+    return source_digest("kda_chunk.hip", "kda_fused.hip", "kda_chunk_util.hpp", "kda_common.hpp",
+                         "kda_internal.hpp")
 
 
 def cpu_baseline(args, d, lens):

@@ -825,6 +825,7 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
 // Long sequences in the two-kernel path: segments of 2^SEG_SHIFT tokens (kda_chunk_util.hpp).
 constexpr int SEG_SHIFT = 13;
 constexpr int64_t SEG_TOK = int64_t(1) << SEG_SHIFT;
+constexpr int SEG_MAX_SEQS = 128;   // segmented launches have at most 128 sequences (use_segments)
 
 // MODE 0: whole sequences.  MODE 1: segment pass 1.  MODE 2: segment pass 2.
 template <int DK, int IDT, int ODT, bool PRECISE, int NW, bool CKPT, int MODE>
@@ -878,8 +879,17 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
         if (!locate_seg(p, sg, unit / H, n, seg)) return;
         seg_slot = unit / H;
     } else if constexpr (MODE == 2) {
-        // every segment of the batch runs here, longest first
-        if (!locate_seg_lpt(p, sg, unit / H, n, seg, seg_slot)) return;
+        // every segment of the batch runs here, longest first: the full segments, then the
+        // sequences' last segments by decreasing length (ranked only by the workgroups that run
+        // one of those)
+        __shared__ int last_order[SEG_MAX_SEQS];
+        const int* order = nullptr;
+        if (p.cu && p.n_seqs <= SEG_MAX_SEQS && p.n_seqs <= static_cast<int>(blockDim.x) &&
+            unit / H >= full_seg_count(p, sg)) {
+            rank_last_segments(p, sg, last_order);
+            order = last_order;
+        }
+        if (!locate_seg_lpt(p, sg, unit / H, n, seg, seg_slot, order)) return;
     }
     const int DV = p.dv;
     const int32_t vstride = static_cast<int32_t>(H) * DV;

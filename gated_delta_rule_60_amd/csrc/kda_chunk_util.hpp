@@ -160,12 +160,48 @@ __device__ __forceinline__ bool locate_seg(const ChunkArgs& p, const SegArgs& sg
     return n < p.n_seqs;
 }
 
+// Length of sequence m's last segment (0 for an empty sequence).
+__device__ __forceinline__ int64_t last_seg_len(const ChunkArgs& p, const SegArgs& sg, int m) {
+    int64_t bos, end;
+    seq_bounds(p, m, bos, end);
+    const int64_t len = end - bos;
+    return len - ((seg_count(len, sg.seg_shift) - 1) << sg.seg_shift);
+}
+// Number of segments of a packed batch that are not their sequence's last (all 2^seg_shift tokens).
+__device__ __forceinline__ int64_t full_seg_count(const ChunkArgs& p, const SegArgs& sg) {
+    int64_t acc = 0;
+    for (int m = 0; m < p.n_seqs; ++m) {
+        int64_t bos, end;
+        seq_bounds(p, m, bos, end);
+        acc += seg_count(end - bos, sg.seg_shift) - 1;
+    }
+    return acc;
+}
+// The sequences of a packed batch ranked by the length of their last segment, longest first
+// (ties in sequence order): order[r] is the sequence of rank r.  Thread t ranks sequence t, so
+// the workgroup must have at least n_seqs threads; every thread calls this (it ends in a barrier).
+__device__ __forceinline__ void rank_last_segments(const ChunkArgs& p, const SegArgs& sg, int* order) {
+    const int t = static_cast<int>(threadIdx.x);
+    if (t < p.n_seqs) {
+        const int64_t lt = last_seg_len(p, sg, t);
+        int r = 0;
+        for (int j = 0; j < p.n_seqs; ++j) {
+            const int64_t lj = last_seg_len(p, sg, j);
+            r += (lj > lt) || (lj == lt && j < t);
+        }
+        order[r] = t;
+    }
+    __syncthreads();
+}
+
 // Work index k -> sequence n, segment s and its slot, ordered longest first: every sequence's
-// segments but its last (all 2^seg_shift tokens), then the last segments (the partial ones), so
-// that a launch with more workgroups than CUs ends on its shortest ones.  Linear in the number of
-// sequences for packed batches (a segmented launch has at most 64 (sequence, head) units).
+// segments but its last (all 2^seg_shift tokens), then the last segments (the partial ones) by
+// decreasing length when `order` ranks them (rank_last_segments), else in sequence order, so that
+// a launch with more workgroups than CUs ends on its shortest ones.  Linear in the number of
+// sequences for packed batches (a segmented launch has at most 128 (sequence, head) units).
 __device__ __forceinline__ bool locate_seg_lpt(const ChunkArgs& p, const SegArgs& sg, int64_t k,
-                                               int& n, int64_t& s, int64_t& slot) {
+                                               int& n, int64_t& s, int64_t& slot,
+                                               const int* order = nullptr) {
     const int sh = sg.seg_shift;
     if (!p.cu) {
         const int64_t per = seg_count(p.T, sh), full = static_cast<int64_t>(p.n_seqs) * (per - 1);
@@ -194,7 +230,7 @@ __device__ __forceinline__ bool locate_seg_lpt(const ChunkArgs& p, const SegArgs
         acc += cnt;
     }
     if (k - acc >= p.n_seqs) return false;
-    n = static_cast<int>(k - acc);
+    n = order ? order[k - acc] : static_cast<int>(k - acc);
     int64_t bos, end;
     seq_bounds(p, n, bos, end);
     s = seg_count(end - bos, sh) - 1;
