@@ -10,8 +10,9 @@ before the timed region starts.
 
 The other workloads are timed in the same run, each with its own roofline: the bf16 prefill
 workload (B=4, H=16, T=4096) under "prefill_bf16" (with the separate kda_gate + kda_chunk_fwd
-pair under "unfused"), the long workload (1 x 65536 tokens, 32 heads) under "long_prefill", the
-decode workload (256 sequences x 32 heads, 64 in-place steps, plus speculative-decode verify and
+pair under "unfused"), the same workload at B=16 (256 (sequence, head) units: the whole-sequence
+fused kernel, no workspace) under "prefill_bf16_b16_fused", the long workload (1 x 65536 tokens,
+32 heads) under "long_prefill", the decode workload (256 sequences x 32 heads, 64 in-place steps, plus speculative-decode verify and
 commit) under "decode".
 
 Prints ONE JSON line.  ``value`` is prefill tokens/s (tokens per step / wall-clock step time
@@ -62,7 +63,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the long-sequence prefill leg")
     ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--mode", choices=("all", "packed", "prefill", "long", "decode"),
+    ap.add_argument("--mode", choices=("all", "packed", "prefill", "fused", "long", "decode"),
                     default="all",
                     help="packed (the headline workload) / prefill / long / decode: run only that "
                          "workload and print no JSON line (for profiler passes)")
@@ -223,9 +224,9 @@ def _median(xs):
     return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
 
 
-def load_prefill(name, inputs, dev, keep_host=False):
+def load_prefill(name, inputs, dev, keep_host=False, overrides=None):
     """Device copies of a prefill workload's inputs (and, when asked, the host tensors)."""
-    cfg = inputs.config(name)
+    cfg = inputs.config(name, **(overrides or {}))
     log("generating", cfg)
     d = inputs.make_prefill(cfg)
     w = {x: d[x].to(dev) for x in ("q", "k", "v", "beta", "z", "A", "S0")}
@@ -272,10 +273,10 @@ def prefill_alg_bytes(w):
     return th * FUSED_BYTES_PER_TH + cfg.H * cfg.dk * 4 + 2 * w["N"] * cfg.H * STATE_BYTES
 
 
-def prefill_leg(name, K, inputs, dev, stream, reps, traffic_summary=None, label=""):
+def prefill_leg(name, K, inputs, dev, stream, reps, traffic_summary=None, label="", overrides=None):
     """A prefill workload other than the headline one: kda_chunk_fwd_gated timed with HIP events
     over `reps` calls after one untimed call; its own HBM roofline."""
-    w, _ = load_prefill(name, inputs, dev)
+    w, _ = load_prefill(name, inputs, dev, overrides=overrides)
     o, hT, ws = prefill_buffers(K, w, dev)
     call = gated_call(K, w, stream, o, hT, ws)
     call()
@@ -368,10 +369,12 @@ def main():
         r = run_decode(args, dev, inputs, K, stream)
         log(f"decode: {r['ms_per_step']:.4f} ms/step; spec decode {r['spec_decode']}")
         return
-    if args.mode in ("prefill", "long"):
-        name = "prefill_bf16" if args.mode == "prefill" else "prefill_long"
-        r, _ = prefill_leg(name, K, inputs, dev, stream, args.steps)
-        log(f"{name}: {r['ms_per_call']:.4f} ms/call (median {r['ms_per_call_median']:.4f})")
+    if args.mode in ("prefill", "fused", "long"):
+        name = "prefill_long" if args.mode == "long" else "prefill_bf16"
+        r, _ = prefill_leg(name, K, inputs, dev, stream, args.steps,
+                           overrides={"B": 16} if args.mode == "fused" else None)
+        log(f"{args.mode} ({name}): {r['ms_per_call']:.4f} ms/call "
+            f"(median {r['ms_per_call_median']:.4f})")
         return
 
     # ------------------------------------------------------------------ headline: packed workload
@@ -440,6 +443,14 @@ def main():
                        "tokens_per_s": round(w1["B"] * w1["T"] / ((gate_ms + chunk_ms) * 1e-3), 1)}
     del w1, o1, h1, ws1, g1
     torch.cuda.empty_cache()
+    # 256 (sequence, head) units: the whole-sequence fused kernel (no workspace round trip)
+    leg16, bufs = prefill_leg("prefill_bf16", K, inputs, dev, stream, max(args.steps, 20),
+                              traffic_summary="chunk_fwd_gated_fused_B16_H16_T4096.md",
+                              label="B=16 H=16 T=4096 d_k=d_v=128, bf16, random initial states, "
+                                    "gate fused: the whole-sequence fused kernel",
+                              overrides={"B": 16})
+    del bufs
+    torch.cuda.empty_cache()
     long_ = None
     if not args.no_long:
         long_, bufs = prefill_leg("prefill_long", K, inputs, dev, stream, max(args.steps, 20),
@@ -485,6 +496,7 @@ def main():
                  "frac_bf16_peak": round(flop / (call_ms * 1e-3) / BF16_PEAK, 4),
                  "executed": mfma_executed("chunk_fwd_gated_varlen_8seq_1M_H8.md", call_ms)},
         "prefill_bf16": leg1,
+        "prefill_bf16_b16_fused": leg16,
         "long_prefill": long_,
         "decode": dec,
         "copy_ceiling_gbs": round(copy_bps / 1e9, 1),
