@@ -451,8 +451,10 @@ def test_checkpoints_full_size_sampled():
 
 # ---- long sequences split into 8192-token segments ----------------------------------------------
 # A launch is segmented when its state pass would use at most 128 column blocks of 64 state
-# columns and sequences average 16384 tokens or more: pass 1 (segment 0 and the middle segments'
-# (M, B) pairs), the scan of the pairs, pass 2.  These shapes are segmented; every unit is checked.
+# columns and sequences average 16384 tokens or more: pass 1 (the (M, B) pairs of every segment
+# but each sequence's last; at d_k != d_v segment 0 from the initial state and the middle
+# segments' pairs), the scan of the pairs, pass 2 (longest segments first).  These shapes are
+# segmented; every unit is checked.
 @pytest.mark.parametrize("T", [2 * 8192, 2 * 8192 + 64, 3 * 8192 + 100, 4 * 8192 - 17])
 def test_segmented_prefill_lengths(T):
     """Two segments (no middle one), a one-chunk last segment, a ragged last segment, four
@@ -471,6 +473,16 @@ def test_segmented_prefill_batch_and_packed():
     d = prefill_case("prefill_varlen", seqlens=lens, H=2)
     say("segmented prefill, packed", lens)
     check_full(d, oracle_g(d), TOL["bf16"], label="seg packed")
+
+
+def test_segmented_prefill_packed_equal_last_segments():
+    """Pass 2 runs the sequences' last segments by decreasing length: a packed batch whose last
+    segments tie (16 tokens twice, 200 tokens twice) next to a full one, a long one and an empty
+    sequence."""
+    lens = [16400, 200, 24592, 0, 200, 3 * 8192, 60000]
+    d = prefill_case("prefill_varlen", seqlens=lens, H=2)
+    say("segmented prefill, packed, tied last segments", lens)
+    check_full(d, oracle_g(d), TOL["bf16"], label="seg packed ties")
 
 
 def test_segmented_prefill_mild_decay():
