@@ -28,19 +28,23 @@
 //
 // 1. Intra-block kernel (everything that does not depend on S; fully parallel): writes one
 //    record per (head, record slot) to the workspace -- Kt, Qt, Kb^T in their MFMA formats,
-//    T', P, the step's e^{G_last} - 1.
+//    the diagonal blocks of T', the cross tile -C, P, the step's e^{G_last} - 1.
 //    16-bit inputs (chunk_intra_tok_kernel): one wave per (32-token record, head); each lane
 //    owns one token of each 16-token sub-block and the channels of its record unit; inputs
 //    arrive by direct-to-LDS loads, the cumsums are DPP scans across the lanes, A and P are fp32
-//    MFMAs fed from registers, T' by substitution and one block-triangular product.
+//    MFMAs fed from registers, the diagonal blocks of T' come by substitution; the off-diagonal
+//    block T'_10 = -T'_11 C T'_00 is left to the state pass, which applies it as two products.
 //    fp32 inputs (chunk_intra_kernel, split-bf16 records of 16 tokens): each lane owns 4 tokens
 //    x 4 channels; quad-lane cumsum, A and P on MFMA from split-bf16 operands staged in LDS.
-// 2. State-passing kernel (the sequential part): one 256-lane workgroup per (sequence, head,
-//    64 state columns); each wave owns 16 state columns in fp32 accumulators for the whole
-//    sequence.  A chunk's two records and its V rows stream into double-buffered LDS while the
-//    previous chunk is processed.  Optionally it stores the state every k tokens (checkpoints).
-//    Long sequences with few (sequence, head) units run it as segment passes around a scan of
-//    the segments' affine pairs (see the segment section below).
+// 2. State-passing kernel (the sequential part): one workgroup of STATE_WAVES waves per
+//    (sequence, head, 16 STATE_WAVES state columns); each wave owns 16 state columns in fp32
+//    accumulators for the whole sequence.  A chunk's two records and its V rows stream into
+//    double-buffered LDS while the previous chunk is processed.  Optionally it stores the state
+//    every k tokens (checkpoints).  Long sequences with few (sequence, head) units run as
+//    segments: pass 1 (the segments' affine pairs; chunk_pair_kernel at d_k = d_v = 128), a scan
+//    of the pairs, pass 2 (see the segment section below).
+// Launches with 16-bit inputs at d_k = d_v = 128 and at least 256 (sequence, head) units run the
+// single fused kernel of kda_fused.hip instead, with no workspace.
 // Precision (16-bit inputs): A and P of each 16-token block are fp32 products; every operand of
 // the state pass is range-bounded and runs in fp16 (11-bit significand) with fp32 accumulation.
 // For fp32 inputs every product is split bf16 (hi*hi + hi*lo + lo*hi).
@@ -1437,7 +1441,9 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
 }
 
 // Segment scan: one workgroup per (sequence, head, 16 state columns) walks the sequence's
-// segments, S_start(s + 1) = M_s S_start(s) + B_s for s = 1 .. nseg - 2, in fp32.  The column
+// segments, S_start(s + 1) = M_s S_start(s) + B_s for s = s0 .. nseg - 2, in fp32: s0 = 0 from
+// the initial state when pass 1 made segment 0 a pair too (from0), else s0 = 1 from segment 1's
+// start state, which pass 1 wrote after running segment 0 whole.  The column
 // blocks are independent (M acts on the rows), so they run apart.  Each step is a d_k x d_k by
 // d_k x 16 product on fp32 MFMAs (16x16x4): wave w owns output row tiles w, w + 4, ..., B_s seeds
 // the accumulators, S_start(s) is read from LDS (double-buffered, one barrier per step), and the
