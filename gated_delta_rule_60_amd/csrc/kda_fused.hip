@@ -526,7 +526,8 @@ __device__ __forceinline__ void consumer_loop(const FCtx& c, const FUnit& u, Fus
         for (int i = 0; i < 4; ++i) w1[i] = static_cast<_Float16>(W1[i]);
         const f16x8 wx = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
         {
-            // O += P W (P and Qt carry the output scale); o rows of this record.  O_1 += [P_10 P_11]
+            // O += P W (P and Qt carry the output scale); o rows of this record, stored with the
+            // default cache policy so that the waves' partial lines merge in L2.  O_1 += [P_10 P_11]
             // [W_0; W_1] is one K = 32 product: a lane's k slots pair its W_0 and W_1 rows with the
             // same columns of P_10 and P_11.
             const f16x4 p00 = *reinterpret_cast<const f16x4*>(rc + F_OFF_P + 8 * lane);
@@ -542,14 +543,14 @@ __device__ __forceinline__ void consumer_loop(const FCtx& c, const FUnit& u, Fus
             if (o32) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[i]), orr, ooff[i], 0, CP_NT);
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[i]), orr, ooff[4 + i], 0, CP_NT);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[i]), orr, ooff[i], 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[i]), orr, ooff[4 + i], 0, 0);
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O0[i]), orr, ooff[i], 0, CP_NT);
-                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O1[i]), orr, ooff[4 + i], 0, CP_NT);
+                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O0[i]), orr, ooff[i], 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O1[i]), orr, ooff[4 + i], 0, 0);
                 }
             }
         }
