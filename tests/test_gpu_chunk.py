@@ -485,6 +485,16 @@ def test_segmented_prefill_packed_equal_last_segments():
     check_full(d, oracle_g(d), TOL["bf16"], label="seg packed ties")
 
 
+def test_segmented_prefill_most_sequences():
+    """The most sequences a segmented launch takes (128 (sequence, head, 64-column) units at
+    d_k = d_v = 64, one head), lengths spread around 16 K tokens so that every last segment
+    differs: pass 2 ranks 128 last segments."""
+    lens = [16400 + (37 * i) % 2000 for i in range(128)]
+    d = prefill_case("prefill_varlen", seqlens=lens, H=1, dk=64, dv=64)
+    say("segmented prefill, 128 packed sequences", sum(lens))
+    check_full(d, oracle_g(d), TOL["bf16"], label="seg 128 seqs")
+
+
 def test_segmented_prefill_mild_decay():
     """Gates scaled down 20x (mean decay about e^-0.125 per token): every channel carries state
     across segment boundaries, so each segment's transition M is far from 0 and the pair scan
