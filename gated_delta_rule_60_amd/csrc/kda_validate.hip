@@ -6,8 +6,8 @@
 // decay factors inside the floating range ([habr] "Как устроена Kimi K3: …", § "Последовательность:
 // три KDA на один глобальный MLA") -- and a packed batch's cu_seqlens start at 0, never decrease
 // and end at the token count.  With the check on, a call first runs small kernels that test them,
-// waits for the verdict (a host synchronisation on the caller's stream) and reports a violation
-// as KDA_ERR_INVALID_ARGUMENT before any other work is enqueued.  The verdict lives in one word
+// waits for their result (a host synchronisation on the caller's stream) and reports a violation
+// as KDA_ERR_INVALID_ARGUMENT before any other work is enqueued.  The result lives in one word
 // of library-owned device memory; calls that overlap on one device share it.  Not for use under
 // stream capture.
 #include <stdlib.h>

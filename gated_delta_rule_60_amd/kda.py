@@ -36,7 +36,7 @@ def load_library(path: Optional[str] = None):
     path = path or lib_path()
     if not os.path.exists(path):
         raise RuntimeError(f"libkda.so not found at {path}; build it first "
-                           "(python -m gated_delta_rule_60_amd.build or __graft_entry__.build())")
+                           "(python -m gated_delta_rule_60_amd.build)")
     lib = ctypes.CDLL(path)
     vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                              ctypes.c_size_t)
