@@ -1453,7 +1453,7 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
 // blocks are independent (M acts on the rows), so they run apart.  Each step is a d_k x d_k by
 // d_k x 16 product on fp32 MFMAs (16x16x4): wave w owns output row tiles w, w + 4, ..., B_s seeds
 // the accumulators, S_start(s) is read from LDS (double-buffered, one barrier per step), and the
-// next step's M rows and B are loaded into registers while the current step computes.
+// M rows and B of the step after next are loaded into registers while the current step computes.
 // MFMA step (m, e) of a tile contracts over the four columns 16 m + 4 c + e, c = 0..3: lane
 // (i, c) supplies M[row i][16 m + 4 c + e] from its float4 of M[row i][16 m + 4 c .. + 3], and
 // S_start[16 m + 4 c + e][j] for lane (j, c) comes from LDS.
@@ -1466,8 +1466,13 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
     __shared__ float sS[2][DK * SP];
     const int DV = p.dv, ncb = DV / 16;
     const int64_t H = p.H;
-    const int cb = static_cast<int>(blockIdx.x % ncb);
-    const int64_t useq = blockIdx.x / ncb;
+    // Workgroup -> (sequence, head) and column block: the column blocks of one (sequence, head)
+    // sit 8 workgroup ids apart, so they land on one XCD and read each M_s from HBM once, the
+    // others from that XCD's L2.
+    const int64_t grp = blockIdx.x / (8 * ncb), rem = blockIdx.x % (8 * ncb);
+    const int cb = static_cast<int>(rem / 8);
+    const int64_t useq = grp * 8 + rem % 8;
+    if (useq >= static_cast<int64_t>(p.n_seqs) * H) return;
     const int n = static_cast<int>(useq / H), h = static_cast<int>(useq % H);
     int64_t len, slot0;
     if (p.cu) {
@@ -1488,9 +1493,11 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
     auto m_of = [&](int64_t s) { return sg.M + ((slot0 + s) * H + h) * DK * DK; };
     auto b_of = [&](int64_t s) { return sg.B + ((slot0 + s) * H + h) * DK * DV + cb * 16; };
 
-    float4 mr[TPW][NM];                               // this lane's M values of the wave's tiles
-    f32x4 br[TPW];                                    // B seeds: rows 16 r + 4 lc + v, column li
-    auto load_step = [&](int64_t s) {
+    // this lane's M values of the wave's tiles and B seeds (rows 16 r + 4 lc + v, column li), for
+    // two steps: the loads run two steps ahead of the products
+    float4 mrA[TPW][NM], mrB[TPW][NM];
+    f32x4 brA[TPW], brB[TPW];
+    auto load_step = [&](int64_t s, float4 (&mr)[TPW][NM], f32x4 (&br)[TPW]) {
         const float* M = m_of(s);
         const float* Bm = b_of(s);
 #pragma unroll
@@ -1509,10 +1516,13 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
                                    : sg.S + ((slot0 + 1) * H + h) * DK * DV + cb * 16;
         for (int e = t; e < DK * 16; e += 256) sS[0][(e >> 4) * SP + (e & 15)] = S1 ? S1[(e >> 4) * DV + (e & 15)] : 0.f;
     }
-    load_step(s_first);
+    load_step(s_first, mrA, brA);
+    if (s_first + 2 < nseg) load_step(s_first + 1, mrB, brB);
     __syncthreads();
     int cur = 0;
-    for (int64_t s = s_first; s + 1 < nseg; ++s) {
+    // one step: S_start(s + 1) = M_s S_start(s) + B_s from the registers of slot (mr, br), which
+    // then receive step s + 2
+    auto step = [&](int64_t s, float4 (&mr)[TPW][NM], f32x4 (&br)[TPW]) __attribute__((always_inline)) {
         f32x4 acc[TPW];
         float4 mc[TPW][NM];
 #pragma unroll
@@ -1521,7 +1531,7 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
 #pragma unroll
             for (int m = 0; m < NM; ++m) mc[q][m] = mr[q][m];
         }
-        if (s + 2 < nseg) load_step(s + 1);          // in flight during this step
+        if (s + 3 < nseg) load_step(s + 2, mr, br);  // in flight during the next two steps
         const float* Sc = sS[cur];
 #pragma unroll
         for (int m = 0; m < NM; ++m)
@@ -1549,6 +1559,11 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
         }
         __syncthreads();                             // S_start(s + 1) complete in LDS
         cur ^= 1;
+    };
+    for (int64_t s = s_first; s + 1 < nseg; s += 2) {
+        step(s, mrA, brA);
+        if (s + 2 >= nseg) break;
+        step(s + 1, mrB, brB);
     }
 }
 
@@ -1667,7 +1682,8 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((seg_scan_kernel<DK>), dim3(static_cast<unsigned>(static_cast<int64_t>(a.n_seqs) * a.H * (a.dv / 16))),
+    hipLaunchKernelGGL((seg_scan_kernel<DK>),
+                       dim3(static_cast<unsigned>((static_cast<int64_t>(a.n_seqs) * a.H + 7) / 8 * 8 * (a.dv / 16))),
                        dim3(256), 0, stream, a, sg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
