@@ -135,6 +135,30 @@ def test_fused_whole_packed_and_gated():
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
+def test_fused_whole_input_and_output_dtypes():
+    """The fused kernel's other variants: g given in bf16, z given in fp32 through the fused gate,
+    and bf16 o, which must be the RNE rounding of the fp32 o; two runs agree bit for bit."""
+    d = prefill_case("prefill_bf16", B=64, H=4, T=100)
+    say("fused whole dtypes")
+    h0 = d["S0"].to(DEV)
+    qkvb = [d[x].to(DEV) for x in ("q", "k", "v", "beta")]
+    g = oracle_g(d, torch.bfloat16)
+    o1, h1 = K.kda_chunk_fwd(*qkvb, g.to(DEV), initial_state=h0, o_dtype=torch.float32)
+    o2, h2 = K.kda_chunk_fwd(*qkvb, g.to(DEV), initial_state=h0, o_dtype=torch.float32)
+    o3, h3 = K.kda_chunk_fwd(*qkvb, g.to(DEV), initial_state=h0, o_dtype=torch.bfloat16)
+    z32 = d["z"].to(torch.float32)
+    o4, h4 = K.kda_chunk_fwd_gated(*qkvb, d["A"].to(DEV), z32.to(DEV), initial_state=h0,
+                                   o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    assert torch.equal(o3, o1.to(torch.bfloat16)) and torch.equal(h3, h1)
+    for (o, hT), g_ref, lab in (((o1, h1), g, "g bf16"), ((o4, h4), oracle.gate(d["A"], z32), "z f32")):
+        o_ref, S_ref, _ = oracle.forward(d["q"], d["k"], d["v"], d["beta"], g_ref, S0=d["S0"])
+        eo, es = rel_err(o, o_ref), rel_err(hT, S_ref)
+        say(f"  fused whole {lab}: o err {eo:.2e}  S err {es:.2e}")
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("gmode", ["floor", "one"])
 def test_prefill_gate_extremes(gmode):
     """g = -5 in every channel (the decay floor: diagonal-block factors reach e^80) and g = 0
