@@ -255,8 +255,15 @@ def prefill_buffers(K, w, dev):
 
 
 def time_calls(call, stream, reps):
-    """`reps` calls back to back with an event between consecutive calls (HIP events on the
-    launch stream): (mean, median) ms per call."""
+    """(mean, median) ms per call, HIP events on the launch stream: the mean over `reps` calls
+    back to back between two events, the median over another `reps` calls with an event between
+    consecutive calls (whose own cost the mean leaves out)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    e1.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     evs[0].record(stream)
     for i in range(reps):
@@ -264,7 +271,7 @@ def time_calls(call, stream, reps):
         evs[i + 1].record(stream)
     evs[-1].synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
-    return evs[0].elapsed_time(evs[-1]) / reps, _median(per)
+    return e0.elapsed_time(e1) / reps, _median(per)
 
 
 def prefill_alg_bytes(w):
