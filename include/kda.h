@@ -92,7 +92,10 @@ int kda_gate(const float *A, const void *z, int z_dtype, void *g, int g_dtype, i
  * first computes, for every (head, 32-token record; 16 tokens for fp32 inputs), everything that
  * does not depend on the state and writes it to the workspace; the second passes the state
  * along each sequence reading it.  At d_k = 128 a record is 27.5 KiB for bf16 inputs (880 bytes
- * per token and head) and 26.5 KiB for fp32 inputs (16 tokens).
+ * per token and head) and 26.5 KiB for fp32 inputs (16 tokens).  Long sequences with few
+ * (sequence, head) units also need per-segment state buffers.  Batches of bf16 inputs at
+ * d_k = d_v = 128 with n_seqs * H >= 256 run one fused kernel that builds the records on chip:
+ * their size is 0 (a NULL workspace is accepted).
  * Never fails; returns 0 for invalid sizes (kda_chunk_fwd then reports the error).
  */
 size_t kda_chunk_fwd_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
