@@ -1514,7 +1514,19 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
         // S_start(s_first): the initial state (zeros when absent) or segment 1's start from pass 1
         const float* S1 = sg.from0 ? (p.h0 ? p.h0 + useq * DK * DV + cb * 16 : nullptr)
                                    : sg.S + ((slot0 + 1) * H + h) * DK * DV + cb * 16;
-        for (int e = t; e < DK * 16; e += 256) sS[0][(e >> 4) * SP + (e & 15)] = S1 ? S1[(e >> 4) * DV + (e & 15)] : 0.f;
+        // every load first, then the LDS stores: one wait for all of them
+        constexpr int PER = DK * 16 / 256;
+        float s1v[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = t + 256 * i;
+            s1v[i] = S1 ? S1[(e >> 4) * DV + (e & 15)] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = t + 256 * i;
+            sS[0][(e >> 4) * SP + (e & 15)] = s1v[i];
+        }
     }
     load_step(s_first, mrA, brA);
     if (s_first + 2 < nseg) load_step(s_first + 1, mrB, brB);
@@ -1532,12 +1544,19 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
             for (int m = 0; m < NM; ++m) mc[q][m] = mr[q][m];
         }
         if (s + 3 < nseg) load_step(s + 2, mr, br);  // in flight during the next two steps
+        // this lane's S_start(s) operands, all read from LDS before the products (one wait)
         const float* Sc = sS[cur];
+        float sv[NM][4];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[m][e] = Sc[(16 * m + 4 * lc + e) * SP + li];
+        wave_fence();
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float sb = Sc[(16 * m + 4 * lc + e) * SP + li];
+                const float sb = sv[m][e];
 #pragma unroll
                 for (int q = 0; q < TPW; ++q) {
                     const float4& a4 = mc[q][m];
