@@ -1451,16 +1451,19 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
 // the initial state when pass 1 made segment 0 a pair too (from0), else s0 = 1 from segment 1's
 // start state, which pass 1 wrote after running segment 0 whole.  The column
 // blocks are independent (M acts on the rows), so they run apart.  Each step is a d_k x d_k by
-// d_k x 16 product on fp32 MFMAs (16x16x4): wave w owns output row tiles w, w + 4, ..., B_s seeds
+// d_k x 16 product on fp32 MFMAs (16x16x4): wave w owns output row tile w (d_k / 16 waves), B_s seeds
 // the accumulators, S_start(s) is read from LDS (double-buffered, one barrier per step), and the
 // M rows and B of the step after next are loaded into registers while the current step computes.
 // MFMA step (m, e) of a tile contracts over the four columns 16 m + 4 c + e, c = 0..3: lane
 // (i, c) supplies M[row i][16 m + 4 c + e] from its float4 of M[row i][16 m + 4 c .. + 3], and
 // S_start[16 m + 4 c + e][j] for lane (j, c) comes from LDS.
+constexpr int scan_waves(int dk) { return dk / 16; }   // one 16-row tile of the output per wave
 template <int DK>
-__global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) {
+__global__ void __launch_bounds__(64 * scan_waves(DK)) seg_scan_kernel(ChunkArgs p, SegArgs sg) {
     constexpr int NT = DK / 16;                      // row tiles
-    constexpr int TPW = NT / 4;                      // row tiles per wave
+    constexpr int NWS = scan_waves(DK);
+    constexpr int TPW = NT / NWS;                    // row tiles per wave
+    constexpr int NTH = 64 * NWS;
     constexpr int NM = DK / 16;                      // float4s of one M row a lane holds
     constexpr int SP = 17;                           // LDS row pitch of S_start (floats)
     __shared__ float sS[2][DK * SP];
@@ -1502,7 +1505,7 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
         const float* Bm = b_of(s);
 #pragma unroll
         for (int q = 0; q < TPW; ++q) {
-            const int r = wave + 4 * q;
+            const int r = wave + NWS * q;
 #pragma unroll
             for (int m = 0; m < NM; ++m)
                 mr[q][m] = *reinterpret_cast<const float4*>(M + (16 * r + li) * DK + 16 * m + 4 * lc);
@@ -1515,16 +1518,16 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
         const float* S1 = sg.from0 ? (p.h0 ? p.h0 + useq * DK * DV + cb * 16 : nullptr)
                                    : sg.S + ((slot0 + 1) * H + h) * DK * DV + cb * 16;
         // every load first, then the LDS stores: one wait for all of them
-        constexpr int PER = DK * 16 / 256;
+        constexpr int PER = DK * 16 / NTH;
         float s1v[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int e = t + 256 * i;
+            const int e = t + NTH * i;
             s1v[i] = S1 ? S1[(e >> 4) * DV + (e & 15)] : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int e = t + 256 * i;
+            const int e = t + NTH * i;
             sS[0][(e >> 4) * SP + (e & 15)] = s1v[i];
         }
     }
@@ -1568,7 +1571,7 @@ __global__ void __launch_bounds__(256) seg_scan_kernel(ChunkArgs p, SegArgs sg) 
         float* Sn = sS[cur ^ 1];
 #pragma unroll
         for (int q = 0; q < TPW; ++q) {
-            const int r = wave + 4 * q;
+            const int r = wave + NWS * q;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int row = 16 * r + 4 * lc + v;
@@ -1703,7 +1706,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((seg_scan_kernel<DK>),
                        dim3(static_cast<unsigned>((static_cast<int64_t>(a.n_seqs) * a.H + 7) / 8 * 8 * (a.dv / 16))),
-                       dim3(256), 0, stream, a, sg);
+                       dim3(64 * scan_waves(DK)), 0, stream, a, sg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (wide)
