@@ -1536,17 +1536,12 @@ __global__ void __launch_bounds__(64 * scan_waves(DK)) seg_scan_kernel(ChunkArgs
     __syncthreads();
     int cur = 0;
     // one step: S_start(s + 1) = M_s S_start(s) + B_s from the registers of slot (mr, br), which
-    // then receive step s + 2
+    // then receive step s + 2 (in flight during the next step)
     auto step = [&](int64_t s, float4 (&mr)[TPW][NM], f32x4 (&br)[TPW]) __attribute__((always_inline)) {
         f32x4 acc[TPW];
-        float4 mc[TPW][NM];
 #pragma unroll
-        for (int q = 0; q < TPW; ++q) {
-            acc[q] = br[q];
-#pragma unroll
-            for (int m = 0; m < NM; ++m) mc[q][m] = mr[q][m];
-        }
-        if (s + 3 < nseg) load_step(s + 2, mr, br);  // in flight during the next two steps
+        for (int q = 0; q < TPW; ++q) acc[q] = br[q];
+        const float4 (&mc)[TPW][NM] = mr;
         // this lane's S_start(s) operands, all read from LDS before the products (one wait)
         const float* Sc = sS[cur];
         float sv[NM][4];
@@ -1567,6 +1562,7 @@ __global__ void __launch_bounds__(64 * scan_waves(DK)) seg_scan_kernel(ChunkArgs
                     acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, sb, acc[q], 0, 0, 0);
                 }
             }
+        if (s + 3 < nseg) load_step(s + 2, mr, br);  // the slot's operands are consumed
         float* dst = sg.S + ((slot0 + s + 1) * H + h) * DK * DV + cb * 16;
         float* Sn = sS[cur ^ 1];
 #pragma unroll
