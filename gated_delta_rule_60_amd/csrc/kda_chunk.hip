@@ -90,10 +90,13 @@ constexpr int QP_LAST = 3 | (3 << 2) | (3 << 4) | (3 << 6);    // [3,3,3,3]
 // Record of one (head, block slot) in the workspace (byte offsets).  E = 16 * DK elements per
 // array.  A fast record covers 32 tokens: two 16-token sub-blocks, one 32-token state step; a
 // precise record covers one 16-token block.
-//   fast   : per sub-block s = 0, 1: [Kt fp16 frag32][Qt fp16 frag32][Kb^T fp16 frag16]; then
-//            T'_00, -C, T'_11 and P_00, P_10, P_11 (fp16 fragT, [row sub-block][column
-//            sub-block]); then e^{G_31} - 1 (DK fp32).  Kt, Qt are scaled from the record's first
-//            token, Kb from its last, so every exponent is <= 0.
+//   fast   : six fp16 [16][DK] arrays: [-Kt_0 frag32][Qt_0 frag32][Kb^T][-Kt_1][Qt_1][Kb^T], the
+//            two Kb^T arrays holding Kb^T of both sub-blocks in fragKb order (tiles 0 .. DK/32 - 1
+//            in the first, the rest in the second); then T'_00, -C, T'_11 and P_00, P_10, P_11
+//            (fp16 fragT, [row sub-block][column sub-block]); then e^{G_31} - 1 (DK fp32).  Kt,
+//            Qt are scaled from the record's first token, Kb from its last, so every exponent is
+//            <= 0.  Kt is stored negated so that the state passes form V - Kt S as one product
+//            accumulated onto V.
 //   precise: [Kt hi][Kt lo][Qt hi][Qt lo] (bf16 frag32) [Kb^T hi][Kb^T lo] (bf16 frag16), then T'
 //            and P (bf16 hi, lo; fragT), then e^{G_15} - 1 (DK fp32).
 //   Qt and P carry the output scale.  |P| <= |q| |k| <= 1 for L2-normalised q, k, inside fp16.
@@ -519,7 +522,7 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     // phase tiles whose 16-byte chunks are XOR-swizzled by row: slot(r, c) = r * CPR + (c ^ r').
     // Each lane then reads its own channels without bank conflicts.
     __shared__ __attribute__((aligned(16))) uint8_t sIn[PB];          // one phase's tiles
-    __shared__ __attribute__((aligned(16))) uint16_t sKb[2][BLK * 32];  // Kb^T of one group, frag16
+    __shared__ __attribute__((aligned(16))) uint16_t sKb[2 * BLK * 32];  // Kb^T of one group, fragKb
     __shared__ __attribute__((aligned(16))) float sRate[2][GATE ? DK : 4];   // gate rates: hi, lo
     __shared__ float sBeta[TOKR];
     // After the last group the input tiles are dead and hold A_00, A_11 in fp32 (for the
@@ -706,8 +709,9 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
                 accP[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt[j], kd, accP[0], 0, 0, 0);
                 kb0[j] = kd * gm[0][j];
             }
+            // Kt is stored negated: the state passes form V - Kt S as one product onto V
             *reinterpret_cast<uint4*>(rec + (64 * kk + lane) * 16) =
-                make_uint4(f16_pair(kt[0], kt[1]), f16_pair(kt[2], kt[3]), f16_pair(kt[4], kt[5]), f16_pair(kt[6], kt[7]));
+                make_uint4(f16_pair(-kt[0], -kt[1]), f16_pair(-kt[2], -kt[3]), f16_pair(-kt[4], -kt[5]), f16_pair(-kt[6], -kt[7]));
             *reinterpret_cast<uint4*>(rec + E2 + (64 * kk + lane) * 16) =
                 make_uint4(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]), f16_pair(qt[4], qt[5]), f16_pair(qt[6], qt[7]));
         }
@@ -742,22 +746,29 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
                 qt[j] *= gm[0][j];
             }
             *reinterpret_cast<uint4*>(rec + 3 * E2 + (64 * kk + lane) * 16) =
-                make_uint4(f16_pair(kt[0], kt[1]), f16_pair(kt[2], kt[3]), f16_pair(kt[4], kt[5]), f16_pair(kt[6], kt[7]));
+                make_uint4(f16_pair(-kt[0], -kt[1]), f16_pair(-kt[2], -kt[3]), f16_pair(-kt[4], -kt[5]), f16_pair(-kt[6], -kt[7]));
             *reinterpret_cast<uint4*>(rec + 4 * E2 + (64 * kk + lane) * 16) =
                 make_uint4(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]), f16_pair(qt[4], qt[5]), f16_pair(qt[6], qt[7]));
-            // Kb^T of both sub-blocks, staged channel-major: Kb_0 scaled to the record's last token
+            // Kb^T of both sub-blocks, staged in fragKb order (Kb_0 scaled to the record's last
+            // token).  The group's two tiles hold 64 16-byte slots each; slot L sits at
+            // L ^ ((L >> 3) & 7), which spreads each write instruction over twice the banks.
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int c = 32 * kk + 16 * (j >> 2) + 4 * q + (j & 3);
-                sKb[0][frag16(c, m) - 512 * kk] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb0[j] * gm[1][j]));
-                sKb[1][frag16(c, m) - 512 * kk] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb1[j]));
+                const int L = (c & 15) + 16 * (m >> 2);
+                const int at = 512 * (j >> 2) + 8 * (L ^ ((L >> 3) & 7)) + (m & 3);
+                sKb[at] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb0[j] * gm[1][j]));
+                sKb[at + 4] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb1[j]));
             }
         }
-        wave_fence();   // the group's Kb^T is read across lanes, then leaves as 1 KB stores
-        *reinterpret_cast<uint4*>(rec + 2 * E2 + 1024 * kk + 16 * lane) =
-            *reinterpret_cast<const uint4_ma*>(reinterpret_cast<const uint8_t*>(sKb[0]) + 16 * lane);
-        *reinterpret_cast<uint4*>(rec + 5 * E2 + 1024 * kk + 16 * lane) =
-            *reinterpret_cast<const uint4_ma*>(reinterpret_cast<const uint8_t*>(sKb[1]) + 16 * lane);
+        wave_fence();   // the group's Kb^T is read across lanes, then leaves as two 1 KB stores
+        {
+            const int src = 16 * (lane ^ ((lane >> 3) & 7));
+            uint8_t* const dst = rec + kb_tile_off(2 * kk, DK / 16, E2) + 16 * lane;
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4_ma*>(reinterpret_cast<const uint8_t*>(sKb) + src);
+            *reinterpret_cast<uint4*>(dst + 1024) =
+                *reinterpret_cast<const uint4_ma*>(reinterpret_cast<const uint8_t*>(sKb) + 1024 + src);
+        }
         if (m == 15) {   // e^{G_31} - 1 per channel: the product of the sub-blocks' e^{G_15}
             float* gp = reinterpret_cast<float*>(rec + R::OFF_G) + 32 * kk + 4 * q;
             float d[8];
@@ -1030,6 +1041,11 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     // One chunk: NB state steps from the records in `buf` (32 tokens each fast, 16 precise).
     auto run = [&](const uint8_t* buf, int64_t c, uint8_t* nbuf) {
         const int nt = tokens_in(c);
+        // per-lane bases: fragment rows, 8-byte fragments, the decay vector, this lane's V column
+        const uint8_t* const l16 = lds_at(buf, 16 * lane);
+        const uint8_t* const l8 = lds_at(buf, 8 * lane);
+        const float* const lg = reinterpret_cast<const float*>(lds_at(buf, R::OFF_G + 16 * lq));
+        const uint8_t* const lv = lds_at(buf, RBYTES + ESZ * (4 * lq * BVW + 16 * wave + ln));
         // o rows of this chunk and head; rows past the chunk's tokens fall outside the range
         const __amdgpu_buffer_rsrc_t orr =
             make_rsrc(static_cast<char*>(p.o) + ((bos + c * CHT) * H + h) * DV * OSZ,
@@ -1050,15 +1066,21 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                     __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O[i]), orr, off, 0, O_AUX);
             }
         };
-        auto v_minus = [&](const f32x4& Y, int row0) -> f32x4 {   // V - Y, rows as store_o
+        auto v_rows = [&](int row0) -> f32x4 {   // V, rows as store_o
             f32x4 X;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int ve = (row0 + 4 * lq + i) * BVW + 16 * wave + ln;   // V[token][column]
-                const float vv = (ESZ == 4) ? reinterpret_cast<const float*>(buf + RBYTES)[ve]
-                                            : bf16_val(reinterpret_cast<const uint16_t*>(buf + RBYTES)[ve]);
-                X[i] = vv - Y[i];
+                const int ve = (row0 + i) * BVW;            // V[row0 + 4 lq + i][16 wave + ln]
+                X[i] = (ESZ == 4) ? reinterpret_cast<const float*>(lv)[ve]
+                                  : bf16_val(reinterpret_cast<const uint16_t*>(lv)[ve]);
             }
+            return X;
+        };
+        auto v_minus = [&](const f32x4& Y, int row0) -> f32x4 {   // V - Y
+            const f32x4 V = v_rows(row0);
+            f32x4 X;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X[i] = V[i] - Y[i];
             return X;
         };
         // The Kt / Qt fragments of record b + 1 are read from LDS while record b computes (they
@@ -1068,16 +1090,16 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
         using FragA = typename std::conditional<PRECISE, bf16x8, f16x8>::type;
         constexpr int NFA = 4;
         FragA fa[NFA][KS], fn[NFA][KS];
-        auto load_fa = [&](const uint8_t* rb, FragA (&f)[NFA][KS]) {
+        auto load_fa = [&](int b, FragA (&f)[NFA][KS]) {     // record b of the chunk
 #pragma unroll
             for (int a = 0; a < NFA; ++a)
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
                     const int arr = PRECISE ? a : a + (a >> 1);   // fast: arrays 0, 1, 3, 4
-                    f[a][kk] = *reinterpret_cast<const FragA*>(rb + arr * E2 + 1024 * kk + 16 * lane);
+                    f[a][kk] = *reinterpret_cast<const FragA*>(l16 + b * R::BYTES + arr * E2 + 1024 * kk);
                 }
         };
-        load_fa(buf, fa);
+        load_fa(0, fa);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             if (b < NSLICE) {
@@ -1086,24 +1108,26 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                 // counts on every load being older than the last records' o stores)
                 __builtin_amdgcn_sched_barrier(0x78F);
             }
-            const uint8_t* rb = buf + b * R::BYTES;
-            if (b + 1 < NB) load_fa(rb + R::BYTES, fn);
-            const float* gam = reinterpret_cast<const float*>(rb + R::OFF_G);   // e^{G_last} - 1
+            const int rb = b * R::BYTES;                    // the record's byte offset in the buffer
+            if (b + 1 < NB) load_fa(b + 1, fn);
+            const float* gam = lg + rb / 4;                 // e^{G_last} - 1, from channel 4 lq
             float4 gm[CT];
 #pragma unroll
-            for (int i = 0; i < CT; ++i) gm[i] = *reinterpret_cast<const float4*>(gam + 16 * i + 4 * lq);
+            for (int i = 0; i < CT; ++i) gm[i] = *reinterpret_cast<const float4*>(gam + 16 * i);
             if constexpr (!PRECISE) {
                 // ---- one 32-token step: sub-blocks 0 and 1, S taken at the record's first token
-                const uint8_t* tb = rb + R::OFF_T + 8 * lane;   // T'_00, -C, T'_11 (fragT)
-                const uint8_t* pb = rb + R::OFF_P + 8 * lane;   // P_00, P_10, P_11
+                const uint8_t* tb = l8 + rb + R::OFF_T;   // T'_00, -C, T'_11 (fragT)
+                const uint8_t* pb = l8 + rb + R::OFF_P;   // P_00, P_10, P_11
                 const f16x4 t00 = *reinterpret_cast<const f16x4*>(tb);
                 const f16x4 ncm = *reinterpret_cast<const f16x4*>(tb + 512);
                 const f16x4 t11 = *reinterpret_cast<const f16x4*>(tb + 1024);
                 const f16x4 p00 = *reinterpret_cast<const f16x4*>(pb);
                 const f16x8 p1x = __builtin_shufflevector(*reinterpret_cast<const f16x4*>(pb + 512),
                                                           *reinterpret_cast<const f16x4*>(pb + 1024), 0, 1, 2, 3, 4, 5, 6, 7);
-                // Y_s = Kt_s S and O_s = Qt_s S (contraction over d_k; S packed as the B operand)
-                f32x4 Y0 = zero4(), Y1 = zero4(), O0 = zero4(), O1 = zero4();
+                // X_s = V_s - Kt_s S (the record holds -Kt: one product accumulated onto V; the
+                // beta scaling sits in T') and O_s = Qt_s S, contracting over d_k with S packed as
+                // the B operand
+                f32x4 X0 = v_rows(32 * b), X1 = v_rows(32 * b + 16), O0 = zero4(), O1 = zero4();
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
                     f16x8 sb;
@@ -1112,14 +1136,12 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                         sb[i] = static_cast<_Float16>(S[2 * kk][i]);
                         sb[4 + i] = static_cast<_Float16>(S[2 * kk + 1][i]);
                     }
-                    Y0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[0][kk], sb, Y0, 0, 0, 0);
-                    Y1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[2][kk], sb, Y1, 0, 0, 0);
+                    X0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[0][kk], sb, X0, 0, 0, 0);
+                    X1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[2][kk], sb, X1, 0, 0, 0);
                     O0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[1][kk], sb, O0, 0, 0, 0);
                     O1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[3][kk], sb, O1, 0, 0, 0);
                 }
-                // X = V - Y (the beta scaling sits in T'); W_0 = T'_00 X_0, X_1' = X_1 - C W_0,
-                // W_1 = T'_11 X_1'
-                const f32x4 X0 = v_minus(Y0, 32 * b), X1 = v_minus(Y1, 32 * b + 16);
+                // W_0 = T'_00 X_0, X_1' = X_1 - C W_0, W_1 = T'_11 X_1'
                 f16x4 x0, x1, w0, w1;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) x0[i] = static_cast<_Float16>(X0[i]);
@@ -1139,12 +1161,9 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                 store_o(O0, 32 * b);
                 store_o(O1, 32 * b + 16);
                 // S <- Diag(e^{G_31}) S + Kb^T W = S + Diag(e^{G_31} - 1) S + [Kb_0^T Kb_1^T] W
-                const uint8_t* kb0 = rb + 2 * E2 + 8 * lane;   // frag16 Kb^T of sub-block 0
-                const uint8_t* kb1 = rb + 5 * E2 + 8 * lane;
 #pragma unroll
                 for (int i = 0; i < CT; ++i) {
-                    const f16x8 ka = __builtin_shufflevector(*reinterpret_cast<const f16x4*>(kb0 + 512 * i),
-                                                             *reinterpret_cast<const f16x4*>(kb1 + 512 * i), 0, 1, 2, 3, 4, 5, 6, 7);
+                    const f16x8 ka = *reinterpret_cast<const f16x8*>(l16 + rb + kb_tile_off(i, CT, E2));
                     f32x4 acc;
                     acc[0] = fmaf(S[i][0], gm[i].x, S[i][0]); acc[1] = fmaf(S[i][1], gm[i].y, S[i][1]);
                     acc[2] = fmaf(S[i][2], gm[i].z, S[i][2]); acc[3] = fmaf(S[i][3], gm[i].w, S[i][3]);
@@ -1152,9 +1171,9 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                 }
             } else {
                 // ---- one 16-token step, split-bf16 operands
-                const uint16_t* Tp = reinterpret_cast<const uint16_t*>(rb + R::OFF_T) + 4 * lane;
-                const s16x4 ph = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 8 * lane);
-                const s16x4 pl = *reinterpret_cast<const s16x4*>(rb + R::OFF_P + 512 + 8 * lane);
+                const uint16_t* Tp = reinterpret_cast<const uint16_t*>(l8 + rb + R::OFF_T);
+                const s16x4 ph = *reinterpret_cast<const s16x4*>(l8 + rb + R::OFF_P);
+                const s16x4 pl = *reinterpret_cast<const s16x4*>(l8 + rb + R::OFF_P + 512);
                 f32x4 Y = zero4(), O = zero4();
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
@@ -1175,8 +1194,8 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                 split4(W, wh, wl);
                 O = mfma16_bf16_x3(ph, pl, wh, wl, O);
                 store_o(O, 16 * b);
-                const uint8_t* kbh = rb + 4 * E2 + 8 * lane;
-                const uint8_t* kbl = rb + 5 * E2 + 8 * lane;
+                const uint8_t* kbh = l8 + rb + 4 * E2;
+                const uint8_t* kbl = l8 + rb + 5 * E2;
 #pragma unroll
                 for (int i = 0; i < CT; ++i) {
                     const s16x4 kh = *reinterpret_cast<const s16x4*>(kbh + 512 * i);
@@ -1343,23 +1362,35 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
         }
     };
     // one chunk: two 32-token steps of both tiles
-    auto run = [&](const uint8_t* buf, int64_t c, uint8_t* nbuf) {
+    auto run = [&](uint8_t* buf, int64_t c, uint8_t* nbuf) {
         if (c + 1 < c_end) prefetch(nbuf, c + 1);
         __builtin_amdgcn_sched_barrier(0x78F);
+        // per-lane bases: fragment rows, 8-byte fragments, the decay vector, this lane's V column
+        const uint8_t* const l16 = lds_at(buf, 16 * lane);
+        const uint8_t* const l8 = lds_at(buf, 8 * lane);
+        const float* const lg = reinterpret_cast<const float*>(lds_at(buf, R::OFF_G + 16 * lq));
+        const uint16_t* const lv = lds_at(reinterpret_cast<uint16_t*>(buf + RBYTES), 2 * (4 * lq * BVW + n0 + ln));
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const uint8_t* rb = buf + b * R::BYTES;
-            const float* gam = reinterpret_cast<const float*>(rb + R::OFF_G);   // e^{G_last} - 1
-            const uint8_t* tb = rb + R::OFF_T + 8 * lane;                        // T'_00, -C, T'_11
-            const f16x4 t00 = *reinterpret_cast<const f16x4*>(tb);
-            const f16x4 ncm = *reinterpret_cast<const f16x4*>(tb + 512);
-            const f16x4 t11 = *reinterpret_cast<const f16x4*>(tb + 1024);
-            // Y_s = Kt_s S for both tiles (contraction over d_k; S packed as the B operand)
-            f32x4 Y[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
+            const int rb = b * R::BYTES;
+            const float* gam = lg + rb / 4;                                   // e^{G_last} - 1
+            const f16x4 t00 = *reinterpret_cast<const f16x4*>(l8 + rb + R::OFF_T);   // T'_00, -C, T'_11
+            const f16x4 ncm = *reinterpret_cast<const f16x4*>(l8 + rb + R::OFF_T + 512);
+            const f16x4 t11 = *reinterpret_cast<const f16x4*>(l8 + rb + R::OFF_T + 1024);
+            // X_s = V_s - Kt_s S for both tiles (V = 0 for M): the record holds -Kt, so one
+            // product accumulates onto V (S packed as the B operand, contraction over d_k)
+            f32x4 X[2][2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                X[0][0][i] = 0.f;
+                X[0][1][i] = 0.f;
+                X[1][0][i] = bf16_val(lv[(32 * b + i) * BVW]);
+                X[1][1][i] = bf16_val(lv[(32 * b + 16 + i) * BVW]);
+            }
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
-                const f16x8 k0 = *reinterpret_cast<const f16x8*>(rb + 1024 * kk + 16 * lane);
-                const f16x8 k1 = *reinterpret_cast<const f16x8*>(rb + 3 * E2 + 1024 * kk + 16 * lane);
+                const f16x8 k0 = *reinterpret_cast<const f16x8*>(l16 + rb + 1024 * kk);
+                const f16x8 k1 = *reinterpret_cast<const f16x8*>(l16 + rb + 3 * E2 + 1024 * kk);
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     f16x8 sb;
@@ -1368,44 +1399,44 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
                         sb[i] = static_cast<_Float16>(S[t][2 * kk][i]);
                         sb[4 + i] = static_cast<_Float16>(S[t][2 * kk + 1][i]);
                     }
-                    Y[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, sb, Y[t][0], 0, 0, 0);
-                    Y[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, sb, Y[t][1], 0, 0, 0);
+                    X[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, sb, X[t][0], 0, 0, 0);
+                    X[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, sb, X[t][1], 0, 0, 0);
                 }
             }
-            // X = V - Y (V = 0 for M); W_0 = T'_00 X_0, X_1' = X_1 - C W_0, W_1 = T'_11 X_1'
+            // W_0 = T'_00 X_0, X_1' = X_1 - C W_0, W_1 = T'_11 X_1', the two tiles' chains
+            // advanced step by step so each product's latency is covered by the other tile's
+            f16x4 x0[2], w0[2], x1[2], w1[2];
+            f32x4 Wt[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x0[t][i] = static_cast<_Float16>(X[t][0][i]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) Wt[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(t00, x0[t], zero4(), 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w0[t][i] = static_cast<_Float16>(Wt[t][i]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) Wt[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(ncm, w0[t], X[t][1], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x1[t][i] = static_cast<_Float16>(Wt[t][i]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) Wt[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(t11, x1[t], zero4(), 0, 0, 0);
             f16x8 wx[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                f32x4 X0, X1;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ve0 = (32 * b + 4 * lq + i) * BVW + n0 + ln, ve1 = ve0 + 16 * BVW;
-                    const uint16_t* vb = reinterpret_cast<const uint16_t*>(buf + RBYTES);
-                    X0[i] = (t == 1 ? bf16_val(vb[ve0]) : 0.f) - Y[t][0][i];
-                    X1[i] = (t == 1 ? bf16_val(vb[ve1]) : 0.f) - Y[t][1][i];
-                }
-                f16x4 x0, x1, w0, w1;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x0[i] = static_cast<_Float16>(X0[i]);
-                const f32x4 W0 = __builtin_amdgcn_mfma_f32_16x16x16f16(t00, x0, zero4(), 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w0[i] = static_cast<_Float16>(W0[i]);
-                const f32x4 X1p = __builtin_amdgcn_mfma_f32_16x16x16f16(ncm, w0, X1, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x1[i] = static_cast<_Float16>(X1p[i]);
-                const f32x4 W1 = __builtin_amdgcn_mfma_f32_16x16x16f16(t11, x1, zero4(), 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w1[i] = static_cast<_Float16>(W1[i]);
-                wx[t] = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
+                for (int i = 0; i < 4; ++i) w1[t][i] = static_cast<_Float16>(Wt[t][i]);
+                wx[t] = __builtin_shufflevector(w0[t], w1[t], 0, 1, 2, 3, 4, 5, 6, 7);
             }
             // S <- Diag(e^{G_31}) S + Kb^T W for both tiles
-            const uint8_t* kb0 = rb + 2 * E2 + 8 * lane;
-            const uint8_t* kb1 = rb + 5 * E2 + 8 * lane;
 #pragma unroll
             for (int i = 0; i < CT; ++i) {
-                const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * i + 4 * lq);
-                const f16x8 ka = __builtin_shufflevector(*reinterpret_cast<const f16x4*>(kb0 + 512 * i),
-                                                         *reinterpret_cast<const f16x4*>(kb1 + 512 * i), 0, 1, 2, 3, 4, 5, 6, 7);
+                const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * i);
+                const f16x8 ka = *reinterpret_cast<const f16x8*>(l16 + rb + kb_tile_off(i, CT, E2));
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     f32x4 acc;

@@ -99,12 +99,37 @@ __device__ __forceinline__ int tok_major(int r, int c) {
 //           in slots 4..7 -- the K order in which the state tiles are packed as the B operand.
 //   frag16: [DK][16] operand of a 16x16x16 product (row = channel, K = token): tile i, lane
 //           (m, q) holds channel 16i + m, tokens 4q .. 4q + 3.
+//   fragKb: [DK][32] operand of a 16x16x32 product (row = channel, K = the 32 tokens of a
+//           record): in tile i (1 KB), lane (m, q) holds channel 16i + m, tokens 4q .. 4q + 3 of
+//           sub-block 0 in slots 0..3 and the same tokens of sub-block 1 in slots 4..7 -- the K
+//           order in which W_0 and W_1 are joined as the B operand.  fragkb gives the half index
+//           inside the tile; kb_tile_off the tile's byte offset in a record.
 //   fragT : [16][16] operand of a 16x16x16 product: lane (m, q) holds row m, columns 4q .. 4q + 3.
 __device__ __forceinline__ int frag32(int r, int c) {
     return ((c >> 5) * 64 + r + 16 * ((c & 15) >> 2)) * 8 + ((c & 16) >> 2) + (c & 3);
 }
 __device__ __forceinline__ int frag16(int c, int t) { return ((c >> 4) * 64 + (c & 15) + 16 * (t >> 2)) * 4 + (t & 3); }
+__device__ __forceinline__ int fragkb(int c, int s, int t) { return ((c & 15) + 16 * (t >> 2)) * 8 + 4 * s + (t & 3); }
+// Kb^T tiles 0 .. ct/2 - 1 fill 16-bit record array 2, the others array 5 (arrays of e2 bytes), so
+// the two tiles of a 32-channel group are adjacent.
+__host__ __device__ constexpr int kb_tile_off(int i, int ct, int e2) {
+    return i < ct / 2 ? 2 * e2 + 1024 * i : 5 * e2 + 1024 * (i - ct / 2);
+}
 __device__ __forceinline__ int fragT(int r, int s) { return (r + 16 * (s >> 2)) * 4 + (s & 3); }
+
+// `base + off` as a pointer whose offset sits in a register the compiler cannot see through,
+// while the pointer still derives from `base`: reads through it then address from that register
+// with immediate offsets (below 64 KB) instead of forming each address, and alias analysis still
+// knows which LDS buffer they read (so no waits for transfers into the other buffer).
+template <typename T>
+__device__ __forceinline__ T* lds_at(T* base, uint32_t off) {
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    lds_u8* const b = (lds_u8*)(base);
+    const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(b));
+    uint32_t x = a + off;
+    asm volatile("" : "+v"(x));
+    return (T*)(b + (x - a));
+}
 
 // LDS ordering inside a one-wave workgroup: a wave's LDS operations execute in order, so only the
 // compiler must keep them in place.  A wavefront-scope fence does that and emits no wait (a

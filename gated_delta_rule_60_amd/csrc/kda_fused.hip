@@ -14,9 +14,9 @@
 // One workgroup of twelve waves runs one (sequence, head) from its inputs to its outputs; the
 // launch serves 16-bit inputs at d_k = d_v = 128 when the (sequence, head) units fill the chip.
 // The block form is the one of the two-kernel path (kda_chunk.hip), and so is the 32-token record:
-// two 16-token sub-blocks with Kt = e^G k, Qt = e^G q (scaled), Kb = e^{G_31 - G} k in fp16 MFMA
-// fragment order, T'_00, -C, T'_11, P_00, P_10, P_11 and the decay over the record.  Here the
-// records never leave LDS.  In iteration r:
+// two 16-token sub-blocks with -Kt = -e^G k, Qt = e^G q (scaled), Kb = e^{G_31 - G} k in fp16 MFMA
+// fragment order (Kb^T of both sub-blocks joined per lane), T'_00, -C, T'_11, P_00, P_10, P_11 and
+// the decay over the record.  Here the records never leave LDS.  In iteration r:
 //   * four producer waves, one per 32-channel group, build record r + 2 from inputs loaded into
 //     registers during the previous iteration: the gate, the cumsums, the factors, Kt / Qt / Kb
 //     and their partial A, P and cross products over their 32 channels;
@@ -24,7 +24,7 @@
 //     T'_00 and T'_11 by forward substitution, and P_00, P_10, P_11 and -C = -Kt_1 Kb_0^T in fp16
 //     (T'_10 = -T'_11 C T'_00 is applied below, so it is never formed);
 //   * eight consumer waves, 16 state columns each, pass the fp32 state through record r:
-//     Y = Kt S, O = Qt S, X = V - Y, W_0 = T'_00 X_0, W_1 = T'_11 (X_1 - C W_0), O += P W,
+//     X = V - Kt S, O = Qt S, W_0 = T'_00 X_0, W_1 = T'_11 (X_1 - C W_0), O += P W,
 //     S <- Diag(e^{G_31}) S + Kb^T W, and store o.
 // The V rows of record r + 1 stream into LDS by direct-to-LDS loads while record r is processed,
 // so the kernel reads q, k, v, beta and g (or z) once and writes o once.  Tokens past a
@@ -196,8 +196,6 @@ __device__ __forceinline__ void produce(const ChunkArgs& p, const PIn<(GDT == KD
     const bool unit_scale = (p.scale == 1.f);
 
     f32x4 accA[2] = {zero4(), zero4()}, accP[2] = {zero4(), zero4()}, accC = zero4(), accQ = zero4();
-    uint16_t* const kb0a = reinterpret_cast<uint16_t*>(rec + 2 * FE2);
-    uint16_t* const kb1a = reinterpret_cast<uint16_t*>(rec + 5 * FE2);
     // sub-block 0: Kt, Qt, Kd with its own cumsum; Kb_0 = Kd e^{G_15} <= 1 kept for the cross products
     float kb0[8];
     {
@@ -213,8 +211,9 @@ __device__ __forceinline__ void produce(const ChunkArgs& p, const PIn<(GDT == KD
             accP[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt[j], kd, accP[0], 0, 0, 0);
             kb0[j] = kd * gm[0][j];
         }
+        // Kt is stored negated: the state step forms V - Kt S as one product onto V
         *reinterpret_cast<uint4*>(rec + (64 * kk + lane) * 16) =
-            make_uint4(f16_pair(kt[0], kt[1]), f16_pair(kt[2], kt[3]), f16_pair(kt[4], kt[5]), f16_pair(kt[6], kt[7]));
+            make_uint4(f16_pair(-kt[0], -kt[1]), f16_pair(-kt[2], -kt[3]), f16_pair(-kt[4], -kt[5]), f16_pair(-kt[6], -kt[7]));
         *reinterpret_cast<uint4*>(rec + FE2 + (64 * kk + lane) * 16) =
             make_uint4(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]), f16_pair(qt[4], qt[5]), f16_pair(qt[6], qt[7]));
     }
@@ -247,15 +246,16 @@ __device__ __forceinline__ void produce(const ChunkArgs& p, const PIn<(GDT == KD
             qt[j] *= gm[0][j];
         }
         *reinterpret_cast<uint4*>(rec + 3 * FE2 + (64 * kk + lane) * 16) =
-            make_uint4(f16_pair(kt[0], kt[1]), f16_pair(kt[2], kt[3]), f16_pair(kt[4], kt[5]), f16_pair(kt[6], kt[7]));
+            make_uint4(f16_pair(-kt[0], -kt[1]), f16_pair(-kt[2], -kt[3]), f16_pair(-kt[4], -kt[5]), f16_pair(-kt[6], -kt[7]));
         *reinterpret_cast<uint4*>(rec + 4 * FE2 + (64 * kk + lane) * 16) =
             make_uint4(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]), f16_pair(qt[4], qt[5]), f16_pair(qt[6], qt[7]));
-        // Kb^T of both sub-blocks, channel-major: Kb_0 scaled to the record's last token
+        // Kb^T of both sub-blocks in fragKb order: Kb_0 scaled to the record's last token
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int c = 32 * kk + 16 * (j >> 2) + 4 * q + (j & 3);
-            kb0a[frag16(c, m)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb0[j] * gm[1][j]));
-            kb1a[frag16(c, m)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb1[j]));
+            uint16_t* const kt16 = reinterpret_cast<uint16_t*>(rec + kb_tile_off(c >> 4, 8, FE2));
+            kt16[fragkb(c, 0, m)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb0[j] * gm[1][j]));
+            kt16[fragkb(c, 1, m)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb1[j]));
         }
     }
     if (m == 15) {   // e^{G_31} - 1 per channel: the product of the sub-blocks' e^{G_15}
@@ -482,8 +482,14 @@ __device__ __forceinline__ void consumer_loop(const FCtx& c, const FUnit& u, Fus
         }
         if (r + 1 < nrec) issue_v(r + 1, vnext);
         const uint8_t* rc = L.rec[r % 3];
-        // Y_s = Kt_s S and O_s = Qt_s S (contraction over d_k; S packed as the B operand)
-        f32x4 Y[2] = {zero4(), zero4()}, O[2] = {zero4(), zero4()};
+        // X_s = V_s - Kt_s S (the record holds -Kt: one product accumulated onto V; the beta
+        // scaling sits in T') and O_s = Qt_s S, contracting over d_k with S packed as the B operand
+        f32x4 Y[2], O[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Y[0][i] = bf16_val(*reinterpret_cast<const uint16_t*>(vt + voff[i]));
+            Y[1][i] = bf16_val(*reinterpret_cast<const uint16_t*>(vt + voff[4 + i]));
+        }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const f16x8 ka0 = *reinterpret_cast<const f16x8*>(rc + 1024 * kk + 16 * lane);
@@ -501,17 +507,11 @@ __device__ __forceinline__ void consumer_loop(const FCtx& c, const FUnit& u, Fus
             O[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa0, sb, O[0], 0, 0, 0);
             O[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa1, sb, O[1], 0, 0, 0);
         }
-        // X = V - Y (the beta scaling sits in T'); W_0 = T'_00 X_0; X_1' = X_1 - C W_0;
-        // W_1 = T'_11 X_1'
+        // W_0 = T'_00 X_0; X_1' = X_1 - C W_0; W_1 = T'_11 X_1'
         const f16x4 t00 = *reinterpret_cast<const f16x4*>(rc + F_OFF_T + 8 * lane);
         const f16x4 ncm = *reinterpret_cast<const f16x4*>(rc + F_OFF_T + 512 + 8 * lane);
         const f16x4 t11 = *reinterpret_cast<const f16x4*>(rc + F_OFF_T + 1024 + 8 * lane);
-        f32x4 X0, X1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            X0[i] = bf16_val(*reinterpret_cast<const uint16_t*>(vt + voff[i])) - Y[0][i];
-            X1[i] = bf16_val(*reinterpret_cast<const uint16_t*>(vt + voff[4 + i])) - Y[1][i];
-        }
+        const f32x4 X0 = Y[0], X1 = Y[1];
         f16x4 x0, x1, w0, w1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) x0[i] = static_cast<_Float16>(X0[i]);
@@ -556,13 +556,10 @@ __device__ __forceinline__ void consumer_loop(const FCtx& c, const FUnit& u, Fus
         }
         // S <- Diag(e^{G_31}) S + Kb^T W = S + Diag(e^{G_31} - 1) S + [Kb_0^T Kb_1^T] [W_0; W_1]
         const float* gam = reinterpret_cast<const float*>(rc + F_OFF_G);
-        const uint8_t* kb0 = rc + 2 * FE2 + 8 * lane;
-        const uint8_t* kb1 = rc + 5 * FE2 + 8 * lane;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * i + 4 * lq);
-            const f16x8 ka = __builtin_shufflevector(*reinterpret_cast<const f16x4*>(kb0 + 512 * i),
-                                                     *reinterpret_cast<const f16x4*>(kb1 + 512 * i), 0, 1, 2, 3, 4, 5, 6, 7);
+            const f16x8 ka = *reinterpret_cast<const f16x8*>(rc + kb_tile_off(i, 8, FE2) + 16 * lane);
             f32x4 acc;
             acc[0] = fmaf(S[i][0], gm.x, S[i][0]); acc[1] = fmaf(S[i][1], gm.y, S[i][1]);
             acc[2] = fmaf(S[i][2], gm.z, S[i][2]); acc[3] = fmaf(S[i][3], gm.w, S[i][3]);

@@ -10,8 +10,9 @@ record's first token [habr § Последовательность: the bounded 
   T' = (I + A)^{-1} Diag(beta) (its diagonal blocks T'_00, T'_11),  C[i, j] = sum_c k_{16+i,c}
   k_jc e^{G_{16+i,c} - G_jc} (the cross block of A without beta, stored negated),
   and e^{G_31} - 1 per channel.
-The record stores them in fp16 MFMA fragment order (Kt, Qt: 16x16x32 A operands; Kb^T: 16x16x16
-A operand, channel-major; T', P: [16][16] tiles), so each field is checked to fp16 precision.
+The record stores them in fp16 MFMA fragment order (-Kt, Qt: 16x16x32 A operands, Kt negated;
+Kb^T of both sub-blocks: one 16x16x32 A operand, channel-major, a lane's tokens of sub-block 0 then
+the same tokens of sub-block 1; T', P: [16][16] tiles), so each field is checked to fp16 precision.
 The gates are scaled down 20x so that every field, the cross-sub-block tiles included, is O(1).
 """
 import numpy as np
@@ -42,9 +43,14 @@ def frag32(r, c):
     return ((c >> 5) * 64 + r + 16 * ((c & 15) >> 2)) * 8 + ((c & 16) >> 2) + (c & 3)
 
 
-def frag16(c, t):
-    """Half index of (channel c, token t) in a 16x16x16 A-operand array (tile c // 16)."""
-    return ((c >> 4) * 64 + (c & 15) + 16 * (t >> 2)) * 4 + (t & 3)
+def fragkb(c, s, t, dk):
+    """Half index of (channel c, sub-block s, token t) of Kb^T in a record: tile c // 16 (1 KB;
+    tiles below dk / 32 in array 2, the others in array 5), lane (c % 16, t // 4), slot
+    4 * s + t % 4."""
+    ct, e2 = dk // 16, 16 * dk * 2
+    tile = c >> 4
+    off = np.where(tile < ct // 2, 2 * e2 + 1024 * tile, 5 * e2 + 1024 * (tile - ct // 2)) // 2
+    return off + ((c & 15) + 16 * (t >> 2)) * 8 + 4 * s + (t & 3)
 
 
 def fragT(r, s):
@@ -60,16 +66,15 @@ def decode(rec, dk):
     def tok_major(off):
         return h(off, 16 * dk)[frag32(r16, c16)]
 
-    def chan_major(off):
-        return h(off, 16 * dk)[frag16(c16, r16)]
 
     rr, ss = np.meshgrid(np.arange(16), np.arange(16), indexing="ij")
     tile = lambda off: h(off, 256)[fragT(rr, ss)]
     out = {}
+    whole = rec[:OFF_T].view(np.float16).astype(np.float64)
     for s in range(2):
         base = 3 * s * E2
-        out[f"Kt{s}"], out[f"Qt{s}"], out[f"Kb{s}"] = (tok_major(base), tok_major(base + E2),
-                                                       chan_major(base + 2 * E2))
+        out[f"Kt{s}"], out[f"Qt{s}"] = -tok_major(base), tok_major(base + E2)
+        out[f"Kb{s}"] = whole[fragkb(c16, s, r16, dk)]
     out["T00"], out["negC"], out["T11"] = tile(OFF_T), tile(OFF_T + 512), tile(OFF_T + 1024)
     out["P00"], out["P10"], out["P11"] = tile(OFF_P), tile(OFF_P + 512), tile(OFF_P + 1024)
     out["gamma"] = rec[OFF_G:OFF_G + 4 * dk].view(np.float32).astype(np.float64)
