@@ -1336,8 +1336,10 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
         const int64_t rem = len - c * CHT;
         return static_cast<int>(rem < 0 ? 0 : rem < CHT ? rem : CHT);
     };
-    // chunk c's records (their Kt, Kb, T' and decay units) and its V rows into an LDS buffer
-    auto prefetch = [&](uint8_t* buf, int64_t c) {
+    // Chunk c's records (their Kt, Kb, T' and decay units) and its V rows into an LDS buffer:
+    // items [i0, i1) of this wave's share.
+    constexpr int NITEM = ROUNDS + VROUNDS;
+    auto prefetch = [&](uint8_t* buf, int64_t c, int i0, int i1) {
         const int nt = tokens_in(c);
         const int nbk = (nt + R::TOK - 1) / R::TOK;
         const __amdgpu_buffer_rsrc_t rr =
@@ -1348,12 +1350,13 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
 #pragma unroll
         for (int it = 0; it < ROUNDS; ++it) {
             const int u = it * NW + wave;
-            if ((SKIP >> u) & 1) continue;
+            if (it < i0 || it >= i1 || ((SKIP >> u) & 1)) continue;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void*)(buf + u * WKB), 16,
                                                      u * WKB + 16 * lane, 0, 0, 0);
         }
 #pragma unroll
         for (int it = 0; it < VROUNDS; ++it) {
+            if (ROUNDS + it < i0 || ROUNDS + it >= i1) continue;
             const int u = it * NW + wave;
             const int byte = u * WKB + 16 * lane;
             const int row = byte / VROW, col = byte % VROW;
@@ -1363,8 +1366,16 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
     };
     // one chunk: two 32-token steps of both tiles
     auto run = [&](uint8_t* buf, int64_t c, uint8_t* nbuf) {
-        if (c + 1 < c_end) prefetch(nbuf, c + 1);
-        __builtin_amdgcn_sched_barrier(0x78F);
+        // The next chunk's transfers: a wave issues its share at one of four points of record 0
+        // (its start, after its Y products, after its W chain, after its state update), two waves
+        // on different SIMDs per point.  Issued by all waves at once, the transfers fill the
+        // memory pipeline and the waves stall in turn for up to a third of the chunk; staggered,
+        // each wave waits only behind one other.  (Memory instructions stay at these points.)
+        auto issue = [&](int k) {
+            __builtin_amdgcn_sched_barrier(0x78F);
+            if (k == ((wave + 2 * (wave >> 2)) & 3) && c + 1 < c_end) prefetch(nbuf, c + 1, 0, NITEM);
+            __builtin_amdgcn_sched_barrier(0x78F);
+        };
         // per-lane bases: fragment rows, 8-byte fragments, the decay vector, this lane's V column
         const uint8_t* const l16 = lds_at(buf, 16 * lane);
         const uint8_t* const l8 = lds_at(buf, 8 * lane);
@@ -1372,6 +1383,7 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
         const uint16_t* const lv = lds_at(reinterpret_cast<uint16_t*>(buf + RBYTES), 2 * (4 * lq * BVW + n0 + ln));
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
+            if (b == 0) issue(0);
             const int rb = b * R::BYTES;
             const float* gam = lg + rb / 4;                                   // e^{G_last} - 1
             const f16x4 t00 = *reinterpret_cast<const f16x4*>(l8 + rb + R::OFF_T);   // T'_00, -C, T'_11
@@ -1403,6 +1415,7 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
                     X[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, sb, X[t][1], 0, 0, 0);
                 }
             }
+            if (b == 0) issue(1);
             // W_0 = T'_00 X_0, X_1' = X_1 - C W_0, W_1 = T'_11 X_1', the two tiles' chains
             // advanced step by step so each product's latency is covered by the other tile's
             f16x4 x0[2], w0[2], x1[2], w1[2];
@@ -1432,6 +1445,7 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
                 for (int i = 0; i < 4; ++i) w1[t][i] = static_cast<_Float16>(Wt[t][i]);
                 wx[t] = __builtin_shufflevector(w0[t], w1[t], 0, 1, 2, 3, 4, 5, 6, 7);
             }
+            if (b == 0) issue(2);
             // S <- Diag(e^{G_31}) S + Kb^T W for both tiles
 #pragma unroll
             for (int i = 0; i < CT; ++i) {
@@ -1445,10 +1459,11 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
                     S[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, wx[t], acc, 0, 0, 0);
                 }
             }
+            if (b == 0) issue(3);
         }
     };
 
-    prefetch(bufA, c_begin);
+    prefetch(bufA, c_begin, 0, NITEM);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     for (int64_t ci = c_begin; ci < c_end; ci += 2) {
