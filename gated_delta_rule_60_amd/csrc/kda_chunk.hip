@@ -61,7 +61,11 @@ constexpr int BLK = 16;     // tokens per block (one state step)
 // passes (8 when d_k = d_v = 128).
 constexpr int STATE_WAVES = 2;
 constexpr int SEG_WAVES = 4;
-constexpr int STATE_SLICES = 2;  // slices a chunk's transfers are issued in (at most NB - 1)
+constexpr int STATE_SLICES = 1;  // transfer slices of a chunk in the state pass without helpers
+// Helper waves of the state pass: a workgroup of at most two computing waves uses at most two of
+// a CU's four SIMDs, so as many more waves only issue its transfers (the computing waves then
+// never stall on a run of memory instructions).
+constexpr int state_helpers(int nw) { return nw <= 2 ? nw : 0; }
 
 // ---- MFMA wrappers (operands already in their 16-bit format) --------------------------------
 __device__ __forceinline__ f32x4 mfma32_bf16_x3(const bf16x8& ah, const bf16x8& al,
@@ -834,7 +838,8 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
 }
 
 // ============================================================================================
-// 2. state-passing kernel: one workgroup of NW waves per (sequence, head, 16 NW state columns)
+// 2. state-passing kernel: one workgroup of NW computing waves per (sequence, head, 16 NW state
+//    columns), plus NW waves that only issue its transfers when NW <= 2
 // ============================================================================================
 
 // Long sequences in the two-kernel path: segments of 2^SEG_SHIFT tokens (kda_chunk_util.hpp).
@@ -844,7 +849,7 @@ constexpr int SEG_MAX_SEQS = 128;   // segmented launches have at most 128 seque
 
 // MODE 0: whole sequences.  MODE 1: segment pass 1.  MODE 2: segment pass 2.
 template <int DK, int IDT, int ODT, bool PRECISE, int NW, bool CKPT, int MODE>
-__global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, int32_t n_vblk,
+__global__ void __launch_bounds__(64 * (NW + state_helpers(NW)), 1) chunk_state_kernel(ChunkArgs p, int32_t n_vblk,
                                                                  int64_t nslots, const uint8_t* ws,
                                                                  SegArgs sg) {
     using R = Rec<DK, PRECISE>;
@@ -874,6 +879,10 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int ln = lane & 15, lq = lane >> 4;
+    // waves 0 .. NW - 1 compute; waves NW .. NW + NH - 1 (NH = NW or 0) issue the transfers
+    constexpr int NH = state_helpers(NW);
+    const bool helper = NH > 0 && wave >= NW;
+    const int dwave = NH > 0 ? wave - NW : wave;       // the transfer share of an issuing wave
 
     // Workgroup -> (unit, column block).  The column blocks of one unit sit 8 workgroup ids
     // apart so they land on the same XCD and share its L2 for the unit's records.  A unit is a
@@ -976,7 +985,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                                    : static_cast<int64_t>(n) * (p.T / ck_every);
     auto checkpoint = [&](int64_t done) {          // `done` tokens of the sequence processed
         if constexpr (!CKPT) return;
-        if (!emit_o || done > len || done % ck_every != 0) return;
+        if (helper || !emit_o || done > len || done % ck_every != 0) return;
         const int64_t slot = ck_base + done / ck_every - 1;
         if (slot >= p.ckpt_slots) return;
         float* dst = p.ckpt + (slot * H + h) * DK * DV;
@@ -985,7 +994,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(16 * i + 4 * lq + r) * DV + n0 + ln] = S[i][r];
     };
-    {
+    if (!helper) {
         // an absent initial state is an empty range: every load reads 0
         const __amdgpu_buffer_rsrc_t h0r =
             make_rsrc(init, init ? static_cast<uint32_t>(DK * ldst * 4) : 0u);
@@ -1005,11 +1014,14 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     };
     // Chunk c's records and its V slice go straight from memory into an LDS buffer (records past
     // the sequence's last block, V rows past its last token, and the padding read as zeros:
-    // identity steps).  The transfers are issued in NSLICE slices, one at the start of each of the
-    // chunk's first blocks: all at once they collide with the blocks' own LDS reads (measured
-    // slower), in three slices fewer bytes are in flight.
+    // identity steps).  The transfers are issued in NSLICE slices at the chunk's issue points:
+    // point 2b is the start of block b, point 2b + 1 its end before its o stores.  A wave issues
+    // one slice at a point, since a long run of transfers stalls it until the memory pipeline
+    // takes them (at two waves per workgroup, 30 transfers held each wave for a quarter of the
+    // chunk).
     constexpr int NITEM = ROUNDS + VROUNDS;
-    constexpr int NSLICE = STATE_SLICES < NB ? STATE_SLICES : NB - 1;
+    constexpr int NSLICE = NH > 0 ? 1 : STATE_SLICES;
+    static_assert(NSLICE <= 2 * NB, "issue points of a chunk");
     auto prefetch_slice = [&](uint8_t* buf, int64_t c, int slice) {
         const int nt = tokens_in(c);
         const int nbk = (nt + R::TOK - 1) / R::TOK;
@@ -1023,12 +1035,12 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
         for (int it = 0; it < NITEM; ++it) {
             if (it < i0 || it >= i1) continue;
             if (it < ROUNDS) {
-                const int u = it * NW + wave;           // this wave's 1 KB unit of the records
+                const int u = it * NW + dwave;          // this wave's 1 KB unit of the records
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rr, (__attribute__((address_space(3))) void*)(buf + u * WKB), 16,
                     u * WKB + 16 * lane, 0, 0, 0);
             } else {
-                const int u = (it - ROUNDS) * NW + wave;   // this wave's 1 KB unit of V
+                const int u = (it - ROUNDS) * NW + dwave;  // this wave's 1 KB unit of V
                 const int byte = u * WKB + 16 * lane;     // within the [CHT][BVW] slice
                 const int row = byte / VROW, col = byte % VROW;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -1041,6 +1053,15 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     // One chunk: NB state steps from the records in `buf` (32 tokens each fast, 16 precise).
     auto run = [&](const uint8_t* buf, int64_t c, uint8_t* nbuf) {
         const int nt = tokens_in(c);
+        // memory instructions keep their order across an issue point (the end-of-chunk wait
+        // counts the o stores issued after the last slice)
+        auto issue_at = [&](int k) {
+            if constexpr (NH == 0) {
+                __builtin_amdgcn_sched_barrier(0x78F);
+                if (k < NSLICE) prefetch_slice(nbuf, c + 1, k);
+                __builtin_amdgcn_sched_barrier(0x78F);
+            }
+        };
         // per-lane bases: fragment rows, 8-byte fragments, the decay vector, this lane's V column
         const uint8_t* const l16 = lds_at(buf, 16 * lane);
         const uint8_t* const l8 = lds_at(buf, 8 * lane);
@@ -1102,12 +1123,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
         load_fa(0, fa);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            if (b < NSLICE) {
-                prefetch_slice(nbuf, c + 1, b);
-                // memory instructions keep their order across this point (the end-of-chunk wait
-                // counts on every load being older than the last records' o stores)
-                __builtin_amdgcn_sched_barrier(0x78F);
-            }
+            issue_at(2 * b);
             const int rb = b * R::BYTES;                    // the record's byte offset in the buffer
             if (b + 1 < NB) load_fa(b + 1, fn);
             const float* gam = lg + rb / 4;                 // e^{G_last} - 1, from channel 4 lq
@@ -1158,6 +1174,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                 // O += P W (P and Qt carry the output scale)
                 O0 = __builtin_amdgcn_mfma_f32_16x16x16f16(p00, w0, O0, 0, 0, 0);
                 O1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(p1x, wx, O1, 0, 0, 0);
+                issue_at(2 * b + 1);
                 store_o(O0, 32 * b);
                 store_o(O1, 32 * b + 16);
                 // S <- Diag(e^{G_31}) S + Kb^T W = S + Diag(e^{G_31} - 1) S + [Kb_0^T Kb_1^T] W
@@ -1193,6 +1210,7 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
                 s16x4 wh, wl;
                 split4(W, wh, wl);
                 O = mfma16_bf16_x3(ph, pl, wh, wl, O);
+                issue_at(2 * b + 1);
                 store_o(O, 16 * b);
                 const uint8_t* kbh = l8 + rb + 4 * E2;
                 const uint8_t* kbl = l8 + rb + 5 * E2;
@@ -1219,30 +1237,44 @@ __global__ void __launch_bounds__(64 * NW, 1) chunk_state_kernel(ChunkArgs p, in
     // waits for those transfers -- the o stores of the records from the one that issued the last
     // slice on (OST each) may stay in flight, every load is older -- and meets the other waves at
     // the barrier.
-    constexpr int WAIT_LOADS = vmcnt_imm(OST * (NB - NSLICE + 1));
+    // blocks whose o stores follow the last slice (point NSLICE - 1): b >= (NSLICE - 1) / 2
+    constexpr int WAIT_LOADS = vmcnt_imm(OST * (NB - (NSLICE - 1) / 2));
+    // With helpers, a helper issues all of chunk c + 1's transfers while the computing waves run
+    // chunk c, then waits for them; the computing waves issue only o stores and do not wait.
+    auto step = [&](const uint8_t* buf, int64_t c, uint8_t* nbuf) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NH == 0) {
+            run(buf, c, nbuf);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(WAIT_LOADS);
+        } else {
+            if (helper) {
+                prefetch_slice(nbuf, c + 1, 0);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            } else {
+                run(buf, c, nbuf);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    };
+    if (NH == 0 || helper) {
 #pragma unroll
-    for (int sl = 0; sl < NSLICE; ++sl) prefetch_slice(bufA, c_begin, sl);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        for (int sl = 0; sl < NSLICE; ++sl) prefetch_slice(bufA, c_begin, sl);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
     __syncthreads();
     // (A checkpoint's stores go out before the next chunk's transfers, so they are older than
     // every load the waits above count on.)
     for (int64_t ci = c_begin; ci < c_end; ci += 2) {
-        __builtin_amdgcn_sched_barrier(0);
-        run(bufA, ci, bufB);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(WAIT_LOADS);
-        __syncthreads();
+        step(bufA, ci, bufB);
         checkpoint((ci + 1) * CHT);
         if (ci + 1 >= c_end) break;
-        __builtin_amdgcn_sched_barrier(0);
-        run(bufB, ci + 1, bufA);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(WAIT_LOADS);
-        __syncthreads();
+        step(bufB, ci + 1, bufA);
         checkpoint((ci + 2) * CHT);
     }
 
-    if (fin) {
+    if (fin && !helper) {
 #pragma unroll
         for (int i = 0; i < CT; ++i)
 #pragma unroll
@@ -1664,8 +1696,8 @@ void launch_state(const ChunkArgs& a, int64_t nslots, const uint8_t* ws, const S
     const int64_t groups = (units + 7) / 8;
     const int32_t n_vblk = a.dv / (16 * NW);
     hipLaunchKernelGGL((chunk_state_kernel<DK, IDT, ODT, PRECISE, NW, CKPT, MODE>),
-                       dim3(static_cast<unsigned>(groups * 8 * nvx)), dim3(64 * NW), 0, stream, a,
-                       n_vblk, nslots, ws, sg);
+                       dim3(static_cast<unsigned>(groups * 8 * nvx)), dim3(64 * (NW + state_helpers(NW))), 0,
+                       stream, a, n_vblk, nslots, ws, sg);
 }
 
 template <int DK, int IDT, int ODT, bool PRECISE, int MODE, int NW = STATE_WAVES>
