@@ -875,12 +875,16 @@ __global__ void __launch_bounds__(64 * (NW + state_helpers(NW)), 1) chunk_state_
     // alias the reads of the other and inserts no waits for them.
     __shared__ __attribute__((aligned(16))) uint8_t bufA[LBYTES];
     __shared__ __attribute__((aligned(16))) uint8_t bufB[LBYTES];
+    // waves 0 .. NW - 1 compute; waves NW .. NW + NH - 1 (NH = NW or 0) issue the transfers and,
+    // from a two-chunk LDS stage the computing waves write o into, the o stores
+    constexpr int NH = state_helpers(NW);
+    constexpr int OROW = BVW * OSZ;                    // bytes of one token's o slice
+    constexpr int OSTAGE = CHT * OROW;                 // one chunk's o slice
+    __shared__ __attribute__((aligned(16))) uint8_t ostage[NH > 0 ? 2 * OSTAGE : 16];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int ln = lane & 15, lq = lane >> 4;
-    // waves 0 .. NW - 1 compute; waves NW .. NW + NH - 1 (NH = NW or 0) issue the transfers
-    constexpr int NH = state_helpers(NW);
     const bool helper = NH > 0 && wave >= NW;
     const int dwave = NH > 0 ? wave - NW : wave;       // the transfer share of an issuing wave
 
@@ -1012,6 +1016,33 @@ __global__ void __launch_bounds__(64 * (NW + state_helpers(NW)), 1) chunk_state_
         const int64_t rem = len - c * CHT;
         return static_cast<int>(rem < 0 ? 0 : rem < CHT ? rem : CHT);
     };
+    // o stores: a computing wave's store covers 32 (bf16) or 64 bytes of a row, a helper's 16 of
+    // the workgroup's row slice.  When the workgroup holds every column of the state (8 waves at
+    // d_v = 128) its waves' partial lines merge in L2 under the default cache policy
+    // (non-temporal stores wrote 26% more bytes there and made segment pass 2 10% slower);
+    // narrower workgroups, whose lines are completed by other CUs, measured 5% faster with
+    // non-temporal stores.
+    constexpr int O_AUX = (16 * NW >= 128) ? 0 : CP_NT;
+    // helpers: chunk cp's o slice from the stage, 16 bytes a lane (OROW / 16 lanes a row); rows
+    // past the chunk's tokens fall outside the range
+    constexpr int OPIECE = CHT * OROW / 16;
+    constexpr int OSTORES = NH > 0 ? OPIECE / (64 * NH) : 0;   // store instructions per helper
+    static_assert(NH == 0 || OPIECE % (64 * NH) == 0, "whole store rounds");
+    auto store_stage = [&](int64_t cp) {
+        const int ntp = tokens_in(cp);
+        const __amdgpu_buffer_rsrc_t orr =
+            make_rsrc(static_cast<char*>(p.o) + ((bos + cp * CHT) * H + h) * DV * OSZ,
+                      emit_o ? static_cast<uint32_t>(ntp * vstride * OSZ) : 0u);
+        const uint8_t* const st = ostage + (cp & 1) * OSTAGE;
+#pragma unroll
+        for (int k = 0; k < OSTORES; ++k) {
+            const int q = (k * NH + dwave) * 64 + lane;
+            const int row = q / (OROW / 16), piece = q % (OROW / 16);
+            typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+            const u32x4v val = *reinterpret_cast<const u32x4v*>(st + row * OROW + 16 * piece);
+            __builtin_amdgcn_raw_buffer_store_b128(val, orr, (row * vstride + vb * BVW) * OSZ + 16 * piece, 0, O_AUX);
+        }
+    };
     // Chunk c's records and its V slice go straight from memory into an LDS buffer (records past
     // the sequence's last block, V rows past its last token, and the padding read as zeros:
     // identity steps).  The transfers are issued in NSLICE slices at the chunk's issue points:
@@ -1071,20 +1102,21 @@ __global__ void __launch_bounds__(64 * (NW + state_helpers(NW)), 1) chunk_state_
         const __amdgpu_buffer_rsrc_t orr =
             make_rsrc(static_cast<char*>(p.o) + ((bos + c * CHT) * H + h) * DV * OSZ,
                       emit_o ? static_cast<uint32_t>(nt * vstride * OSZ) : 0u);
-        // o stores: a store covers 32 (bf16) or 64 bytes of a row.  When the workgroup holds
-        // every column of the state (8 waves at d_v = 128) its waves' partial lines merge in L2
-        // under the default cache policy (non-temporal stores wrote 26% more bytes there and made
-        // segment pass 2 10% slower); narrower workgroups, whose lines are completed by other
-        // CUs, measured 5% faster with non-temporal stores.
-        constexpr int O_AUX = (16 * NW >= 128) ? 0 : CP_NT;
         auto store_o = [&](const f32x4& O, int row0) {   // rows row0 + 4 lq + i of the chunk
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int off = ((row0 + 4 * lq + i) * vstride + n0 + ln) * OSZ;
-                if constexpr (ODT == KDA_F32)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i]), orr, off, 0, O_AUX);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O[i]), orr, off, 0, O_AUX);
+                if constexpr (NH > 0) {                  // into the stage (the helpers store it)
+                    const int e = (row0 + 4 * lq + i) * BVW + 16 * wave + ln;
+                    uint8_t* const st = ostage + (c & 1) * OSTAGE;
+                    if constexpr (ODT == KDA_F32) reinterpret_cast<float*>(st)[e] = O[i];
+                    else reinterpret_cast<uint16_t*>(st)[e] = bf16_bits(O[i]);
+                } else {
+                    const int off = ((row0 + 4 * lq + i) * vstride + n0 + ln) * OSZ;
+                    if constexpr (ODT == KDA_F32)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i]), orr, off, 0, O_AUX);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(O[i]), orr, off, 0, O_AUX);
+                }
             }
         };
         auto v_rows = [&](int row0) -> f32x4 {   // V, rows as store_o
@@ -1249,8 +1281,16 @@ __global__ void __launch_bounds__(64 * (NW + state_helpers(NW)), 1) chunk_state_
             __builtin_amdgcn_s_waitcnt(WAIT_LOADS);
         } else {
             if (helper) {
+                // the next chunk's transfers, then the previous chunk's o; the wait leaves the
+                // stores in flight (memory operations of a wave complete in issue order)
                 prefetch_slice(nbuf, c + 1, 0);
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                __builtin_amdgcn_sched_barrier(0x78F);
+                if (c > c_begin) {
+                    store_stage(c - 1);
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(OSTORES));
+                } else {
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                }
             } else {
                 run(buf, c, nbuf);
             }
@@ -1273,6 +1313,7 @@ __global__ void __launch_bounds__(64 * (NW + state_helpers(NW)), 1) chunk_state_
         step(bufB, ci + 1, bufA);
         checkpoint((ci + 2) * CHT);
     }
+    if (helper && c_end > c_begin) store_stage(c_end - 1);   // the last chunk's o (staged before the last barrier)
 
     if (fin && !helper) {
 #pragma unroll
