@@ -94,13 +94,15 @@ constexpr int QP_LAST = 3 | (3 << 2) | (3 << 4) | (3 << 6);    // [3,3,3,3]
 // Record of one (head, block slot) in the workspace (byte offsets).  E = 16 * DK elements per
 // array.  A fast record covers 32 tokens: two 16-token sub-blocks, one 32-token state step; a
 // precise record covers one 16-token block.
-//   fast   : six fp16 [16][DK] arrays: [-Kt_0 frag32][Qt_0 frag32][Kb^T][-Kt_1][Qt_1][Kb^T], the
-//            two Kb^T arrays holding Kb^T of both sub-blocks in fragKb order (tiles 0 .. DK/32 - 1
-//            in the first, the rest in the second); then T'_00, -C, T'_11 and P_00, P_10, P_11
-//            (fp16 fragT, [row sub-block][column sub-block]); then e^{G_31} - 1 (DK fp32).  Kt,
-//            Qt are scaled from the record's first token, Kb from its last, so every exponent is
-//            <= 0.  Kt is stored negated so that the state passes form V - Kt S as one product
-//            accumulated onto V.
+//   fast   : first what every state pass reads -- [-Kt_0 frag32][Kb^T][-Kt_1 frag32][Kb^T] (fp16
+//            [16][DK] arrays; the two Kb^T arrays hold Kb^T of both sub-blocks in fragKb order,
+//            tiles 0 .. DK/32 - 1 in the first, the rest in the second), T'_00, -C, T'_11 (fp16
+//            fragT) and e^{G_31} - 1 (DK fp32), HEAD bytes, a whole number of 1 KB units at
+//            d_k = 128 -- then what only output passes read: [Qt_0 frag32][Qt_1 frag32] and
+//            P_00, P_10, P_11 (fp16 fragT, [row sub-block][column sub-block]).  Kt, Qt are scaled
+//            from the record's first token, Kb from its last, so every exponent is <= 0.  Kt is
+//            stored negated so that the state passes form V - Kt S as one product accumulated
+//            onto V.
 //   precise: [Kt hi][Kt lo][Qt hi][Qt lo] (bf16 frag32) [Kb^T hi][Kb^T lo] (bf16 frag16), then T'
 //            and P (bf16 hi, lo; fragT), then e^{G_15} - 1 (DK fp32).
 //   Qt and P carry the output scale.  |P| <= |q| |k| <= 1 for L2-normalised q, k, inside fp16.
@@ -111,11 +113,21 @@ struct Rec {
     static constexpr int TOK = PRECISE ? 16 : 32;       // tokens per record
     static constexpr int E = BLK * DK;
     static constexpr int NA = 6;                        // 16-bit [16][DK] arrays
-    static constexpr int OFF_T = NA * E * 2;
-    static constexpr int OFF_P = OFF_T + (PRECISE ? 1024 : 1536);
-    static constexpr int OFF_G = OFF_P + (PRECISE ? 1024 : 1536);
-    static constexpr int BYTES = OFF_G + DK * 4;
-    static_assert(BYTES % 16 == 0, "record alignment");
+    static constexpr int E2 = 2 * E;                    // bytes of one of them
+    static constexpr int TB = PRECISE ? 1024 : 1536;    // the T' tiles, and the P tiles
+    // fast layout (the precise one: arrays 0..5, T', P, decay)
+    static constexpr int OFF_KB_LO = E2, OFF_KT1 = 2 * E2, OFF_KB_HI = 3 * E2;
+    static constexpr int OFF_T = PRECISE ? NA * E2 : 4 * E2;
+    static constexpr int OFF_G = PRECISE ? OFF_T + 2 * TB : OFF_T + TB;
+    static constexpr int HEAD = OFF_G + DK * 4;         // fast: the part every state pass reads
+    static constexpr int OFF_QT0 = HEAD, OFF_QT1 = HEAD + E2;
+    static constexpr int OFF_P = PRECISE ? OFF_T + TB : HEAD + 2 * E2;
+    static constexpr int BYTES = PRECISE ? HEAD : OFF_P + TB;
+    static_assert(BYTES % 16 == 0 && HEAD % 16 == 0, "record alignment");
+    // fast: the byte offset of the state pass's A operand a (-Kt_0, Qt_0, -Kt_1, Qt_1)
+    static constexpr int fa_off(int a) { return a == 0 ? 0 : a == 1 ? OFF_QT0 : a == 2 ? OFF_KT1 : OFF_QT1; }
+    // fast: Kb^T tile i
+    static constexpr int kb_off(int i) { return kb_tile_off(i, DK / 16, OFF_KB_LO, OFF_KB_HI); }
 };
 
 // Raw inputs held by one staging lane: 4 tokens x CPT channels; bf16 packed two per register.
@@ -513,7 +525,7 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     constexpr int KS = DK / 32;           // 32-channel groups
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr int E2 = 2 * R::E;          // bytes of one 16-bit record array
-    constexpr int TAIL = R::OFF_G - R::OFF_T;
+    constexpr int TAIL = 2 * R::TB;       // T' and P tiles, staged together
 
     constexpr int PH = DK / 64;           // 64-channel phases: one 128-byte line of a bf16 row
     constexpr int GSZ = (GDT == KDA_F32) ? 4 : 2;
@@ -716,7 +728,7 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
             // Kt is stored negated: the state passes form V - Kt S as one product onto V
             *reinterpret_cast<uint4*>(rec + (64 * kk + lane) * 16) =
                 make_uint4(f16_pair(-kt[0], -kt[1]), f16_pair(-kt[2], -kt[3]), f16_pair(-kt[4], -kt[5]), f16_pair(-kt[6], -kt[7]));
-            *reinterpret_cast<uint4*>(rec + E2 + (64 * kk + lane) * 16) =
+            *reinterpret_cast<uint4*>(rec + R::OFF_QT0 + (64 * kk + lane) * 16) =
                 make_uint4(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]), f16_pair(qt[4], qt[5]), f16_pair(qt[6], qt[7]));
         }
         // sub-block 1: the same with its own cumsum, plus C = Kt_1 Kb_0^T and Qt_1 Kb_0^T; the
@@ -749,9 +761,9 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
                 kt[j] *= gm[0][j];
                 qt[j] *= gm[0][j];
             }
-            *reinterpret_cast<uint4*>(rec + 3 * E2 + (64 * kk + lane) * 16) =
+            *reinterpret_cast<uint4*>(rec + R::OFF_KT1 + (64 * kk + lane) * 16) =
                 make_uint4(f16_pair(-kt[0], -kt[1]), f16_pair(-kt[2], -kt[3]), f16_pair(-kt[4], -kt[5]), f16_pair(-kt[6], -kt[7]));
-            *reinterpret_cast<uint4*>(rec + 4 * E2 + (64 * kk + lane) * 16) =
+            *reinterpret_cast<uint4*>(rec + R::OFF_QT1 + (64 * kk + lane) * 16) =
                 make_uint4(f16_pair(qt[0], qt[1]), f16_pair(qt[2], qt[3]), f16_pair(qt[4], qt[5]), f16_pair(qt[6], qt[7]));
             // Kb^T of both sub-blocks, staged in fragKb order (Kb_0 scaled to the record's last
             // token).  The group's two tiles hold 64 16-byte slots each; slot L sits at
@@ -768,7 +780,7 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
         wave_fence();   // the group's Kb^T is read across lanes, then leaves as two 1 KB stores
         {
             const int src = 16 * (lane ^ ((lane >> 3) & 7));
-            uint8_t* const dst = rec + kb_tile_off(2 * kk, DK / 16, E2) + 16 * lane;
+            uint8_t* const dst = rec + R::kb_off(2 * kk) + 16 * lane;
             *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4_ma*>(reinterpret_cast<const uint8_t*>(sKb) + src);
             *reinterpret_cast<uint4*>(dst + 1024) =
                 *reinterpret_cast<const uint4_ma*>(reinterpret_cast<const uint8_t*>(sKb) + 1024 + src);
@@ -786,7 +798,7 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     // ---- A_00, A_11 to LDS (for the substitutions); -C and P staged in fp16.  Lane (m, q) holds
     // rows 4q + i of column m.  Staged tiles: T'_00, -C, T'_11, then P_00, P_10, P_11.
     uint16_t* const tT = reinterpret_cast<uint16_t*>(sTail);
-    uint16_t* const tP = reinterpret_cast<uint16_t*>(sTail + (R::OFF_P - R::OFF_T));
+    uint16_t* const tP = reinterpret_cast<uint16_t*>(sTail + R::TB);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * q + i, sc = m;
@@ -834,7 +846,8 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     }
     wave_fence();   // T', -C and P staged
     for (int u = lane; u < TAIL / 16; u += 64)
-        *reinterpret_cast<uint4*>(rec + R::OFF_T + 16 * u) = *reinterpret_cast<const uint4_ma*>(sTail + 16 * u);
+        *reinterpret_cast<uint4*>(rec + (16 * u < R::TB ? R::OFF_T : R::OFF_P - R::TB) + 16 * u) =
+            *reinterpret_cast<const uint4_ma*>(sTail + 16 * u);
 }
 
 // ============================================================================================
@@ -1148,8 +1161,8 @@ __global__ void __launch_bounds__(64 * (NW + state_helpers(NW)), 1) chunk_state_
             for (int a = 0; a < NFA; ++a)
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
-                    const int arr = PRECISE ? a : a + (a >> 1);   // fast: arrays 0, 1, 3, 4
-                    f[a][kk] = *reinterpret_cast<const FragA*>(l16 + b * R::BYTES + arr * E2 + 1024 * kk);
+                    const int off = PRECISE ? a * E2 : R::fa_off(a);
+                    f[a][kk] = *reinterpret_cast<const FragA*>(l16 + b * R::BYTES + off + 1024 * kk);
                 }
         };
         load_fa(0, fa);
@@ -1212,7 +1225,7 @@ __global__ void __launch_bounds__(64 * (NW + state_helpers(NW)), 1) chunk_state_
                 // S <- Diag(e^{G_31}) S + Kb^T W = S + Diag(e^{G_31} - 1) S + [Kb_0^T Kb_1^T] W
 #pragma unroll
                 for (int i = 0; i < CT; ++i) {
-                    const f16x8 ka = *reinterpret_cast<const f16x8*>(l16 + rb + kb_tile_off(i, CT, E2));
+                    const f16x8 ka = *reinterpret_cast<const f16x8*>(l16 + rb + R::kb_off(i));
                     f32x4 acc;
                     acc[0] = fmaf(S[i][0], gm[i].x, S[i][0]); acc[1] = fmaf(S[i][1], gm[i].y, S[i][1]);
                     acc[2] = fmaf(S[i][2], gm[i].z, S[i][2]); acc[3] = fmaf(S[i][3], gm[i].w, S[i][3]);
@@ -1327,24 +1340,8 @@ __global__ void __launch_bounds__(64 * (NW + state_helpers(NW)), 1) chunk_state_
 // Segment pass 1 at d_k = d_v = 128 with 16-bit inputs: one workgroup of eight waves per
 // (segment, head) for every segment but a sequence's last, running the segment's pair at once --
 // wave w holds state columns 16 w .. 16 w + 15 of both M (from the identity, V = 0) and B (from
-// zero, with V).  The records stream through LDS once, their Qt and P parts skipped (no o here);
-// the two tiles' dependent chains interleave in each wave.
-constexpr uint64_t pair_skip_mask() {     // 1 KB units of a two-record chunk that hold only Qt / P
-    using R = Rec<128, false>;
-    uint64_t m = 0;
-    for (int u = 0; u < 64; ++u) {
-        const int lo = 1024 * u, hi = lo + 1024;
-        for (int b = 0; b < 2; ++b) {
-            const int o = b * R::BYTES;
-            const int rng[3][2] = {{o + R::E * 2, o + 2 * R::E * 2}, {o + 4 * R::E * 2, o + 5 * R::E * 2},
-                                   {o + R::OFF_P, o + R::OFF_G}};
-            for (int k = 0; k < 3; ++k)
-                if (lo >= rng[k][0] && hi <= rng[k][1]) m |= uint64_t(1) << u;
-        }
-    }
-    return m;
-}
-
+// zero, with V).  The records' heads (no Qt, P: no o here) stream through LDS once, packed; the
+// two tiles' dependent chains interleave in each wave.
 template <int IDT>
 __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t nslots, const uint8_t* ws,
                                                             SegArgs sg) {
@@ -1353,15 +1350,15 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
     constexpr int KS = DK / 32, CT = DK / 16;
     constexpr int NB = 2, CHT = NB * R::TOK;           // two 32-token records per chunk
     constexpr int WKB = 64 * 16;
-    constexpr int ROUNDS = (NB * R::BYTES + NW * WKB - 1) / (NW * WKB);
-    constexpr int RBYTES = ROUNDS * NW * WKB;
+    constexpr int PREC = R::HEAD;                      // a record's head: -Kt, Kb^T, T', decay
+    constexpr int RUNITS = NB * PREC / WKB;            // 1 KB units of a chunk's heads
+    constexpr int ROUNDS = (RUNITS + NW - 1) / NW;
+    constexpr int RBYTES = NB * PREC;                  // record b's head at b * PREC in LDS
     constexpr int BVW = 16 * NW;                       // 128 columns: all of M, all of B
     constexpr int VROW = BVW * 2;
     constexpr int VROUNDS = (CHT * VROW + NW * WKB - 1) / (NW * WKB);
     constexpr int LBYTES = RBYTES + VROUNDS * NW * WKB;
-    constexpr int E2 = 2 * R::E;
-    constexpr uint64_t SKIP = pair_skip_mask();
-    static_assert(ROUNDS * NW <= 64, "skip mask covers the chunk");
+    static_assert(PREC % WKB == 0, "record heads are whole 1 KB units");
     static_assert(IDT == KDA_BF16, "16-bit inputs");
     __shared__ __attribute__((aligned(16))) uint8_t bufA[LBYTES];
     __shared__ __attribute__((aligned(16))) uint8_t bufB[LBYTES];
@@ -1409,8 +1406,8 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
         const int64_t rem = len - c * CHT;
         return static_cast<int>(rem < 0 ? 0 : rem < CHT ? rem : CHT);
     };
-    // Chunk c's records (their Kt, Kb, T' and decay units) and its V rows into an LDS buffer:
-    // items [i0, i1) of this wave's share.
+    // Chunk c's record heads and its V rows into an LDS buffer: items [i0, i1) of this wave's
+    // share.
     constexpr int NITEM = ROUNDS + VROUNDS;
     auto prefetch = [&](uint8_t* buf, int64_t c, int i0, int i1) {
         const int nt = tokens_in(c);
@@ -1422,10 +1419,11 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
             static_cast<uint32_t>(nt * vstride * 2));
 #pragma unroll
         for (int it = 0; it < ROUNDS; ++it) {
-            const int u = it * NW + wave;
-            if (it < i0 || it >= i1 || ((SKIP >> u) & 1)) continue;
+            const int u = it * NW + wave;               // unit u % (PREC / WKB) of record u / (PREC / WKB)
+            if (it < i0 || it >= i1 || u >= RUNITS) continue;
+            const int src = (u / (PREC / WKB)) * R::BYTES + (u % (PREC / WKB)) * WKB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void*)(buf + u * WKB), 16,
-                                                     u * WKB + 16 * lane, 0, 0, 0);
+                                                     src + 16 * lane, 0, 0, 0);
         }
 #pragma unroll
         for (int it = 0; it < VROUNDS; ++it) {
@@ -1457,7 +1455,7 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             if (b == 0) issue(0);
-            const int rb = b * R::BYTES;
+            const int rb = b * PREC;
             const float* gam = lg + rb / 4;                                   // e^{G_last} - 1
             const f16x4 t00 = *reinterpret_cast<const f16x4*>(l8 + rb + R::OFF_T);   // T'_00, -C, T'_11
             const f16x4 ncm = *reinterpret_cast<const f16x4*>(l8 + rb + R::OFF_T + 512);
@@ -1475,7 +1473,7 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 const f16x8 k0 = *reinterpret_cast<const f16x8*>(l16 + rb + 1024 * kk);
-                const f16x8 k1 = *reinterpret_cast<const f16x8*>(l16 + rb + 3 * E2 + 1024 * kk);
+                const f16x8 k1 = *reinterpret_cast<const f16x8*>(l16 + rb + R::OFF_KT1 + 1024 * kk);
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     f16x8 sb;
@@ -1523,7 +1521,7 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
 #pragma unroll
             for (int i = 0; i < CT; ++i) {
                 const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * i);
-                const f16x8 ka = *reinterpret_cast<const f16x8*>(l16 + rb + kb_tile_off(i, CT, E2));
+                const f16x8 ka = *reinterpret_cast<const f16x8*>(l16 + rb + R::kb_off(i));
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     f32x4 acc;

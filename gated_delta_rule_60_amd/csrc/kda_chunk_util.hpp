@@ -110,10 +110,10 @@ __device__ __forceinline__ int frag32(int r, int c) {
 }
 __device__ __forceinline__ int frag16(int c, int t) { return ((c >> 4) * 64 + (c & 15) + 16 * (t >> 2)) * 4 + (t & 3); }
 __device__ __forceinline__ int fragkb(int c, int s, int t) { return ((c & 15) + 16 * (t >> 2)) * 8 + 4 * s + (t & 3); }
-// Kb^T tiles 0 .. ct/2 - 1 fill 16-bit record array 2, the others array 5 (arrays of e2 bytes), so
-// the two tiles of a 32-channel group are adjacent.
-__host__ __device__ constexpr int kb_tile_off(int i, int ct, int e2) {
-    return i < ct / 2 ? 2 * e2 + 1024 * i : 5 * e2 + 1024 * (i - ct / 2);
+// Kb^T tiles 0 .. ct/2 - 1 fill the record array at byte lo, the others the one at hi, so the two
+// tiles of a 32-channel group are adjacent.
+__host__ __device__ constexpr int kb_tile_off(int i, int ct, int lo, int hi) {
+    return i < ct / 2 ? lo + 1024 * i : hi + 1024 * (i - ct / 2);
 }
 __device__ __forceinline__ int fragT(int r, int s) { return (r + 16 * (s >> 2)) * 4 + (s & 3); }
 

@@ -253,7 +253,7 @@ __device__ __forceinline__ void produce(const ChunkArgs& p, const PIn<(GDT == KD
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int c = 32 * kk + 16 * (j >> 2) + 4 * q + (j & 3);
-            uint16_t* const kt16 = reinterpret_cast<uint16_t*>(rec + kb_tile_off(c >> 4, 8, FE2));
+            uint16_t* const kt16 = reinterpret_cast<uint16_t*>(rec + kb_tile_off(c >> 4, 8, 2 * FE2, 5 * FE2));
             kt16[fragkb(c, 0, m)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb0[j] * gm[1][j]));
             kt16[fragkb(c, 1, m)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(kb1[j]));
         }
@@ -559,7 +559,7 @@ __device__ __forceinline__ void consumer_loop(const FCtx& c, const FUnit& u, Fus
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * i + 4 * lq);
-            const f16x8 ka = *reinterpret_cast<const f16x8*>(rc + kb_tile_off(i, 8, FE2) + 16 * lane);
+            const f16x8 ka = *reinterpret_cast<const f16x8*>(rc + kb_tile_off(i, 8, 2 * FE2, 5 * FE2) + 16 * lane);
             f32x4 acc;
             acc[0] = fmaf(S[i][0], gm.x, S[i][0]); acc[1] = fmaf(S[i][1], gm.y, S[i][1]);
             acc[2] = fmaf(S[i][2], gm.z, S[i][2]); acc[3] = fmaf(S[i][3], gm.w, S[i][3]);

@@ -28,13 +28,16 @@ TOL = 2e-3                           # fp16 storage is 2^-11 relative
 
 
 def layout(dk):
-    """Byte offsets of a record at head size dk: six fp16 [16][dk] arrays, then T'_00, -C, T'_11,
-    then P_00, P_10, P_11 (fp16 16 x 16 tiles), then e^{G_31} - 1 (dk fp32)."""
+    """Byte offsets of a record at head size dk.  First what every state pass reads: -Kt_0, Kb^T
+    (tiles below dk / 32), -Kt_1, Kb^T (the other tiles) -- fp16 [16][dk] arrays -- then T'_00,
+    -C, T'_11 (fp16 16 x 16 tiles) and e^{G_31} - 1 (dk fp32); then Qt_0, Qt_1 and P_00, P_10,
+    P_11.  Returns (array bytes, -Kt_0, -Kt_1, Qt_0, Qt_1, T', P, decay, record bytes)."""
     e2 = 16 * dk * 2
-    off_t = 6 * e2
-    off_p = off_t + 3 * 512
-    off_g = off_p + 3 * 512
-    return e2, off_t, off_p, off_g, off_g + 4 * dk
+    off_t = 4 * e2
+    off_g = off_t + 3 * 512
+    head = off_g + 4 * dk
+    off_p = head + 2 * e2
+    return e2, 0, 2 * e2, head, head + e2, off_t, off_p, off_g, off_p + 3 * 512
 
 
 def frag32(r, c):
@@ -45,11 +48,11 @@ def frag32(r, c):
 
 def fragkb(c, s, t, dk):
     """Half index of (channel c, sub-block s, token t) of Kb^T in a record: tile c // 16 (1 KB;
-    tiles below dk / 32 in array 2, the others in array 5), lane (c % 16, t // 4), slot
-    4 * s + t % 4."""
+    tiles below dk / 32 in the array after -Kt_0, the others in the one after -Kt_1), lane
+    (c % 16, t // 4), slot 4 * s + t % 4."""
     ct, e2 = dk // 16, 16 * dk * 2
     tile = c >> 4
-    off = np.where(tile < ct // 2, 2 * e2 + 1024 * tile, 5 * e2 + 1024 * (tile - ct // 2)) // 2
+    off = np.where(tile < ct // 2, e2 + 1024 * tile, 3 * e2 + 1024 * (tile - ct // 2)) // 2
     return off + ((c & 15) + 16 * (t >> 2)) * 8 + 4 * s + (t & 3)
 
 
@@ -59,7 +62,7 @@ def fragT(r, s):
 
 
 def decode(rec, dk):
-    E2, OFF_T, OFF_P, OFF_G, _ = layout(dk)
+    E2, OFF_KT0, OFF_KT1, OFF_QT0, OFF_QT1, OFF_T, OFF_P, OFF_G, _ = layout(dk)
     h = lambda off, n: rec[off:off + 2 * n].view(np.float16).astype(np.float64)
     r16, c16 = np.meshgrid(np.arange(16), np.arange(dk), indexing="ij")
 
@@ -71,9 +74,8 @@ def decode(rec, dk):
     tile = lambda off: h(off, 256)[fragT(rr, ss)]
     out = {}
     whole = rec[:OFF_T].view(np.float16).astype(np.float64)
-    for s in range(2):
-        base = 3 * s * E2
-        out[f"Kt{s}"], out[f"Qt{s}"] = -tok_major(base), tok_major(base + E2)
+    for s, (kt, qt) in enumerate(((OFF_KT0, OFF_QT0), (OFF_KT1, OFF_QT1))):
+        out[f"Kt{s}"], out[f"Qt{s}"] = -tok_major(kt), tok_major(qt)
         out[f"Kb{s}"] = whole[fragkb(c16, s, r16, dk)]
     out["T00"], out["negC"], out["T11"] = tile(OFF_T), tile(OFF_T + 512), tile(OFF_T + 1024)
     out["P00"], out["P10"], out["P11"] = tile(OFF_P), tile(OFF_P + 512), tile(OFF_P + 1024)
@@ -111,7 +113,7 @@ def expected(g, k, q, beta, t0, n):
 
 
 def _check_records(W, base, slots, T, d, g, dk):
-    rec_bytes = layout(dk)[4]
+    rec_bytes = layout(dk)[-1]
     f64 = lambda x: x.double().numpy().reshape(T, -1)
     g64, k64, q64, b64 = f64(g), f64(d["k"]), f64(d["q"]), d["beta"].double().numpy().reshape(T)
     assert W.size >= (base + max(slots) + 1) * rec_bytes
