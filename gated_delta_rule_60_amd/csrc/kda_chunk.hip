@@ -27,7 +27,7 @@
 // 64-token chunk's triangular system is solved blockwise, the coupling going through the state.
 //
 // 1. Intra-block kernel (everything that does not depend on S; fully parallel): writes one
-//    record per (head, record slot) to the workspace -- Kt, Qt, Kb^T in their MFMA formats,
+//    record per (head, record slot) to the workspace -- -Kt, Qt, Kb^T in their MFMA formats,
 //    the diagonal blocks of T', the cross tile -C, P, the step's e^{G_last} - 1.
 //    16-bit inputs (chunk_intra_tok_kernel): one wave per (32-token record, head); each lane
 //    owns one token of each 16-token sub-block and the channels of its record unit; inputs
@@ -36,11 +36,13 @@
 //    block T'_10 = -T'_11 C T'_00 is left to the state pass, which applies it as two products.
 //    fp32 inputs (chunk_intra_kernel, split-bf16 records of 16 tokens): each lane owns 4 tokens
 //    x 4 channels; quad-lane cumsum, A and P on MFMA from split-bf16 operands staged in LDS.
-// 2. State-passing kernel (the sequential part): one workgroup of STATE_WAVES waves per
-//    (sequence, head, 16 STATE_WAVES state columns); each wave owns 16 state columns in fp32
+// 2. State-passing kernel (the sequential part): one workgroup of STATE_WAVES computing waves
+//    per (sequence, head, 16 STATE_WAVES state columns); each wave owns 16 state columns in fp32
 //    accumulators for the whole sequence.  A chunk's two records and its V rows stream into
-//    double-buffered LDS while the previous chunk is processed.  Optionally it stores the state
-//    every k tokens (checkpoints).  Long sequences with few (sequence, head) units run as
+//    double-buffered LDS while the previous chunk is processed; in the two-wave workgroups two
+//    more waves issue those transfers and store o from an LDS stage, so the computing waves
+//    issue no memory instructions in the loop.  Optionally it stores the state every k tokens
+//    (checkpoints).  Long sequences with few (sequence, head) units run as
 //    segments: pass 1 (the segments' affine pairs; chunk_pair_kernel at d_k = d_v = 128), a scan
 //    of the pairs, pass 2 (see the segment section below).
 // Launches with 16-bit inputs at d_k = d_v = 128 and at least 256 (sequence, head) units run the
