@@ -48,17 +48,38 @@ struct StepSmem {
     float kq[4];
 };
 
+// A token's inputs as one lane uses them: lanes t < DK hold channel t of g, k, q; every lane holds
+// its four columns of v and beta.  The single-token step loads them before the state read, so its
+// token does not wait on a second memory round trip.
+struct TokIn {
+    float g, k, q, beta;
+    float4 v;
+};
+template <int DK, int DV, int IDT, int GDT>
+__device__ __forceinline__ TokIn load_token(const void* __restrict__ q, const void* __restrict__ k,
+                                            const void* __restrict__ v, const void* __restrict__ beta,
+                                            const void* __restrict__ g, int64_t tok) {
+    const int t = threadIdx.x, cg = t % (DV / 4);
+    TokIn in;
+    in.g = in.k = in.q = 0.f;
+    if (t < DK) {
+        in.g = load_as_f32<GDT>(g, tok * DK + t);
+        in.k = load_as_f32<IDT>(k, tok * DK + t);
+        in.q = load_as_f32<IDT>(q, tok * DK + t);
+    }
+    in.beta = load_as_f32<IDT>(beta, tok);
+    in.v = load4_as_f32<IDT>(v, tok * DV + 4 * cg);
+    return in;
+}
+
 // One token of one (sequence, head) on the state held in registers s[] (rows rg*RPT + i, columns
-// 4cg .. 4cg+3).  tok indexes the token's [.., H, d] rows of q, k, g (times DK), v (times DV) and
-// beta; o (if not null) receives the token's output row.  With STORE each updated row also goes
-// to S as soon as it is formed (interleaving the stores with the update keeps the write stream
-// smooth).  Every lane of the workgroup calls it.
-template <int DK, int DV, int IDT, int GDT, int ODT, bool STORE>
+// 4cg .. 4cg+3), from its inputs `in`; tok indexes its output row, which o (if not null)
+// receives.  With STORE each updated row also goes to S as soon as it is formed (interleaving the
+// stores with the update keeps the write stream smooth).  Every lane of the workgroup calls it.
+template <int DK, int DV, int ODT, bool STORE>
 __device__ __forceinline__ void decode_token(float4 (&s)[DK / (256 / (DV / 4))], StepSmem<DK, DV>& sm,
-                                             const void* __restrict__ q, const void* __restrict__ k,
-                                             const void* __restrict__ v, const void* __restrict__ beta,
-                                             const void* __restrict__ g, int64_t tok,
-                                             void* __restrict__ o, float scale, float* __restrict__ S) {
+                                             const TokIn& in, int64_t tok, void* __restrict__ o,
+                                             float scale, float* __restrict__ S) {
     constexpr int CG = DV / 4;    // lanes per state row
     constexpr int RG = 256 / CG;  // row groups
     constexpr int RPT = DK / RG;  // rows per lane
@@ -67,9 +88,9 @@ __device__ __forceinline__ void decode_token(float4 (&s)[DK / (256 / (DV / 4))],
 
     float kq = 0.0f;
     if (t < DK) {
-        const float a = expf(load_as_f32<GDT>(g, tok * DK + t));
-        const float kk = load_as_f32<IDT>(k, tok * DK + t);
-        const float qq = load_as_f32<IDT>(q, tok * DK + t);
+        const float a = expf(in.g);
+        const float kk = in.k;
+        const float qq = in.q;
         sm.alpha[t] = a;
         sm.ak[t] = a * kk;
         sm.aq[t] = a * qq;
@@ -102,8 +123,8 @@ __device__ __forceinline__ void decode_token(float4 (&s)[DK / (256 / (DV / 4))],
         B4.x += y.x; B4.y += y.y; B4.z += y.z; B4.w += y.w;
     }
     const float kqs = sm.kq[0] + sm.kq[1] + sm.kq[2] + sm.kq[3];
-    const float bt = load_as_f32<IDT>(beta, tok);
-    const float4 vv = load4_as_f32<IDT>(v, tok * DV + 4 * cg);
+    const float bt = in.beta;
+    const float4 vv = in.v;
     const float4 u = make_float4(vv.x - A4.x, vv.y - A4.y, vv.z - A4.z, vv.w - A4.w);
     if (o != nullptr && rg == 0) {
         const float c = bt * kqs;
@@ -142,12 +163,13 @@ __global__ void __launch_bounds__(256) decode_kernel(const void* __restrict__ q,
     const int cg = t % CG, rg = t / CG;
     float* S = state + unit * (DK * DV);
 
-    // Issue the whole state read first.
+    // The token's inputs, then the whole state read.
+    const TokIn in = load_token<DK, DV, IDT, GDT>(q, k, v, beta, g, unit);
     float4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         s[i] = stream_load4(S + (rg * RPT + i) * DV + 4 * cg);
-    decode_token<DK, DV, IDT, GDT, ODT, true>(s, sm, q, k, v, beta, g, unit, o, scale, S);
+    decode_token<DK, DV, ODT, true>(s, sm, in, unit, o, scale, S);
 }
 
 // Several tokens per sequence on one read of the state ([habr, § Как обслуживать два разных
@@ -183,6 +205,7 @@ __global__ void __launch_bounds__(256) decode_multi_kernel(const void* __restric
         steps = a < 0 ? 0 : (a > K ? K : a);
         if (steps == 0) return;                  // nothing accepted: the state stays as it is
     }
+    auto tok = [&](int32_t j) -> int64_t { return (n * K + j) * H + h; };
     float4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
@@ -190,13 +213,14 @@ __global__ void __launch_bounds__(256) decode_multi_kernel(const void* __restric
     const int32_t last = COMMIT ? steps - 1 : steps;   // commit: the last token also stores S
     for (int32_t j = 0; j < last; ++j) {
         if (j > 0) __syncthreads();              // the previous token's shared values are read
-        decode_token<DK, DV, IDT, GDT, ODT, false>(s, sm, q, k, v, beta, g, (n * K + j) * H + h,
-                                                   COMMIT ? nullptr : o, scale, S);
+        // (inputs loaded at the token's start: loading them a token ahead measured slower)
+        decode_token<DK, DV, ODT, false>(s, sm, load_token<DK, DV, IDT, GDT>(q, k, v, beta, g, tok(j)),
+                                         tok(j), COMMIT ? nullptr : o, scale, S);
     }
     if constexpr (COMMIT) {
         if (last > 0) __syncthreads();
-        decode_token<DK, DV, IDT, GDT, ODT, true>(s, sm, q, k, v, beta, g, (n * K + last) * H + h,
-                                                  nullptr, scale, S);
+        decode_token<DK, DV, ODT, true>(s, sm, load_token<DK, DV, IDT, GDT>(q, k, v, beta, g, tok(last)),
+                                        tok(last), nullptr, scale, S);
     }
 }
 
