@@ -224,6 +224,190 @@ __global__ void __launch_bounds__(256) decode_multi_kernel(const void* __restric
     }
 }
 
+// Verify from one read of the state, batched over the draft.  With G_j = g_0 + ... + g_j per
+// channel, the state before token j satisfies
+//     S_j^T y = S_0^T (e^{G_{j-1}} * y) + sum_{i<j} beta_i u_i (k_i . (e^{G_{j-1} - G_i} * y)),
+// so token j's a_j = S_j^T (alpha_j * k_j) and b_j = S_j^T (alpha_j * q_j) are
+//     a_j = S_0^T (e^{G_j} * k_j) + sum_{i<j} beta_i ck_ji u_i,   ck_ji = sum_d k_i e^{G_j - G_i} k_j
+//     b_j = S_0^T (e^{G_j} * q_j) + sum_{i<j} beta_i cq_ji u_i,   cq_ji = sum_d k_i e^{G_j - G_i} q_j
+// with u_j = v_j - a_j and o_j = scale (b_j + beta_j (k_j . q_j) u_j).  The 2K projections
+// against S_0 are one pass over the state (no per-token pass, no state update); the K x K
+// scalars are reductions over d_k; the recurrence for u runs on d_v-vectors.  Token 0 takes
+// exactly the step kernel's arithmetic; later tokens equal successive steps up to rounding.
+constexpr int VERIFY_KMAX = 8;   // longer drafts run decode_multi_kernel
+constexpr int VERIFY_PV = 2;     // projection vectors per pass over the registers
+
+template <int DK, int DV, int IDT, int GDT, int ODT>
+__global__ void __launch_bounds__(256) decode_verify_kernel(const void* __restrict__ q,
+                                                            const void* __restrict__ k,
+                                                            const void* __restrict__ v,
+                                                            const void* __restrict__ beta,
+                                                            const void* __restrict__ g,
+                                                            const float* __restrict__ state,
+                                                            void* __restrict__ o, float scale,
+                                                            int32_t K, int32_t H) {
+    constexpr int CG = DV / 4, RG = 256 / CG, RPT = DK / RG;
+    constexpr int KM = VERIFY_KMAX, NV = 2 * KM, NPAIR = KM * (KM - 1) / 2;
+    static_assert(RPT >= 1 && RG * RPT == DK && DK <= 256, "shape");
+    __shared__ float xv[NV][DK];                  // e^{G_j} k_j at 2j, e^{G_j} q_j at 2j + 1
+    __shared__ float4 red[RG][VERIFY_PV][CG];     // partial projections of one pass
+    __shared__ float4 tot[NV][CG];                // the projections S_0^T x
+    __shared__ float scal[4][2 * NPAIR + KM];     // per-wave partial sums of ck, cq, k.q
+    constexpr int VPL = (KM * CG + 255) / 256;   // v chunks per lane
+    __shared__ float4 vin[VPL * 256 / CG][CG];    // the draft's v rows (rows >= K unused)
+    __shared__ float bin[256];                    // and its betas (entries >= K unused)
+
+    const int64_t unit = blockIdx.x;  // sequence * H + head
+    const int64_t n = unit / H, h = unit % H;
+    const int t = threadIdx.x, wave = t >> 6;
+    const int cg = t % CG, rg = t / CG;
+    auto tok = [&](int32_t j) -> int64_t { return (n * K + j) * H + h; };
+
+    // The draft's inputs go out before the state read: loads complete in issue order, so the work
+    // on them overlaps the state's arrival instead of waiting for it.  The loads take no branch (a
+    // branch would make each wait for its value there): token indices clamp to K - 1 (K >= 1) and
+    // what the clamped loads bring for j >= K is never read.  Lane t takes channel t mod DK of g,
+    // k and q (lanes t < DK use theirs), v chunk t (+ 256 p) and the beta of token t.
+    const int ch = t % DK;
+    auto tokc = [&](int j) { return tok(j < K ? j : K - 1); };
+    float G[KM], kk[KM], qq[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+        G[j] = load_as_f32<GDT>(g, tokc(j) * DK + ch);
+        kk[j] = load_as_f32<IDT>(k, tokc(j) * DK + ch);
+        qq[j] = load_as_f32<IDT>(q, tokc(j) * DK + ch);
+    }
+    float4 vr[VPL];
+#pragma unroll
+    for (int p = 0; p < VPL; ++p) {
+        const int e = t + 256 * p;
+        vr[p] = load4_as_f32<IDT>(v, tokc(e / CG) * DV + 4 * (e % CG));
+    }
+    const float br = load_as_f32<IDT>(beta, tokc(t));
+
+    const float* S = state + unit * (DK * DV);
+    float4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = stream_load4(S + (rg * RPT + i) * DV + 4 * cg);
+
+    // (stored whole, with no branch, so the compiler keeps the loads ahead of the state read)
+#pragma unroll
+    for (int p = 0; p < VPL; ++p) {
+        const int e = t + 256 * p;
+        vin[e / CG][e % CG] = vr[p];
+    }
+    bin[t] = br;
+
+    // channel ch: cumulative log decays, the projection vectors, and the scalars summed over the
+    // channels (pair index p = j (j - 1) / 2 + i for i < j).  Every wave computes (waves past the
+    // first DK lanes on a copy of the channels) and only lanes t < DK store: a branch around the
+    // work would let the compiler move the input loads into it, behind the state read.
+    auto wsum = [&](float r) {
+        // no fused multiply-add of the caller's product into the first add: the product rounds
+        // first, as in the step kernel, so token 0's k . q matches it bit for bit
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) r += __shfl_xor(r, off, 64);
+        return r;
+    };
+    const bool owner = t < DK;
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+            acc += G[j];
+            G[j] = acc;
+            const float e = expf(acc);
+            if (owner) {
+                xv[2 * j][t] = e * kk[j];
+                xv[2 * j + 1][t] = e * qq[j];
+            }
+        }
+        const bool lead = owner && (t & 63) == 0;
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+            if (j >= K) break;
+            const float kq = wsum(kk[j] * qq[j]);
+            if (lead) scal[wave][2 * NPAIR + j] = kq;
+#pragma unroll
+            for (int i = 0; i < j; ++i) {
+                const int pi = j * (j - 1) / 2 + i;
+                const float w = kk[i] * expf(G[j] - G[i]);
+                const float ck = wsum(w * kk[j]), cq = wsum(w * qq[j]);
+                if (lead) {
+                    scal[wave][pi] = ck;
+                    scal[wave][NPAIR + pi] = cq;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // the projections, VERIFY_PV vectors a pass: partial sums over this lane's rows, then over
+    // the row groups
+    const int NVK = 2 * K;
+    for (int v0 = 0; v0 < NVK; v0 += VERIFY_PV) {
+        if (v0 > 0) __syncthreads();             // the previous pass's partials are read
+#pragma unroll
+        for (int w = 0; w < VERIFY_PV; ++w) {
+            float4 pa = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (v0 + w < NVK) {
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    const float x = xv[v0 + w][rg * RPT + i];
+                    pa.x += x * s[i].x; pa.y += x * s[i].y; pa.z += x * s[i].z; pa.w += x * s[i].w;
+                }
+            }
+            red[rg][w][cg] = pa;
+        }
+        __syncthreads();
+        if (t < VERIFY_PV * CG) {                // lane (w, c) sums vector v0 + w over the row groups
+            const int w = t / CG, c = t % CG;
+            float4 A4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const float4 x = red[r][w][c];
+                A4.x += x.x; A4.y += x.y; A4.z += x.z; A4.w += x.w;
+            }
+            if (v0 + w < NVK) tot[v0 + w][c] = A4;
+        }
+    }
+    __syncthreads();
+
+    // the tokens in order, lane c of the first row group owning columns 4c .. 4c + 3; a scalar is
+    // the sum of the channel-holding waves' partials in wave order (token 0's k . q as the step
+    // kernel sums it)
+    auto csum = [&](int x) {
+        float r = scal[0][x];
+#pragma unroll
+        for (int w = 1; w < (DK + 63) / 64; ++w) r += scal[w][x];
+        return r;
+    };
+    if (t < CG) {
+        float4 u[KM];
+        float bt[KM];
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+            if (j >= K) break;
+            bt[j] = bin[j];
+            const float4 vv = vin[j][t];
+            float4 a = tot[2 * j][t], b = tot[2 * j + 1][t];
+#pragma unroll
+            for (int i = 0; i < j; ++i) {
+                const int pi = j * (j - 1) / 2 + i;
+                const float ck = bt[i] * csum(pi), cq = bt[i] * csum(NPAIR + pi);
+                a.x += ck * u[i].x; a.y += ck * u[i].y; a.z += ck * u[i].z; a.w += ck * u[i].w;
+                b.x += cq * u[i].x; b.y += cq * u[i].y; b.z += cq * u[i].z; b.w += cq * u[i].w;
+            }
+            u[j] = make_float4(vv.x - a.x, vv.y - a.y, vv.z - a.z, vv.w - a.w);
+            const float c = bt[j] * csum(2 * NPAIR + j);
+            const float4 oo = make_float4(scale * (b.x + c * u[j].x), scale * (b.y + c * u[j].y),
+                                          scale * (b.z + c * u[j].z), scale * (b.w + c * u[j].w));
+            store4_from_f32<ODT>(o, tok(j) * DV + 4 * t, oo);
+        }
+    }
+}
+
 template <int DK, int DV, int IDT, int GDT, int ODT>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* beta,
                                   const void* g, float* state, void* o, int32_t N, int32_t H,
@@ -261,8 +445,12 @@ static hipError_t dispatch_multi(const void* q, const void* k, const void* v, co
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(N) * H));
 #define KDA_DM(I, G, O)                                                                        \
     if (idt == I && gdt == G && odt == O) {                                                    \
-        hipLaunchKernelGGL((decode_multi_kernel<DK, DV, I, G, O, COMMIT>), grid, dim3(256), 0,  \
-                           st, q, k, v, beta, g, state, o, scale, K, H, accepted);             \
+        if (!COMMIT && K <= VERIFY_KMAX)                                                       \
+            hipLaunchKernelGGL((decode_verify_kernel<DK, DV, I, G, O>), grid, dim3(256), 0, st, \
+                               q, k, v, beta, g, state, o, scale, K, H);                        \
+        else                                                                                   \
+            hipLaunchKernelGGL((decode_multi_kernel<DK, DV, I, G, O, COMMIT>), grid, dim3(256), \
+                               0, st, q, k, v, beta, g, state, o, scale, K, H, accepted);       \
         return hipGetLastError();                                                              \
     }
     KDA_DM(KDA_BF16, KDA_BF16, KDA_BF16)

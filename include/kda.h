@@ -239,8 +239,11 @@ int kda_decode_step(const void *q, const void *k, const void *v, const void *bet
  *
  * kda_decode_verify -- runs all K draft tokens of every sequence from `state` (read only, never
  * written) and writes each token's output o [N, K, H, d_v] (o_dtype): the outputs K calls of
- * kda_decode_step would give, with one read of the state instead of K reads and writes.
- * o must not overlap any other argument.
+ * kda_decode_step would give, with one read of the state instead of K reads and writes.  Drafts
+ * of up to 8 tokens are evaluated together from one pass over the state (the state after token
+ * j is S_0 under the cumulative decay plus j rank-one terms); the first token's output equals
+ * kda_decode_step's bit for bit, the others equal it up to fp32 rounding.  Longer drafts run
+ * token by token and equal the step outputs bit for bit.  o must not overlap any other argument.
  *
  * kda_decode_commit -- once the draft has been checked, advances each state in place by its
  * accepted tokens: accepted is a device int32 [N] array of counts (values outside [0, K] are

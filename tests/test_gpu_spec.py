@@ -1,6 +1,8 @@
 """GPU parity: speculative decoding -- kda_decode_verify (K draft tokens from a read-only state)
 and kda_decode_commit (the accepted prefix applied in place) against the fp64 oracle and against
-successive kda_decode_step calls, which they must equal bit for bit."""
+successive kda_decode_step calls.  Commit must equal them bit for bit; verify (drafts of up to 8
+tokens run batched from one pass over the state) equals them bit for bit on the first token and
+up to fp32 rounding on the others."""
 import numpy as np
 import pytest
 import torch
@@ -48,8 +50,13 @@ def _check(cfg, n_draft, accepted, n_oracle=None):
     torch.cuda.synchronize()
     assert torch.equal(S_v, S0)
     outs, states = _step_states(steps, S0, n_draft)
-    for t in range(n_draft):
-        assert torch.equal(o[:, t], outs[t]), t
+    assert torch.equal(o[:, 0], outs[0])
+    for t in range(1, n_draft):
+        if n_draft > 8:                          # token by token: the step kernel's arithmetic
+            assert torch.equal(o[:, t], outs[t]), t
+            continue
+        diff = (o[:, t] - outs[t]).abs().max().item()
+        assert diff <= 1e-5 * max(outs[t].abs().max().item(), 1e-30), (t, diff)
     # against the oracle (all sequences, or a sample)
     sel = np.arange(N) if n_oracle is None else np.unique(
         np.random.default_rng(1).choice(N, n_oracle, replace=False))
@@ -71,7 +78,8 @@ def _check(cfg, n_draft, accepted, n_oracle=None):
 
 
 @pytest.mark.parametrize("dk,dv,dtype,n_draft", [(128, 128, "bf16", 4), (64, 64, "f32", 3),
-                                                 (128, 64, "bf16", 1), (64, 128, "f32", 6)])
+                                                 (128, 64, "bf16", 1), (64, 128, "f32", 6),
+                                                 (128, 128, "bf16", 8), (128, 128, "f32", 9)])
 def test_verify_commit_small(dk, dv, dtype, n_draft):
     cfg = inputs.config("decode", B=6, H=3, dk=dk, dv=dv, dtype=dtype)
     accepted = [0, 1, n_draft, n_draft // 2, n_draft + 3, -1]     # the last two clamp
