@@ -177,6 +177,8 @@ __global__ void __launch_bounds__(256) decode_kernel(const void* __restrict__ q,
 // token j of sequence n is row (n*K + j)*H + h.
 //   COMMIT = false (verify): all K tokens, o for each, the state is not written.
 //   COMMIT = true: the first accepted[n] tokens (clamped to [0, K]), no o, the state written once.
+constexpr int MULTI_PRE = 8;     // tokens whose inputs are staged before the state read
+
 template <int DK, int DV, int IDT, int GDT, int ODT, bool COMMIT>
 __global__ void __launch_bounds__(256) decode_multi_kernel(const void* __restrict__ q,
                                                            const void* __restrict__ k,
@@ -206,21 +208,69 @@ __global__ void __launch_bounds__(256) decode_multi_kernel(const void* __restric
         if (steps == 0) return;                  // nothing accepted: the state stays as it is
     }
     auto tok = [&](int32_t j) -> int64_t { return (n * K + j) * H + h; };
+
+    // The inputs of the first MULTI_PRE tokens are staged in LDS from loads issued before the
+    // state read: loads complete in issue order, so inputs loaded after the state would wait for
+    // all of it, and each later token for a round trip of its own.  The loads take no branch (the
+    // compiler would move them into it, behind the state read): token indices clamp to K - 1 and
+    // what the clamped loads bring is never read.  Later tokens load at their start.
+    constexpr int PRE = MULTI_PRE, CH = PRE * DK;       // g, k, q of token j, channel c at
+    __shared__ __align__(16) float pin[3 * CH];         //   a * CH + j * DK + c (a = 0, 1, 2)
+    __shared__ float4 pv[PRE][CG];
+    __shared__ float pb[PRE];
+    static_assert(CH % 256 == 0, "staging");
+    auto tokc = [&](int j) { return tok(j < K ? j : K - 1); };
+    // one four-channel group of each of g, k, q per lane (lanes past CH / 4 load a copy)
+    const int e4 = t % (CH / 4), j4 = 4 * e4 / DK, c4 = 4 * e4 % DK;
+    const float4 xg = load4_as_f32<GDT>(g, tokc(j4) * DK + c4);
+    const float4 xk = load4_as_f32<IDT>(k, tokc(j4) * DK + c4);
+    const float4 xq = load4_as_f32<IDT>(q, tokc(j4) * DK + c4);
+    constexpr int VPL = (PRE * CG + 255) / 256;
+    float4 vr[VPL];
+#pragma unroll
+    for (int p = 0; p < VPL; ++p) {
+        const int e = (t + 256 * p) % (PRE * CG);
+        vr[p] = load4_as_f32<IDT>(v, tokc(e / CG) * DV + 4 * (e % CG));
+    }
+    const float br = load_as_f32<IDT>(beta, tokc(t % PRE));
+
     float4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         s[i] = stream_load4(S + (rg * RPT + i) * DV + 4 * cg);
+
+    reinterpret_cast<float4*>(pin)[e4] = xg;          // (lanes past CH / 4 rewrite a copy)
+    reinterpret_cast<float4*>(pin + CH)[e4] = xk;
+    reinterpret_cast<float4*>(pin + 2 * CH)[e4] = xq;
+#pragma unroll
+    for (int p = 0; p < VPL; ++p) {
+        const int e = (t + 256 * p) % (PRE * CG);       // (lanes past PRE * CG rewrite a copy)
+        pv[e / CG][e % CG] = vr[p];
+    }
+    pb[t % PRE] = br;                                   // (every lane: copies of the same value)
+    __syncthreads();
+
+    auto inputs = [&](int32_t j) {
+        if (j >= PRE) return load_token<DK, DV, IDT, GDT>(q, k, v, beta, g, tok(j));
+        TokIn in;
+        in.g = in.k = in.q = 0.f;
+        if (t < DK) {
+            in.g = pin[j * DK + t];
+            in.k = pin[CH + j * DK + t];
+            in.q = pin[2 * CH + j * DK + t];
+        }
+        in.beta = pb[j];
+        in.v = pv[j][cg];
+        return in;
+    };
     const int32_t last = COMMIT ? steps - 1 : steps;   // commit: the last token also stores S
     for (int32_t j = 0; j < last; ++j) {
         if (j > 0) __syncthreads();              // the previous token's shared values are read
-        // (inputs loaded at the token's start: loading them a token ahead measured slower)
-        decode_token<DK, DV, ODT, false>(s, sm, load_token<DK, DV, IDT, GDT>(q, k, v, beta, g, tok(j)),
-                                         tok(j), COMMIT ? nullptr : o, scale, S);
+        decode_token<DK, DV, ODT, false>(s, sm, inputs(j), tok(j), COMMIT ? nullptr : o, scale, S);
     }
     if constexpr (COMMIT) {
         if (last > 0) __syncthreads();
-        decode_token<DK, DV, ODT, true>(s, sm, load_token<DK, DV, IDT, GDT>(q, k, v, beta, g, tok(last)),
-                                        tok(last), nullptr, scale, S);
+        decode_token<DK, DV, ODT, true>(s, sm, inputs(last), tok(last), nullptr, scale, S);
     }
 }
 
