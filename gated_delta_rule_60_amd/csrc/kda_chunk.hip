@@ -533,7 +533,6 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     constexpr int TOKR = R::TOK;          // tokens per record: two sub-blocks
     constexpr int KS = DK / 32;           // 32-channel groups
     constexpr float LOG2E = 1.4426950408889634f;
-    constexpr int E2 = 2 * R::E;          // bytes of one 16-bit record array
     constexpr int TAIL = 2 * R::TB;       // T' and P tiles, staged together
 
     constexpr int PH = DK / 64;           // 64-channel phases: one 128-byte line of a bf16 row
