@@ -12,9 +12,11 @@
 //     S <- Diag(alpha) S + beta k u^T                     one write of S
 // (o follows from o = S_new^T q = S^T Diag(alpha) q + beta u (k . q).)
 //
-// Speculative decoding: decode_multi_kernel runs K draft tokens of a sequence on one read of the
-// state -- verify returns every token's output and leaves the state alone; commit replays the
-// accepted prefix (from the same token inputs) and writes the state once.
+// Speculative decoding, K draft tokens of a sequence on one read of the state: verify returns
+// every token's output and leaves the state alone; commit replays the accepted prefix (from the
+// same token inputs) and writes the state once.  decode_verify_kernel evaluates drafts of up to 8
+// tokens together (projections of the initial state plus one rank-one term per earlier token);
+// decode_multi_kernel runs commit and longer drafts token by token with the state in registers.
 //
 // Layout: one 256-lane workgroup per (sequence, head).  Lane t owns four consecutive state
 // columns (16-byte loads/stores) of d_k / (256 / (d_v / 4)) consecutive rows, so each row is
