@@ -79,7 +79,8 @@ def _check(cfg, n_draft, accepted, n_oracle=None):
 
 @pytest.mark.parametrize("dk,dv,dtype,n_draft", [(128, 128, "bf16", 4), (64, 64, "f32", 3),
                                                  (128, 64, "bf16", 1), (64, 128, "f32", 6),
-                                                 (128, 128, "bf16", 8), (128, 128, "f32", 9)])
+                                                 (128, 128, "bf16", 8), (128, 128, "f32", 9),
+                                                 (128, 64, "bf16", 5), (64, 64, "bf16", 8)])
 def test_verify_commit_small(dk, dv, dtype, n_draft):
     cfg = inputs.config("decode", B=6, H=3, dk=dk, dv=dv, dtype=dtype)
     accepted = [0, 1, n_draft, n_draft // 2, n_draft + 3, -1]     # the last two clamp
