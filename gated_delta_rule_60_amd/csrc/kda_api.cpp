@@ -122,7 +122,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* beta
                    void* o, int o_dtype, int32_t B, int64_t T, int32_t n_seqs, int32_t H,
                    int32_t dk, int32_t dv, int32_t chunk, float scale, void* workspace,
                    size_t workspace_bytes, void* stream, bool gated, float* ckpt = nullptr,
-                   int32_t ckpt_every = 0, int64_t ckpt_slots = 0) {
+                   int32_t ckpt_every = 0, int64_t ckpt_slots = 0, bool single_stream = false) {
     if (!valid_dtype(in_dtype) || !valid_dtype(g_dtype) || !valid_dtype(o_dtype))
         return KDA_ERR_INVALID_ARGUMENT;
     if (B < 1 || T < 0 || n_seqs < 1 || H < 1 || dk < 1 || dv < 1 || !std::isfinite(scale))
@@ -176,6 +176,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* beta
     a.h0 = initial_state; a.hT = final_state; a.cu = cu_seqlens; a.o = o;
     a.in_dtype = in_dtype; a.g_dtype = g_dtype; a.o_dtype = o_dtype;
     a.B = B; a.T = T; a.n_seqs = n_seqs; a.H = H; a.dk = dk; a.dv = dv;
+    a.head0 = 0; a.heads = H; a.single_stream = single_stream ? 1 : 0;
     a.scale = scale; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.ckpt = ckpt; a.ckpt_every = ckpt_every; a.ckpt_slots = ckpt_slots;
     return from_hip(kda::launch_chunk(a, static_cast<hipStream_t>(stream)));
@@ -226,7 +227,7 @@ int kda_chunk_fwd_gated_noalloc(const void* q, const void* k, const void* v, con
     return chunk_fwd_impl(q, k, v, beta, in_dtype, z, z_dtype, A, g_min, initial_state,
                           final_state, cu_seqlens, o, o_dtype, B, T, n_seqs, H, dk, dv, chunk,
                           scale, ws, need > 0 ? size_t(KDA_NOALLOC_SCRATCH_BYTES) : 0, stream,
-                          true);
+                          true, nullptr, 0, 0, /*single_stream=*/true);
 }
 
 int kda_chunk_fwd_checkpointed(const void* q, const void* k, const void* v, const void* beta,

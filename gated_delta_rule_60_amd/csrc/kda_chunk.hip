@@ -50,6 +50,7 @@
 // Precision (16-bit inputs): A and P of each 16-token block are fp32 products; every operand of
 // the state pass is range-bounded and runs in fp16 (11-bit significand) with fp32 accumulation.
 // For fp32 inputs every product is split bf16 (hi*hi + hi*lo + lo*hi).
+#include <mutex>
 #include <type_traits>
 
 #include "kda_chunk_util.hpp"
@@ -249,8 +250,9 @@ __global__ void __launch_bounds__(64) chunk_intra_kernel(ChunkArgs p, int64_t ns
     const int cg = lane >> 2, sub = lane & 3;
 
     const int64_t H = p.H;
-    const int64_t slot = blockIdx.x / H;
-    const int h = static_cast<int>(blockIdx.x % H);
+    const int64_t gu = global_unit(p, blockIdx.x);
+    const int64_t slot = gu / H;
+    const int h = static_cast<int>(gu % H);
     int n;
     int64_t j, bos, len;
     if (!locate_slot<BLK>(p, slot, n, j, bos, len)) return;
@@ -560,8 +562,9 @@ chunk_intra_tok_kernel(ChunkArgs p, int64_t nslots, uint8_t* ws) {
     const int m = lane & 15, q = lane >> 4;
 
     const int64_t H = p.H;
-    const int64_t slot = blockIdx.x / H;
-    const int h = static_cast<int>(blockIdx.x % H);
+    const int64_t gu = global_unit(p, blockIdx.x);
+    const int64_t slot = gu / H;
+    const int h = static_cast<int>(gu % H);
     int n;
     int64_t j0, bos, len;
     if (!locate_slot<TOKR>(p, slot, n, j0, bos, len)) return;
@@ -918,13 +921,14 @@ __global__ void __launch_bounds__(64 * (NW + state_helpers(NW)), 1) chunk_state_
     // (sequence, head), or a (segment slot, head) in the segment passes; pass 1 puts the M column
     // blocks first.
     const int64_t H = p.H;
-    const int64_t units = (MODE == 0 ? static_cast<int64_t>(p.n_seqs) : sg.slots) * H;
+    const int64_t units = (MODE == 0 ? static_cast<int64_t>(p.n_seqs) : sg.slots) * p.heads;
     const int nvx = MODE == 1 ? sg.n_vblk_m + n_vblk : n_vblk;
     const int64_t bid = blockIdx.x;
     const int64_t grp = bid / (8 * nvx), remv = bid % (8 * nvx);
     int vb = static_cast<int>(remv / 8);
-    const int64_t unit = grp * 8 + remv % 8;
-    if (unit >= units) return;
+    const int64_t lu = grp * 8 + remv % 8;
+    if (lu >= units) return;
+    const int64_t unit = global_unit(p, lu);
     const int h = static_cast<int>(unit % H);
     int n = static_cast<int>(unit / H);
     int64_t seg = 0, seg_slot = 0;
@@ -1379,7 +1383,7 @@ __global__ void __launch_bounds__(512, 1) chunk_pair_kernel(ChunkArgs p, int64_t
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int ln = lane & 15, lq = lane >> 4;
     const int64_t H = p.H;
-    const int64_t unit = blockIdx.x;                   // (segment slot, head)
+    const int64_t unit = global_unit(p, blockIdx.x);   // (segment slot, head)
     const int h = static_cast<int>(unit % H);
     int n;
     int64_t seg;
@@ -1603,8 +1607,9 @@ __global__ void __launch_bounds__(64 * scan_waves(DK)) seg_scan_kernel(ChunkArgs
     // others from that XCD's L2.
     const int64_t grp = blockIdx.x / (8 * ncb), rem = blockIdx.x % (8 * ncb);
     const int cb = static_cast<int>(rem / 8);
-    const int64_t useq = grp * 8 + rem % 8;
-    if (useq >= static_cast<int64_t>(p.n_seqs) * H) return;
+    const int64_t lu = grp * 8 + rem % 8;
+    if (lu >= static_cast<int64_t>(p.n_seqs) * p.heads) return;
+    const int64_t useq = global_unit(p, lu);
     const int n = static_cast<int>(useq / H), h = static_cast<int>(useq % H);
     int64_t len, slot0;
     if (p.cu) {
@@ -1761,13 +1766,85 @@ void launch_state_ck(const ChunkArgs& a, int64_t nslots, const uint8_t* ws, cons
 // MI355X's last-level cache (Infinity Cache): 256 MB
 constexpr int64_t LLC_BYTES = int64_t(256) << 20;
 
+// A second stream per device for head-group concurrency, forked from and joined to the caller's
+// stream by events (capturable: the side stream joins a capture through the fork event).  The
+// mutex keeps each call's record-wait pairs together, so that no call waits on another's fork.
+constexpr int SIDE_MAX_DEVICES = 64;
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[SIDE_MAX_DEVICES];
+
+// fn(s0, s1) launches one part of the work on each stream.  Runs both parts on `stream` when the
+// caller allows only its own stream, or when a capture is under way and the side stream does
+// not exist yet (creating it then is not allowed).
+template <typename F>
+hipError_t on_two_streams(const ChunkArgs& a, hipStream_t stream, F&& fn) {
+    if (a.single_stream) return fn(stream, stream);
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SIDE_MAX_DEVICES) return fn(stream, stream);
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream& sd = g_side[dev];
+    if (sd.s == nullptr) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if ((e = hipStreamIsCapturing(stream, &cs)) != hipSuccess) return e;
+        if (cs != hipStreamCaptureStatusNone) return fn(stream, stream);
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        hipStream_t s = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+        if (cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        sd.s = s; sd.fork = f; sd.join = j;
+    }
+    if ((e = hipEventRecord(sd.fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(sd.s, sd.fork, 0)) != hipSuccess) return e;
+    const hipError_t r = fn(stream, sd.s);
+    // the join is recorded whatever fn returned: the caller's stream must not run ahead of work
+    // already queued on the side stream
+    if ((e = hipEventRecord(sd.join, sd.s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, sd.join, 0)) != hipSuccess) return e;
+    return r;
+}
+
+// Segmented 16-bit prefills at d_k = d_v = 128 run as two head groups on two streams: the
+// kernels of one group fill what the other's leave idle (a pass-1 chain beside intra-block
+// streaming, a kernel's tail beside the next).  Measured on the packed 2^20-token, 8-head
+// workload: 6.71 ms as one launch sequence, 6.39-6.48 ms as two concurrent halves.
+bool split_heads(const ChunkArgs& a, bool segmented) {
+    return segmented && a.in_dtype != KDA_F32 && a.dk == 128 && a.dv == 128 && a.heads == a.H &&
+           a.H >= 2;
+}
+
 template <int DK, int IDT, int GDT, int ODT>
 hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     constexpr bool PRECISE = (IDT == KDA_F32);
     const int64_t total = static_cast<int64_t>(a.B) * a.T;
+    if (split_heads(a, use_segments(a.n_seqs, total, a.H, a.dv))) {
+        ChunkArgs g0 = a, g1 = a;
+        g0.heads = a.H / 2;
+        g1.head0 = g0.heads;
+        g1.heads = a.H - g0.heads;
+        return on_two_streams(a, stream, [&](hipStream_t s0, hipStream_t s1) -> hipError_t {
+            const hipError_t e = launch_t<DK, IDT, GDT, ODT>(g0, s0);
+            if (e != hipSuccess) return e;
+            return launch_t<DK, IDT, GDT, ODT>(g1, s1);
+        });
+    }
     const int64_t nslots = slot_count(a.n_seqs, total, a.cu != nullptr, a.B, a.T, Rec<DK, PRECISE>::TOK);
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
-    const int64_t intra_wgs = nslots * a.H;
+    const int64_t intra_wgs = nslots * a.heads;
     const bool segmented = use_segments(a.n_seqs, total, a.H, a.dv);
     if (intra_wgs > 0) {
         // 16-bit inputs: the token-per-lane kernel; fp32 inputs (split-bf16 records): the
@@ -1776,7 +1853,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
             // Records that fit the last-level cache are stored with the default policy, so that
             // the passes after find them there; larger ones stream past it (measured: the
             // non-temporal hint costs 12% at 230 MB of records and saves 1.3% at 7.4 GB)
-            const bool nt = intra_wgs * Rec<DK, false>::BYTES > LLC_BYTES;
+            const bool nt = nslots * a.H * Rec<DK, false>::BYTES > LLC_BYTES;
 #define KDA_INTRA(G, N)                                                                        \
             hipLaunchKernelGGL((chunk_intra_tok_kernel<DK, GDT, G, N>),                       \
                                dim3(static_cast<unsigned>(intra_wgs)), dim3(64), 0, stream, a, nslots, ws)
@@ -1796,7 +1873,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     const int32_t n_vblk = a.dv / (16 * STATE_WAVES);
     SegArgs sg{};
     if (!segmented) {
-        launch_state_ck<DK, IDT, ODT, PRECISE, 0>(a, nslots, ws, sg, static_cast<int64_t>(a.n_seqs) * a.H,
+        launch_state_ck<DK, IDT, ODT, PRECISE, 0>(a, nslots, ws, sg, static_cast<int64_t>(a.n_seqs) * a.heads,
                                                   n_vblk, stream);
         return hipGetLastError();
     }
@@ -1810,7 +1887,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     sg.seg_shift = SEG_SHIFT;
     sg.slots = a.cu ? seg_slot_bound(a.n_seqs, total)
                     : static_cast<int64_t>(a.B) * (a.T <= 0 ? 1 : (a.T + SEG_TOK - 1) / SEG_TOK);
-    const int64_t seg_units = sg.slots * a.H;
+    const int64_t seg_units = sg.slots * a.heads;
     constexpr int NW = SEG_WAVES;
     const bool wide = (DK == 128 && a.dv == 128);
     const int nw = wide ? 2 * NW : NW;
@@ -1837,7 +1914,7 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((seg_scan_kernel<DK>),
-                       dim3(static_cast<unsigned>((static_cast<int64_t>(a.n_seqs) * a.H + 7) / 8 * 8 * (a.dv / 16))),
+                       dim3(static_cast<unsigned>((static_cast<int64_t>(a.n_seqs) * a.heads + 7) / 8 * 8 * (a.dv / 16))),
                        dim3(64 * scan_waves(DK)), 0, stream, a, sg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -185,6 +185,12 @@ __device__ __forceinline__ bool locate_seg(const ChunkArgs& p, const SegArgs& sg
     return n < p.n_seqs;
 }
 
+// Launch-local (slot or sequence, head) index k over the launch's heads [head0, head0 + heads)
+// -> the global index slot * H + h of the same pair (the identity for a launch over all heads).
+__device__ __forceinline__ int64_t global_unit(const ChunkArgs& p, int64_t k) {
+    return (k / p.heads) * p.H + p.head0 + k % p.heads;
+}
+
 // Length of sequence m's last segment (0 for an empty sequence).
 __device__ __forceinline__ int64_t last_seg_len(const ChunkArgs& p, const SegArgs& sg, int m) {
     int64_t bos, end;

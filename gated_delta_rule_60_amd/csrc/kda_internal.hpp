@@ -48,6 +48,9 @@ struct ChunkArgs {
     int32_t B;
     int64_t T;
     int32_t n_seqs, H, dk, dv;
+    int32_t head0, heads;  // the launch covers heads [head0, head0 + heads); H stays the head
+                           // count of every [.., H, ..] layout (a whole call: 0 and H)
+    int32_t single_stream; // run on the caller's stream only: no stream or event is created
     float scale;
     void* workspace;
     size_t workspace_bytes;
