@@ -26,7 +26,11 @@
  *     The decode step drops T.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL = the
  *     default stream).  There is no host synchronisation and the host never reads device data.
- *     Buffers must stay alive until the stream has passed the work.
+ *     Buffers must stay alive until the stream has passed the work.  Segmented 16-bit prefills
+ *     at d_k = d_v = 128 also run half of the heads on a second stream the library keeps per
+ *     device (created on first use, never destroyed).  That stream starts after the work already
+ *     on `stream` and `stream` waits for it before its next work, so the call's ordering on
+ *     `stream` is as for a single stream.  kda_chunk_fwd_gated_noalloc never uses it.
  *   - Every call returns a kda_status; nothing is printed and nothing aborts.  Host-checkable
  *     argument errors are reported before any device work is enqueued.  Device-resident
  *     preconditions (g in [-5, 0], well-formed cu_seqlens) are the caller's contract and are not
